@@ -1,0 +1,523 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError when
+the oracle disagrees with a closed form, a brute-force enumeration, a library
+special case or a structural invariant.  tests/test_oracle_pins.py runs them on
+the real oracle; tests/test_oracle_mutations.py runs them on copies of the
+oracle with planted mistakes and requires that some pin fails for each.
+
+Nothing here calls the HIP library, and no expected value comes from it.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+PT = 64
+D = 128
+
+
+# ----------------------------------------------------------------------------- test-local helpers
+def bf16_exact(x: np.ndarray) -> np.ndarray:
+    """Truncate fp32 values to ones bf16 represents exactly (test data only)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return u.view(np.float32)
+
+
+def bits(x: np.ndarray) -> np.ndarray:
+    """bf16-exact fp32 -> its bf16 bit pattern."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def pack_request(K_parts, V_parts, Hkv, pad_value=0.0):
+    """Pack logical per-head partitions into the documented host page layout.
+
+    K_parts[h][i] / V_parts[h][i]: [len_i][D] bf16-exact fp32.  A page is the
+    64x128 keys token-major followed by the 128x64 values dim-major; a
+    partition starts on a fresh page; unused token slots hold ``pad_value``."""
+    lens = [k.shape[0] for k in K_parts[0]]
+    npg = [(L + PT - 1) // PT for L in lens]
+    pages = sum(npg)
+    buf = np.zeros((Hkv, pages, 2 * PT * D), np.uint16)
+    for h in range(Hkv):
+        p = 0
+        for i, L in enumerate(lens):
+            for j in range(npg[i]):
+                Kpg = np.full((PT, D), pad_value, np.float32)
+                Vpg = np.full((PT, D), pad_value, np.float32)
+                n = min(PT, L - j * PT)
+                Kpg[:n] = K_parts[h][i][j * PT: j * PT + n]
+                Vpg[:n] = V_parts[h][i][j * PT: j * PT + n]
+                buf[h, p, : PT * D] = bits(Kpg).reshape(-1)
+                buf[h, p, PT * D:] = bits(Vpg.T.copy()).reshape(-1)
+                p += 1
+    return buf.reshape(-1), np.asarray(lens, np.int32)
+
+
+def random_parts(rng, Hkv, lens, scale=1.0):
+    K = [[bf16_exact(rng.standard_normal((L, D)).astype(np.float32) * scale) for L in lens]
+         for _ in range(Hkv)]
+    V = [[bf16_exact(rng.standard_normal((L, D)).astype(np.float32)) for L in lens]
+         for _ in range(Hkv)]
+    return K, V
+
+
+def dense_attention(q, K, V):
+    """Library special case: torch's scaled_dot_product_attention in float64."""
+    qt = torch.from_numpy(np.asarray(q, np.float64)).view(1, 1, 1, -1)
+    Kt = torch.from_numpy(np.asarray(K, np.float64)).view(1, 1, K.shape[0], -1)
+    Vt = torch.from_numpy(np.asarray(V, np.float64)).view(1, 1, V.shape[0], -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt).view(-1).numpy()
+
+
+def make(om, B, Hq, Hkv, k, C, max_pages, n_seg=None):
+    ndir = (max_pages + 63) // 64
+    if n_seg is None:
+        n_seg = min(B * C, B * Hkv * ndir)
+    return om.SpinOracle(B, Hq, Hkv, k, C, max_pages, n_seg)
+
+
+# ----------------------------------------------------------------------------- decoding
+def pin_bf16_decode(om):
+    # bf16 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E00 = 0.125, 0x4049 = 3.140625, 0x0000 = 0
+    got = om.bf16_bits_to_f64(np.array([0x3F80, 0xC000, 0x3E00, 0x4049, 0x0000], np.uint16))
+    assert np.array_equal(got, [1.0, -2.0, 0.125, 3.140625, 0.0]), got
+
+
+def pin_page_layout(om):
+    # key (t, d) = t + d/128 ; value (t, d) = -(t + d/128): both bf16-exact up to t < 64
+    t = np.arange(PT)[:, None].astype(np.float32)
+    d = np.arange(D)[None, :].astype(np.float32)
+    K = bf16_exact(t * 4 + d / 64)
+    V = bf16_exact(-(t * 2) - d / 32)
+    page = np.concatenate([bits(K).reshape(-1), bits(V.T.copy()).reshape(-1)])
+    assert np.array_equal(om.page_keys(page), K.astype(np.float64))
+    assert np.array_equal(om.page_values(page), V.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------- Index
+def pin_summary_closed_form(om):
+    """Keys of a partition are c + e_j and c - e_j in pairs (plus c itself for
+    odd lengths), so the mean is exactly c; padding slots hold 1000.0 so
+    counting them would move the mean."""
+    rng = np.random.default_rng(5)
+    Hkv = 2
+    lens = [64, 1, 130, 255, 17, 64, 256, 3]
+    cents = bf16_exact(rng.integers(-8, 8, size=(Hkv, len(lens), D)).astype(np.float32) / 4)
+    Kp, Vp = [], []
+    for h in range(Hkv):
+        kh, vh = [], []
+        for i, L in enumerate(lens):
+            e = bf16_exact(rng.integers(-4, 5, size=(L // 2, D)).astype(np.float32) / 8)
+            rows = [cents[h, i] + e, cents[h, i] - e]
+            if L % 2:
+                rows.append(cents[h, i][None, :])
+            kk = bf16_exact(np.concatenate(rows, axis=0))
+            assert kk.shape[0] == L
+            kh.append(kk)
+            vh.append(np.zeros((L, D), np.float32))
+        Kp.append(kh)
+        Vp.append(vh)
+    buf, lens_a = pack_request(Kp, Vp, Hkv, pad_value=1000.0)
+    pages = sum((L + 63) // 64 for L in lens)
+    o = make(om, 1, 2 * Hkv, Hkv, 2, 64, pages)
+    o.index(0, buf, lens_a)
+    assert np.array_equal(o.requests[0].summaries, cents.astype(np.float32)), "summary != centroid"
+
+
+# ----------------------------------------------------------------------------- Select
+def pin_score_closed_form(om):
+    """Summaries are scaled basis vectors a_i e_{i mod D}; the group of KV head h
+    has queries whose mean is v_h.  Then score = a_i * v_h[i mod D] / sqrt(D).
+    Groups get different queries so a wrong head->group map changes scores."""
+    Hkv, G = 3, 4
+    N = 40
+    a = np.arange(1, N + 1, dtype=np.float64) / 8
+    Kp, Vp = [], []
+    for h in range(Hkv):
+        kh = []
+        for i in range(N):
+            row = np.zeros((64, D), np.float32)
+            row[:, i % D] = a[i] * (h + 1)
+            kh.append(row)
+        Kp.append(kh)
+        Vp.append([np.zeros((64, D), np.float32)] * N)
+    buf, lens = pack_request(Kp, Vp, Hkv)
+    o = make(om, 1, Hkv * G, Hkv, 5, 64, N)
+    o.index(0, buf, lens)
+    q = np.zeros((1, Hkv * G, D), np.float32)
+    rng = np.random.default_rng(3)
+    expect_v = np.zeros((Hkv, D))
+    for h in range(Hkv):
+        base = rng.integers(-6, 7, size=D).astype(np.float32) / 4
+        # queries of the group: base + offsets that sum to zero over the group
+        offs = rng.integers(-3, 4, size=(G - 1, D)).astype(np.float32) / 4
+        offs = np.concatenate([offs, -offs.sum(0, keepdims=True)], axis=0)
+        q[0, h * G:(h + 1) * G] = base + offs
+        expect_v[h] = base
+    sc = o.scores(bits(bf16_exact(q)))
+    for h in range(Hkv):
+        want = np.array([a[i] * (h + 1) * expect_v[h][i % D] for i in range(N)]) / math.sqrt(D)
+        assert np.allclose(sc[0][h], want, rtol=0, atol=1e-12), (h, sc[0][h][:6], want[:6])
+
+
+def pin_topk_bruteforce(om):
+    """Top-k equals a brute-force stable sort of the oracle's own scores with
+    key (-score, index); many exact ties are forced by repeated summaries."""
+    rng = np.random.default_rng(11)
+    for trial in range(6):
+        Hkv, G, N = 2, 2, int(rng.integers(3, 60))
+        k = int(rng.integers(1, N + 4))
+        levels = rng.integers(0, 4, size=(Hkv, N))  # only 4 distinct summaries -> ties
+        Kp, Vp = [], []
+        for h in range(Hkv):
+            kh = []
+            for i in range(N):
+                row = np.zeros((64, D), np.float32)
+                row[:, :4] = levels[h, i] - 1.5
+                kh.append(row)
+            Kp.append(kh)
+            Vp.append([np.zeros((64, D), np.float32)] * N)
+        buf, lens = pack_request(Kp, Vp, Hkv)
+        o = make(om, 1, Hkv * G, Hkv, k, Hkv * 6 * max(k, 1), N)
+        o.index(0, buf, lens)
+        q = bf16_exact(rng.standard_normal((1, Hkv * G, D)).astype(np.float32))
+        sel, sc = o.select(bits(q))
+        for h in range(Hkv):
+            s = sc[0][h]
+            brute = sorted(sorted(range(N), key=lambda i: (-s[i], i))[:k])
+            want = brute + [-1] * (k - len(brute))
+            assert list(sel[0, h]) == want, (trial, h, list(sel[0, h]), want)
+
+
+# ----------------------------------------------------------------------------- bucketed LRU
+def _lru_state(om, C, owners, last_use):
+    o = make(om, 1, 1, 1, 1, C, 4096, n_seg=64)
+    for c, (own, lu) in enumerate(zip(owners, last_use)):
+        o.owner[0, c] = own
+        o.last_use[0, c] = lu
+    return o
+
+
+def pin_lru_hand_example(om):
+    """Worked by hand from the rule (bucket = 63 - min(63, t - last_use); take
+    whole buckets oldest first, lower slot first inside the cutoff bucket).
+
+    t = 100, 10 slots, slot 9 free, slots 2 and 5 mandatory:
+      slot : 0   1   2*  3   4   5*  6   7   8
+      last : 99  30  97  98  37  99  97  10  98
+      age  : 1   70  3   2   63  1   3   90  2
+      bucket 62  0   -   61  0   -   60  0   61
+    need = 4: bucket 0 holds {1, 4, 7} (3 < 4), bucket 60 holds {6}: 3+1 = 4,
+    so cutoff = 60 and the victims are {1, 4, 6, 7}."""
+    owners = [0, 1, 2, 3, 4, 5, 6, 7, 8, -1]
+    last = [99, 30, 97, 98, 37, 99, 97, 10, 98, -1]
+    o = _lru_state(om, 10, owners, last)
+    victims, cut = o.choose_victims(0, 4, {2, 5}, 100)
+    assert (victims, cut) == ([1, 4, 6, 7], 60), (victims, cut)
+    # need = 5: bucket 61 holds {3, 8}; one more is needed, the lower slot (3)
+    victims, cut = o.choose_victims(0, 5, {2, 5}, 100)
+    assert (victims, cut) == ([1, 3, 4, 6, 7], 61), (victims, cut)
+    # need = 2 inside bucket 0: lowest slots {1, 4}
+    victims, cut = o.choose_victims(0, 2, {2, 5}, 100)
+    assert (victims, cut) == ([1, 4], 0), (victims, cut)
+
+
+def pin_lru_properties(om):
+    """Random states: exactly ``need`` victims; none mandatory or free; every
+    victim's bucket <= cutoff; every candidate below the cutoff is a victim;
+    when all candidate buckets are distinct, victims == exact LRU (the need
+    oldest last_use values, by brute force)."""
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        C = int(rng.integers(2, 40))
+        t = int(rng.integers(0, 200))
+        distinct = trial % 2 == 0
+        if distinct:
+            ages = rng.choice(np.arange(1, 64), size=C, replace=False) if C <= 63 else None
+            if ages is None:
+                continue
+            last = t - ages
+        else:
+            last = t - rng.integers(1, 120, size=C)
+        owners = list(range(C))
+        free = set(rng.choice(C, size=int(rng.integers(0, C // 3 + 1)), replace=False).tolist())
+        for c in free:
+            owners[c] = -1
+        resident = [c for c in range(C) if owners[c] != -1]
+        mand = set(c for c in resident if rng.random() < 0.3)
+        cands = [c for c in resident if c not in mand]
+        if not cands:
+            continue
+        need = int(rng.integers(1, len(cands) + 1))
+        o = _lru_state(om, C, owners, [l if owners[c] != -1 else -1 for c, l in enumerate(last)])
+        victims, cut = o.choose_victims(0, need, mand, t)
+        bk = {c: 63 - min(63, t - int(last[c])) for c in cands}
+        assert len(victims) == need, (trial, victims, need)
+        assert len(set(victims)) == need and all(v in bk for v in victims), trial
+        assert all(bk[v] <= cut for v in victims), trial
+        assert all(c in victims for c in cands if bk[c] < cut), trial
+        at_cut = sorted(c for c in cands if bk[c] == cut)
+        assert sorted(v for v in victims if bk[v] == cut) == at_cut[: len([v for v in victims if bk[v] == cut])], trial
+        if distinct:
+            exact = sorted(sorted(cands, key=lambda c: int(last[c]))[:need])
+            assert victims == exact, (trial, victims, exact)
+
+
+# ----------------------------------------------------------------------------- two-level table
+def check_structure(o, pages_per_req):
+    """Structural pins of the residency state, from plain definitions:
+    the two-level map and the owner map are mutual inverses, live counts equal
+    non-empty entries, the directory uses distinct segments, and the stack of
+    unused segments is exactly the rest (each of them empty)."""
+    used = []
+    for b in range(o.B):
+        flat = {}
+        for h in range(o.Hkv):
+            for p in range(pages_per_req[b] if b < len(pages_per_req) else 0):
+                c = o.translate(b, h, p)
+                if c != -1:
+                    flat[(h, p)] = c
+        inv = {}
+        for c in range(o.C):
+            own = int(o.owner[b, c])
+            if own != -1:
+                inv[divmod(own, o.max_pages)] = c
+                assert o.last_use[b, c] >= 0
+            else:
+                assert o.last_use[b, c] == -1
+        assert flat == inv, f"request {b}: two-level map != inverse of owner map"
+        for h in range(o.Hkv):
+            for e in range(o.ndir):
+                s = int(o.directory[b, h, e])
+                if s != -1:
+                    used.append(s)
+                    assert o.seg_live[s] == np.sum(o.segments[s] != -1) > 0
+    assert len(used) == len(set(used)), "segment linked twice"
+    assert sorted(used + list(o.free_stack)) == list(range(o.n_seg)), "segment lost or duplicated"
+    for s in o.free_stack:
+        assert o.seg_live[s] == 0 and np.all(o.segments[s] == -1)
+
+
+def _run_small(om, B=3, Hq=8, Hkv=2, k=4, C=None, lens_fn=None, steps=24, seed=1, n_seg=None):
+    rng = np.random.default_rng(seed)
+    lens_all = [lens_fn(rng, b) for b in range(B)]
+    pages = [sum((L + 63) // 64 for L in lens) for lens in lens_all]
+    max_ppp = max(max((L + 63) // 64 for L in lens) for lens in lens_all)
+    if C is None:
+        C = Hkv * k * max_ppp + 3
+    o = make(om, B, Hq, Hkv, k, C, max(pages), n_seg)
+    bufs = []
+    for b in range(B):
+        Kp, Vp = random_parts(rng, Hkv, lens_all[b])
+        buf, lens = pack_request(Kp, Vp, Hkv)
+        o.index(b, buf, lens)
+        bufs.append(buf)
+    q = bf16_exact(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    return o, pages, rng, q, bufs
+
+
+def pin_two_level_table(om):
+    """Tight pools so eviction fires most steps; structure checked every step,
+    and mandatory pages are resident with the step's last_use after it."""
+    for seed, lens_fn in [
+        (1, lambda r, b: [64] * int(r.integers(150, 300))),
+        (2, lambda r, b: list(r.integers(16, 257, size=int(r.integers(40, 90))))),
+    ]:
+        o, pages, rng, q, _ = _run_small(om, lens_fn=lens_fn, seed=seed)
+        for t in range(24):
+            q = bf16_exact(0.6 * q + rng.standard_normal(q.shape).astype(np.float32))
+            sel, _ = o.select(bits(q))
+            ev0 = [st["evictions"] for st in o.stats]
+            blocks = o.resolve_evict(sel, t)
+            check_structure(o, pages)
+            for b in range(o.B):
+                # eviction frees exactly the shortfall, so a step that evicted
+                # leaves no free slot behind (R7)
+                if o.stats[b]["evictions"] > ev0[b]:
+                    assert int(np.sum(o.owner[b] == -1)) == 0, (t, b)
+            for b in range(o.B):
+                M = o.mandatory_pages(b, sel[b])
+                assert sum(len(x) for x in blocks[b]) == len(M)
+                for (h, p, n) in M:
+                    c = o.translate(b, h, p)
+                    assert c != -1 and o.last_use[b, c] == t
+                resident = int(np.sum(o.owner[b] != -1))
+                assert resident <= o.C
+
+
+def pin_retrieve_bytes(om):
+    """After each step, every resident slot of the pool holds exactly the host
+    bytes of the page that owns it, and bytes moved = misses x 32 KiB."""
+    o, pages, rng, q, bufs = _run_small(om, lens_fn=lambda r, b: [64] * 120, seed=4)
+    prev_miss = 0
+    for t in range(12):
+        q = bf16_exact(0.5 * q + rng.standard_normal(q.shape).astype(np.float32))
+        sel, _ = o.select(bits(q))
+        o.resolve_evict(sel, t)
+        moved = o.retrieve()
+        miss = sum(s["misses"] for s in o.stats)
+        assert moved == (miss - prev_miss) * 32768
+        prev_miss = miss
+        for b in range(o.B):
+            host = bufs[b].reshape(o.Hkv, pages[b], -1)
+            for c in range(o.C):
+                own = int(o.owner[b, c])
+                if own != -1:
+                    h, p = divmod(own, o.max_pages)
+                    assert np.array_equal(o.pool[b * o.C + c], host[h, p])
+
+
+# ----------------------------------------------------------------------------- attention
+def pin_attend_dense(om):
+    """k = all partitions and an ample pool: the sparse paged output equals dense
+    softmax attention (torch SDPA, float64) over the request's logical K/V.
+    Ragged tails, variable partitions and non-zero padding are included."""
+    rng = np.random.default_rng(21)
+    cases = [
+        (2, 8, 2, [[64] * 5 + [37], [64] * 3]),
+        (1, 10, 2, [[16, 200, 64, 1, 129]]),
+        (2, 16, 2, [[256, 100, 33], [70, 70]]),
+    ]
+    for B, Hq, Hkv, lens_req in cases:
+        G = Hq // Hkv
+        kmax = max(len(l) for l in lens_req)
+        max_ppp = max((L + 63) // 64 for l in lens_req for L in l)
+        pages = [sum((L + 63) // 64 for L in l) for l in lens_req]
+        o = make(om, B, Hq, Hkv, kmax, Hkv * kmax * max_ppp, max(pages))
+        logical = []
+        for b in range(B):
+            Kp, Vp = random_parts(rng, Hkv, lens_req[b], scale=2.0)
+            buf, lens = pack_request(Kp, Vp, Hkv, pad_value=-77.0)
+            o.index(b, buf, lens)
+            logical.append((Kp, Vp))
+        q = bf16_exact(rng.standard_normal((B, Hq, D)).astype(np.float32))
+        sel, _ = o.select(bits(q))
+        blocks = o.resolve_evict(sel, 0)
+        o.retrieve()
+        out = o.attend(bits(q), blocks)
+        for b in range(B):
+            for g in range(Hq):
+                h = g // G
+                K = np.concatenate(logical[b][0][h], axis=0)
+                V = np.concatenate(logical[b][1][h], axis=0)
+                want = dense_attention(q[b, g], K, V)
+                assert np.allclose(out[b, g], want, rtol=0, atol=2e-6), (b, g, np.abs(out[b, g] - want).max())
+
+
+def pin_attend_closed_forms(om):
+    """Equal keys -> output = mean of the values; one key far above the rest ->
+    output = that token's value; shuffling the block order changes nothing."""
+    rng = np.random.default_rng(8)
+    Hkv, Hq = 1, 2
+    lens = [64, 64, 20]
+    K = [[np.ones((L, D), np.float32) * 0.5 for L in lens]]
+    V = [[bf16_exact(rng.standard_normal((L, D)).astype(np.float32)) for L in lens]]
+    buf, la = pack_request(K, V, Hkv, pad_value=9.0)
+    o = make(om, 1, Hq, Hkv, 3, 16, 3)
+    o.index(0, buf, la)
+    q = bf16_exact(rng.standard_normal((1, Hq, D)).astype(np.float32))
+    sel, _ = o.select(bits(q))
+    blocks = o.resolve_evict(sel, 0)
+    o.retrieve()
+    out = o.attend(bits(q), blocks)
+    mean_v = np.concatenate(V[0], axis=0).astype(np.float64).mean(0)
+    assert np.allclose(out[0, 0], mean_v, atol=1e-6) and np.allclose(out[0, 1], mean_v, atol=1e-6)
+    # one dominant key: token 70 (partition 1, row 6) aligned with the query
+    K2 = [[np.zeros((L, D), np.float32) for L in lens]]
+    qv = np.zeros(D, np.float32)
+    qv[:8] = 4.0
+    K2[0][1][6, :8] = 4.0          # logit = 8*16/sqrt(128) ~ 11.3 vs 0 elsewhere
+    K2[0][1][6, 8:16] = 4.0        # 8 more dims (query is zero there): no effect
+    buf2, la2 = pack_request(K2, V, Hkv)
+    o2 = make(om, 1, Hq, Hkv, 3, 16, 3)
+    o2.index(0, buf2, la2)
+    qq = np.stack([qv, qv])[None]
+    sel2, _ = o2.select(bits(qq))
+    blocks2 = o2.resolve_evict(sel2, 0)
+    o2.retrieve()
+    out2 = o2.attend(bits(qq), blocks2)
+    logit = 8 * 16 / math.sqrt(D)
+    wdom = math.exp(logit) / (math.exp(logit) + (sum(lens) - 1))
+    want = wdom * V[0][1][6] + (1 - wdom) * (np.concatenate(V[0], 0).astype(np.float64).sum(0) - V[0][1][6]) / (sum(lens) - 1)
+    assert np.allclose(out2[0, 0], want, atol=1e-6), np.abs(out2[0, 0] - want).max()
+    # permutation of block order
+    perm = [list(reversed(blocks[0][0]))]
+    out3 = o.attend(bits(q), [perm])
+    assert np.allclose(out3, out, rtol=0, atol=1e-7)
+
+
+# ----------------------------------------------------------------------------- whole-step invariants
+def pin_step_invariants(om):
+    """Step 0 is all misses; hits + misses = |mandatory|; zero evictions while
+    the budget holds every page ever selected; errors for bad ids / pool."""
+    o, pages, rng, q, _ = _run_small(om, B=2, lens_fn=lambda r, b: [64] * 40, C=2 * 4 * 12, seed=9)
+    seen = [set() for _ in range(o.B)]
+    for t in range(10):
+        q = bf16_exact(0.9 * q + 0.3 * rng.standard_normal(q.shape).astype(np.float32))
+        sel, _ = o.select(bits(q))
+        before = [dict(s) for s in o.stats]
+        o.resolve_evict(sel, t)
+        for b in range(o.B):
+            M = o.mandatory_pages(b, sel[b])
+            d_h = o.stats[b]["hits"] - before[b]["hits"]
+            d_m = o.stats[b]["misses"] - before[b]["misses"]
+            assert d_h + d_m == len(M)
+            if t == 0:
+                assert d_h == 0
+            seen[b] |= {(h, p) for h, p, _ in M}
+            if len(seen[b]) <= o.C:
+                assert o.stats[b]["evictions"] == 0
+    bad = np.zeros((o.B, o.Hkv, o.k), np.int64)
+    bad[0, 0, 0] = 10 ** 6
+    try:
+        o.resolve_evict(bad, 99)
+        raise AssertionError("out-of-range partition accepted")
+    except IndexError:
+        pass
+    # a pool of one segment cannot hold two KV heads' pages
+    o2, _, _, q2, _ = _run_small(om, B=1, lens_fn=lambda r, b: [64] * 300, n_seg=1, seed=3)
+    sel2, _ = o2.select(bits(q2))
+    try:
+        o2.resolve_evict(sel2, 0)
+        raise AssertionError("exhausted segment pool not reported")
+    except MemoryError:
+        pass
+
+
+def pin_first_step_slots(om):
+    """On a fresh request every mandatory page misses, and misses take the free
+    slots in ascending order (R10): the block table, read in canonical order
+    (head, partition, page ascending), is slots 0, 1, 2, ... of the request."""
+    rng = np.random.default_rng(12)
+    lens = [64, 130, 20, 256, 64, 64, 99]
+    Hkv, Hq, k = 2, 4, 3
+    o = make(om, 2, Hq, Hkv, k, 2 * k * 4 + 5, 13)
+    for b in range(2):
+        Kp, Vp = random_parts(rng, Hkv, lens)
+        buf, la = pack_request(Kp, Vp, Hkv)
+        o.index(b, buf, la)
+    q = bf16_exact(rng.standard_normal((2, Hq, D)).astype(np.float32))
+    sel, _ = o.select(bits(q))
+    blocks = o.resolve_evict(sel, 0)
+    for b in range(2):
+        flat = [s for h in range(Hkv) for s, _ in blocks[b][h]]
+        assert flat == [b * o.C + i for i in range(len(flat))], (b, flat)
+        pages = [(h, int(p)) for h in range(Hkv) for part in sorted(sel[b, h])
+                 for p in range(sum((L + 63) // 64 for L in lens[:part]),
+                                sum((L + 63) // 64 for L in lens[:part + 1]))]
+        assert [divmod(int(o.owner[b, i]), o.max_pages) for i in range(len(flat))] == pages
+        ntok = [n for h in range(Hkv) for _, n in blocks[b][h]]
+        want = [min(64, lens[part] - 64 * j) for h in range(Hkv) for part in sorted(sel[b, h])
+                for j in range((lens[part] + 63) // 64)]
+        assert ntok == want
+
+
+ALL_PINS = [
+    pin_bf16_decode, pin_page_layout, pin_summary_closed_form, pin_score_closed_form,
+    pin_topk_bruteforce, pin_lru_hand_example, pin_lru_properties, pin_two_level_table,
+    pin_retrieve_bytes, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
+    pin_first_step_slots,
+]
