@@ -1,0 +1,232 @@
+"""Sparse-decode benchmark on one MI355X.
+
+A step is one pass of the whole decode path for a batch: select (score +
+top-k), two-level resolve with bucketed-LRU eviction, retrieve of missed pages
+from pinned host memory (on a second stream), and paged sparse attention.
+Inputs (host KV, queries for every step) are resident before the timed
+region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config c4] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PCIE_GEN5_X16_GBS = 63.0       # 32 GT/s x 16 lanes, 128b/130b, one direction
+PAGE_BYTES = 32768
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pcie_link():
+    """Negotiated link of the GPU from sysfs (best effort)."""
+    try:
+        import torch
+        p = torch.cuda.get_device_properties(0)
+        bus = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+        base = f"/sys/bus/pci/devices/{bus}"
+        speed = open(f"{base}/current_link_speed").read().strip()
+        width = open(f"{base}/current_link_width").read().strip()
+        return {"bus": bus, "speed": speed, "width": width}
+    except Exception as e:  # noqa: BLE001
+        return {"error": str(e)}
+
+
+def memcpy_h2d_gbs(nbytes=1 << 30):
+    """Practical H2D ceiling: one pinned -> device copy engine transfer."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 3 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
+
+
+def cpu_baseline(w, geo, draws, host_np, budget_s=20.0):
+    """The CPU oracle as it stands, on the same workload from step 0, for as
+    many whole decode steps as fit in about budget_s seconds (at least one)."""
+    from oracle.spin_oracle import SpinOracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        blas = 1
+    n_seg = min(w.B * w.slots_per_request, w.B * w.Hkv * ((geo.max_pages + 63) // 64))
+    o = SpinOracle(w.B, w.Hq, w.Hkv, w.k, w.slots_per_request, geo.max_pages, n_seg)
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        o.index(b, host_np[b], geo.lens[b])
+    t_index = time.perf_counter() - t0
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        o.step(draws.q_bits[steps], steps)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= draws.q_bits.shape[0]:
+            break
+    return {"value": w.B * w.Hq * steps / el, "unit": "head-tokens/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"first {steps} decode steps of {w.name} (full batch), float64 numpy "
+                      f"oracle, {el:.1f} s; index (not timed) took {t_index:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=120)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--pps", type=int, default=0, help="attention pages per split (0 = auto)")
+    ap.add_argument("--single-stream", action="store_true", help="retrieve on the compute stream")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path shards by "
+              "request with no exchange, so N GPUs run N independent copies of this benchmark.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_attention_tiered_amd import binding as bd
+    from sparse_attention_tiered_amd import workload as W
+
+    w = W.get(args.config)
+    n_steps = max(w.steps, args.warmup + args.steps)
+    t0 = time.time()
+    geo = W.geometry(w)
+    draws = W.draw_queries(w, geo, n_steps)
+    host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
+    W.fill_all(w, geo, draws, [h[1] for h in host])
+    log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s "
+        f"({sum(h[0].numel() * 2 for h in host) / 1e9:.2f} GB pinned host KV)")
+    cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts, geo.max_pages, w.k, w.slots_per_request,
+                         max_pages_per_partition=geo.max_ppp, attend_pages_per_split=args.pps)
+    spin = bd.Spin(cfg)
+    t0 = time.time()
+    for b in range(w.B):
+        spin.index(b, host[b][0], w.ctx[b], geo.lens[b] if w.var_len is not None else None)
+    log(f"[bench] index (summaries over PCIe) {time.time() - t0:.2f}s; attend splits={spin.splits}")
+    q = torch.from_numpy(draws.q_bits.view(np.int16)).to("cuda")
+    S = torch.cuda.current_stream()
+    Cs = S if args.single_stream else torch.cuda.Stream()
+
+    def step(t, ev=None):
+        if ev is not None:
+            ev[0].record(S)
+        spin.select(q[t], stream=S)
+        if ev is not None:
+            ev[1].record(S)
+        spin.resolve_evict(t, stream=S)
+        if ev is not None:
+            ev[2].record(S)
+        spin.retrieve(copy_stream=Cs)
+        if ev is not None:
+            ev[3].record(Cs)
+        spin.attend(q[t], stream=S)
+        if ev is not None:
+            ev[4].record(S)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    st0, _ = spin.stats()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(S)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    end.record(S)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    st1, _ = spin.stats()
+    total_ms = start.elapsed_time(end)
+    K = args.steps
+    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend": 0.0}
+    for e in evs:
+        stage["select"] += e[0].elapsed_time(e[1])
+        stage["resolve_evict"] += e[1].elapsed_time(e[2])
+        stage["retrieve"] += e[2].elapsed_time(e[3])
+        stage["attend"] += e[3].elapsed_time(e[4])
+    stage_ms = {k: v / K for k, v in stage.items()}
+    ms_per_step = total_ms / K
+    value = w.B * w.Hq / (ms_per_step * 1e-3)
+
+    hits = st1.hits - st0.hits
+    misses = st1.misses - st0.misses
+    evictions = st1.evictions - st0.evictions
+    # algorithmic bytes per launch (one step)
+    attend_bytes = (hits + misses) * PAGE_BYTES / K + w.B * w.Hq * 128 * (2 + 4)
+    n_parts = sum(len(l) for l in geo.lens)
+    score_bytes = w.Hkv * n_parts * 128 * 4 + w.B * w.Hq * 128 * 2 + w.Hkv * n_parts * 4
+    retrieve_bytes = misses * PAGE_BYTES / K
+    link = pcie_link()
+    memcpy_gbs = memcpy_h2d_gbs()
+    rl = {
+        "attend": {"bound": "hbm", "achieved": attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": attend_bytes,
+                   "kernels": ["k_attend_partial", "k_attend_reduce"]},
+        "select": {"bound": "hbm", "achieved": score_bytes / (stage_ms["select"] * 1e-3) / 1e9,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
+                   "kernels": ["k_score", "k_topk"]},
+        "retrieve": {"bound": "pcie",
+                     "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if misses else 0.0,
+                     "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
+                     "kernels": ["k_retrieve"]},
+    }
+    for v in rl.values():
+        v["frac"] = v["achieved"] / v["peak"]
+    dominant = max(("attend", "select", "retrieve"), key=lambda k: stage_ms[k])
+    roof = dict(rl[dominant])
+    roof["stage"] = dominant
+    roof["traffic"] = None
+    line = {
+        "metric": "sparse decode head-tokens/s + achieved HBM GB/s vs peak; H2D GB/s vs PCIe",
+        "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "context": w.ctx[0], "topk": w.k, "slots_per_request": w.slots_per_request,
+                   "partitions": "variable 16-256" if w.var_len else "fixed 64",
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "stages_ms": stage_ms,
+        "rooflines": rl,
+        "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,
+                      "evictions_per_step": evictions / K},
+        "pcie": {"link": link, "memcpy_h2d_GBps": memcpy_gbs},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, geo, draws, [h[1] for h in host], args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    spin.close()
+
+
+if __name__ == "__main__":
+    main()

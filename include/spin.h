@@ -1,0 +1,223 @@
+/*
+ * spin.h -- C ABI of the MI355X sparse-decode library (libspin.so).
+ *
+ * One decode step of one attention layer over a KV cache split into
+ * partitions, following the five-operation pipeline of "Unifying Sparse
+ * Attention with Hierarchical Memory for Scalable Long-Context LLM Serving"
+ * (SPIN).  Page citations below:
+ *   [XT] the m.x-techcon.com article on the paper ("吞吐量提升5.66倍！…Spin框架…"),
+ *        design section "Spin的核心设计：从抽象到高效管理", parts 1 (partition
+ *        abstraction, Fig. 3), 2 (locality-aware KV management, Fig. 5) and
+ *        3 (hierarchical metadata, Fig. 6);
+ *   [GP] the gist.science/pt summary, "2. Metodologia" parts A, B, C.
+ *
+ * Index, Select and Attention are the algorithm's operations; Offload and
+ * Retrieve move data between host memory and the GPU ([XT] part 1, Fig. 3;
+ * [GP] A).  Here the full KV of a request stays in pinned host memory (the
+ * offloaded copy); the GPU holds a per-request pool of page slots.
+ *
+ * ---------------------------------------------------------------- layouts
+ * bf16 values are passed as their 16-bit patterns.
+ *   page     64 token slots of one KV head, 32768 bytes:
+ *            keys   [64 tokens][128 dims] bf16, token-major, then
+ *            values [128 dims][64 tokens] bf16, dim-major (transposed).
+ *            Slots past a partition's last token are ignored.
+ *   host KV  one pinned, device-mapped buffer per request:
+ *            [Hkv][pages][page]; partition i of every head starts on page
+ *            sum_{j<i} ceil(len_j / 64) ([GP] B: physical pages per head).
+ *   pool     device, [max_batch * slots_per_request][page]; request b owns
+ *            global slots b*C .. b*C + C - 1 (C = slots_per_request).
+ *   q        device, [max_batch][Hq][128] bf16; query head g uses KV head
+ *            g / (Hq / Hkv).
+ *   sel      device, [max_batch][Hkv][topk] int32, ascending partition ids,
+ *            -1 padding when a head has fewer than topk partitions.
+ *   block    device tables written by spin_resolve_evict:
+ *            table [max_batch][Hkv][max_blocks] int32 global pool slot,
+ *            ntok  [max_batch][Hkv][max_blocks] int32 valid tokens of the page,
+ *            count [max_batch][Hkv] int32 pages of the head.  Entries are in
+ *            canonical order (partition ascending, page ascending); entries
+ *            past count hold -1 / 0.  max_blocks = topk * max_pages_per_partition.
+ *   out      device, [max_batch][Hq][128] float32.
+ *
+ * ---------------------------------------------------------------- contract
+ * Every call returns SPIN_OK (0) or a negative code.  Device pointers must be
+ * 256-byte aligned (workspace, pool) or 16-byte aligned (q, out), and must
+ * outlive the context.  The caller owns all device memory (workspace, pool,
+ * inputs, outputs) and the pinned host KV; the library allocates no device
+ * memory.  Enqueue calls (select / resolve_evict / retrieve / attend / step)
+ * are asynchronous and stream-ordered; spin_index, spin_release, spin_create,
+ * spin_get_stats, spin_snapshot, spin_read_summaries and spin_sync_status
+ * synchronise.  Errors a kernel detects (a partition id out of range, an
+ * exhausted segment pool) set a device error word that the next synchronising
+ * call reports as SPIN_EDEVICE; the residency state is then undefined until
+ * the requests are indexed again.  A context is not thread-safe; use one per
+ * (compute stream, copy stream) pair.  Streams are hipStream_t values passed
+ * as void* (NULL = the null stream).
+ */
+#ifndef SPIN_H
+#define SPIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPIN_API __attribute__((visibility("default")))
+
+#define SPIN_OK 0
+#define SPIN_EINVAL (-1)     /* bad argument or configuration */
+#define SPIN_ECAPACITY (-2)  /* budget smaller than one step's mandatory pages */
+#define SPIN_ESEGPOOL (-3)   /* device reported an exhausted segment pool */
+#define SPIN_EHIP (-4)       /* a HIP runtime call failed; see spin_last_hip_error */
+#define SPIN_EDEVICE (-5)    /* device error word set (see spin_get_stats) */
+#define SPIN_ESTATE (-6)     /* call made in the wrong state (e.g. unindexed request) */
+
+/* device error-word bits */
+#define SPIN_DEVERR_PARTITION 1   /* a selected partition id is out of range */
+#define SPIN_DEVERR_SEGPOOL 2     /* no free second-level segment for an insert */
+#define SPIN_DEVERR_STATE 4       /* residency state found inconsistent */
+
+typedef struct spin_ctx spin_ctx;
+
+typedef struct spin_config {
+  int32_t max_batch;               /* requests (B), >= 1 */
+  int32_t num_q_heads;             /* Hq, a multiple of Hkv, Hq / Hkv <= 16 */
+  int32_t num_kv_heads;            /* Hkv, 1..16 */
+  int32_t head_dim;                /* must be 128 */
+  int32_t page_tokens;             /* must be 64 */
+  int32_t max_partitions;          /* per (request, KV head), 1..16384 */
+  int32_t max_pages;               /* per (request, KV head) */
+  int32_t max_pages_per_partition; /* 1..4 (a partition is at most 256 tokens) */
+  int32_t topk;                    /* partitions selected per KV head, 1..1024 */
+  int32_t slots_per_request;       /* C: GPU page slots of one request, <= 65536 */
+  int32_t num_segments;            /* second-level segments in the shared pool */
+  int32_t seg_entries;             /* must be 64 */
+  int32_t num_buckets;             /* must be 64 */
+  int32_t attend_pages_per_split;  /* attention split size in pages; 0 = automatic */
+} spin_config;
+
+typedef struct spin_stats {
+  uint64_t hits;           /* mandatory pages found resident, summed over steps */
+  uint64_t misses;         /* mandatory pages fetched from host memory */
+  uint64_t evictions;      /* pages reclaimed by the bucketed LRU */
+  uint64_t h2d_bytes;      /* misses * 32768 */
+  int32_t live_segments;   /* segments linked into the directory now */
+  int32_t error_word;      /* SPIN_DEVERR_* bits */
+} spin_stats;
+
+/* Fill *cfg with the fixed geometry (head_dim 128, page_tokens 64,
+ * seg_entries 64, num_buckets 64) and zeros elsewhere. */
+SPIN_API int spin_config_init(spin_config* cfg);
+
+/* Check a configuration.  SPIN_ECAPACITY when slots_per_request is below
+ * Hkv * topk * max_pages_per_partition, the most pages one step can need
+ * ([XT] part 2: the mandatory pages of a step must fit in the request's GPU
+ * area), SPIN_EINVAL for other violations. */
+SPIN_API int spin_config_check(const spin_config* cfg);
+
+/* Bytes of device workspace and of the page pool the caller must provide. */
+SPIN_API int spin_workspace_size(const spin_config* cfg, size_t* ws_bytes, size_t* pool_bytes);
+
+/* Derived sizes: directory entries per (request, head) = ceil(max_pages/64),
+ * max_blocks = topk * max_pages_per_partition, and attention splits per head. */
+SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_blocks,
+                          int32_t* attend_splits);
+
+/* Create a context over caller-owned device memory and reset all state
+ * (every slot free, every directory entry empty, all segments on the free
+ * stack).  Synchronises `stream`. */
+SPIN_API int spin_create(const spin_config* cfg, void* d_workspace, size_t ws_bytes,
+                         void* d_pool, size_t pool_bytes, void* stream, spin_ctx** out);
+SPIN_API int spin_destroy(spin_ctx* ctx);
+
+/* Index + Offload registration of request `req` ([XT] part 1, Fig. 3; [GP] A).
+ * h_kv: the request's pinned host KV in the host layout above (it must come
+ * from hipHostMalloc / a pinned torch tensor; its device-mapped address is
+ * taken with hipHostGetDevicePointer).  part_lens: host array of n_parts
+ * partition lengths in tokens (1..64*max_pages_per_partition), or NULL for
+ * fixed 64-token partitions covering n_tokens (the last one may be shorter).
+ * Releases whatever the request held, records its CPU page table (host base
+ * address, partition -> first page, lengths) and writes its partition
+ * summaries: the mean key over each partition's tokens, accumulated in
+ * float64 and rounded to float32.  Synchronises `stream`. */
+SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_tokens,
+                        const int32_t* part_lens, int32_t n_parts, void* stream);
+
+/* Return request `req`'s slots and second-level segments to the free state;
+ * the request then has no partitions.  Synchronises `stream`. */
+SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream);
+
+/* Select ([XT] part 1, Fig. 3): score every partition of every (request, KV
+ * head), score = (mean of the group's G queries) . summary / sqrt(128), in
+ * float32, and keep the topk highest per KV head (ties: lower partition id).
+ * d_scores may be NULL ([max_batch][Hkv][max_partitions] float32, -inf past a
+ * request's partitions). */
+SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* d_scores,
+                         void* stream);
+
+/* Residency check and eviction for decode step t ([XT] part 2 / Fig. 5 steps
+ * 1-2, part 3 / Fig. 6; [GP] B, C).  The mandatory pages are every page of
+ * every selected partition of the request.  Each is translated through the
+ * two-level page table (directory -> segment -> slot); hits get last_use = t.
+ * When a request's misses exceed its free slots, exactly the shortfall is
+ * reclaimed by bucketed LRU: bucket = 63 - min(63, t - last_use) over the
+ * resident, non-mandatory slots; whole buckets from 0 upward, lower slot
+ * first in the last bucket.  Misses take the free slots in ascending order.
+ * Emptied segments return to the shared pool; first inserts into an empty
+ * directory range take one.  Writes the block tables and the fetch list.
+ * t must not decrease between calls. */
+SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
+                                int32_t* d_block_table, int32_t* d_block_ntok,
+                                int32_t* d_block_count, void* stream);
+
+/* Retrieve ([XT] part 2 / Fig. 5 steps 3-4): copy every page listed by the
+ * last spin_resolve_evict from its host address into its pool slot, on
+ * `copy_stream` (it waits for that resolve; spin_attend waits for this). */
+SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream);
+
+/* Attention ([XT] part 1, Fig. 3) over the block-table pages:
+ * out[b][g] = softmax(q[b][g] . K^T / sqrt(128)) V over the valid tokens of
+ * the pages of KV head g / G, bf16 inputs, float32 accumulation.  A head with
+ * no pages yields zeros.  Waits for the last spin_retrieve. */
+SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                         const int32_t* d_block_ntok, const int32_t* d_block_count,
+                         float* d_out, void* stream);
+
+/* One whole decode step: select, resolve_evict, retrieve (on copy_stream),
+ * attend.  copy_stream may equal stream. */
+SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
+                       int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
+                       float* d_out, void* stream, void* copy_stream);
+
+/* Totals since create.  per_request may be NULL, else [max_batch][4] int64:
+ * hits, misses, evictions, cutoff bucket of the last step (-1 = none).
+ * Synchronises the device. */
+SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* stats, int64_t* per_request);
+
+/* Copy the residency state to host arrays (any may be NULL):
+ * directory [max_batch][Hkv][ndir], segments [num_segments][64],
+ * seg_live [num_segments], seg_stack [num_segments] (entries below *seg_top
+ * are the free segments, top last), owner [max_batch][C] (h * max_pages +
+ * page, or -1), last_use [max_batch][C] (-1 when free), free_count
+ * [max_batch].  Synchronises the device. */
+SPIN_API int spin_snapshot(spin_ctx* ctx, int32_t* directory, int32_t* segments,
+                           int32_t* seg_live, int32_t* seg_stack, int32_t* seg_top,
+                           int32_t* owner, int32_t* last_use, int32_t* free_count);
+
+/* Copy request req's summaries ([Hkv][n_parts][128] float32) to host memory. */
+SPIN_API int spin_read_summaries(spin_ctx* ctx, int32_t req, float* host_out);
+
+/* Synchronise the device and report the device error word: SPIN_OK,
+ * SPIN_ESEGPOOL (segment pool exhausted) or SPIN_EDEVICE (other bits). */
+SPIN_API int spin_sync_status(spin_ctx* ctx);
+
+SPIN_API const char* spin_strerror(int code);
+/* The hipError_t of the last failed HIP call in this context (0 if none). */
+SPIN_API int spin_last_hip_error(spin_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPIN_H */

@@ -1,0 +1,55 @@
+// Wave64 / workgroup primitives used by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spin {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int n = __shfl_up(v, o, 64);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,
+// <= 1024), in thread order.  `tmp` is __shared__ int[NT / 64 + 1].  Every
+// thread must call it; it contains barriers.  *total receives the sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    const int x = lane < W ? tmp[lane] : 0;
+    const int xs = wave_incl_scan(x);
+    if (lane < W) tmp[lane] = xs - x;
+    if (lane == W - 1) tmp[W] = xs;
+  }
+  __syncthreads();
+  const int res = tmp[w] + inc - v;
+  *total = tmp[W];
+  __syncthreads();
+  return res;
+}
+
+// Relaxed device-scope load that does not use a stale L1 line.
+__device__ __forceinline__ int load_device(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace spin

@@ -1,0 +1,126 @@
+// State reset, request release, and Index (partition summaries).
+//
+// Index follows the partition abstraction of the SPIN pages ([XT] design part
+// 1, Fig. 3: Index organises the KV into partitions and summarises them).  The
+// summary is the mean key of a partition's valid tokens, read zero-copy from
+// the request's pinned host KV through its device-mapped address.  bf16 keys
+// are summed in float64, which is exact for up to 256 bf16 terms of the
+// magnitudes involved, then divided and rounded once to float32.
+#include "device_util.h"
+#include "spin_internal.h"
+
+namespace spin {
+
+__global__ void k_init(Dev d) {
+  const size_t tid = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
+  const size_t nth = gridDim.x * (size_t)blockDim.x;
+  const size_t ndir = (size_t)d.B * d.Hkv * d.ndir;
+  for (size_t i = tid; i < ndir; i += nth) d.directory[i] = -1;
+  for (size_t i = tid; i < (size_t)d.n_seg * kSegEntries; i += nth) d.segments[i] = -1;
+  for (size_t i = tid; i < (size_t)d.n_seg; i += nth) {
+    d.seg_live[i] = 0;
+    d.seg_stack[i] = d.n_seg - 1 - (int)i;  // top (last) is segment 0
+  }
+  for (size_t i = tid; i < (size_t)d.B * d.C; i += nth) {
+    d.owner[i] = -1;
+    d.last_use[i] = -1;
+  }
+  for (size_t i = tid; i < (size_t)d.B; i += nth) {
+    d.free_count[i] = d.C;
+    d.req_parts[i] = 0;
+    d.req_pages[i] = 0;
+    d.host_base[i] = 0;
+    d.nmiss[i] = 0;
+    d.nfreed[i] = 0;
+    d.stats[4 * i + 0] = 0;
+    d.stats[4 * i + 1] = 0;
+    d.stats[4 * i + 2] = 0;
+    d.stats[4 * i + 3] = -1;
+  }
+  if (tid == 0) {
+    d.seg_ctl[0] = d.n_seg;
+    d.err[0] = 0;
+    d.fetch_count[0] = 0;
+  }
+}
+
+// Release request `req`: its linked segments go back on the free stack in
+// (KV head, directory index) order with their entries cleared, and all of its
+// slots become free.  One workgroup.
+__global__ __launch_bounds__(1024) void k_release(Dev d, int req) {
+  __shared__ int tmp[17];
+  const int tid = threadIdx.x;
+  const int n = d.Hkv * d.ndir;
+  int* dir = d.directory + (size_t)req * n;
+  const int top = d.seg_ctl[0];
+  int carry = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int e = base + tid;
+    int seg = e < n ? dir[e] : -1;
+    if (seg >= d.n_seg) {
+      atomicOr(d.err, kErrState);
+      seg = -1;
+    }
+    int tot;
+    const int ex = block_excl_scan<1024>(seg >= 0 ? 1 : 0, tmp, &tot);
+    if (seg >= 0) {
+      for (int j = 0; j < kSegEntries; ++j) d.segments[(size_t)seg * kSegEntries + j] = -1;
+      d.seg_live[seg] = 0;
+      const int at = top + carry + ex;
+      if (at < d.n_seg) d.seg_stack[at] = seg;
+      else atomicOr(d.err, kErrState);
+      dir[e] = -1;
+    }
+    carry += tot;
+  }
+  for (int c = tid; c < d.C; c += 1024) {
+    d.owner[(size_t)req * d.C + c] = -1;
+    d.last_use[(size_t)req * d.C + c] = -1;
+  }
+  if (tid == 0) {
+    d.seg_ctl[0] = min(top + carry, d.n_seg);
+    d.free_count[req] = d.C;
+    d.req_parts[req] = 0;
+    d.req_pages[req] = 0;
+    d.nmiss[req] = 0;
+    d.nfreed[req] = 0;
+  }
+}
+
+// One workgroup of 64 lanes per (partition, KV head); lane l owns dims 2l, 2l+1.
+__global__ __launch_bounds__(64) void k_index(Dev d, int req) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int len = d.part_len[(size_t)req * d.Nmax + i];
+  const int first = d.part_first[(size_t)req * d.Nmax + i];
+  const int pages = d.req_pages[req];
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(
+      d.host_base[req] + ((size_t)h * pages + first) * (size_t)kPageBytes);
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll 8
+  for (int t = 0; t < len; ++t) {
+    const uint32_t u = base[((t >> 6) * kPageElems + (t & 63) * kHeadDim) / 2 + lane];
+    s0 += (double)bf16_lo(u);
+    s1 += (double)bf16_hi(u);
+  }
+  float* out = d.summaries + (((size_t)req * d.Hkv + h) * d.Nmax + i) * kHeadDim;
+  out[2 * lane] = (float)(s0 / (double)len);
+  out[2 * lane + 1] = (float)(s1 / (double)len);
+}
+
+hipError_t launch_init(const Dev& d, hipStream_t s) {
+  hipLaunchKernelGGL(k_init, dim3(1024), dim3(256), 0, s, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_release(const Dev& d, int req, hipStream_t s) {
+  hipLaunchKernelGGL(k_release, dim3(1), dim3(1024), 0, s, d, req);
+  return hipGetLastError();
+}
+
+hipError_t launch_index(const Dev& d, int req, int n_parts, hipStream_t s) {
+  if (n_parts == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_index, dim3(n_parts, d.Hkv), dim3(64), 0, s, d, req);
+  return hipGetLastError();
+}
+
+}  // namespace spin

@@ -1,0 +1,317 @@
+// Residency check, bucketed-LRU eviction and the two-level page table.
+//
+// Follows the SPIN pages' KV manager ([XT] design part 2, Fig. 5 steps 1-2;
+// [GP] B) and hierarchical metadata ([XT] part 3, Fig. 6; [GP] C):
+//   * a request's GPU area holds the pages the step needs (mandatory) plus a
+//     buffer of earlier pages;
+//   * the lookup is two-level: a small static directory per (request, KV
+//     head) on the GPU points at 64-entry segments that come from one shared
+//     pool only while they hold resident pages;
+//   * eviction is a bucketed LRU: one pass over the request's slots builds a
+//     64-bin histogram of recency buckets, and whole buckets are reclaimed
+//     from the oldest until the shortfall is covered, mandatory pages never
+//     being candidates.
+// Readings where the pages are silent: bucket = 63 - min(63, t - last_use);
+// exactly the shortfall is evicted, lower slot first inside the cutoff
+// bucket; misses take free slots in ascending order; emptied segments return
+// to the pool in (KV head, directory index) order per request, requests in
+// ascending order, and all returns happen before any segment is handed out.
+//
+// k_resolve runs one 1024-thread workgroup per request: every ordering
+// decision is a workgroup prefix scan in canonical order, so results are
+// deterministic and match a sequential walk.  k_segments is one workgroup for
+// the whole batch because the segment pool is shared.
+#include "device_util.h"
+#include "spin_internal.h"
+
+namespace spin {
+
+__global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__ sel, int t,
+                                                  int* __restrict__ bt, int* __restrict__ bntok,
+                                                  int* __restrict__ bcount) {
+  __shared__ uint32_t mand[kMaxSlots / 32];
+  __shared__ int item_off[kMaxItems + 1];
+  __shared__ int hist[kBuckets];
+  __shared__ int tmp[17];
+  __shared__ int sh_cut, sh_below;
+
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int C = d.C, Hkv = d.Hkv, k = d.k, MB = d.max_blocks;
+  const int n_parts = d.req_parts[b];
+  const int n_items = Hkv * k;
+  const int* selb = sel + (size_t)b * n_items;
+  const int* pfirst = d.part_first + (size_t)b * d.Nmax;
+  const int* plen = d.part_len + (size_t)b * d.Nmax;
+  int* owner = d.owner + (size_t)b * C;
+  int* last = d.last_use + (size_t)b * C;
+  int* dir = d.directory + (size_t)b * Hkv * d.ndir;
+  int4* misses = d.miss_tmp + (size_t)b * d.max_mand;
+  int* btb = bt + (size_t)b * Hkv * MB;
+  int* bnb = bntok + (size_t)b * Hkv * MB;
+
+  for (int i = tid; i < (C + 31) / 32; i += 1024) mand[i] = 0;
+
+  // 1. position of every selected partition in the canonical page list
+  int carry = 0;
+  for (int base = 0; base < n_items; base += 1024) {
+    const int i = base + tid;
+    int np = 0;
+    if (i < n_items) {
+      const int p = selb[i];
+      if (p >= 0) {
+        if (p < n_parts) np = (plen[p] + kPageTokens - 1) / kPageTokens;
+        else atomicOr(d.err, kErrPartition);
+      }
+    }
+    int tot;
+    const int ex = block_excl_scan<1024>(np, tmp, &tot);
+    if (i < n_items) item_off[i] = carry + ex;
+    carry += tot;
+  }
+  if (tid == 0) item_off[n_items] = carry;
+  const int M = carry;
+  __syncthreads();
+
+  // block counts per head; clear the unused tail of the block table
+  for (int i = tid; i < Hkv * MB; i += 1024) {
+    const int h = i / MB, pos = i - h * MB;
+    const int cnt = item_off[(h + 1) * k] - item_off[h * k];
+    if (pos >= cnt) {
+      btb[i] = -1;
+      bnb[i] = 0;
+    }
+  }
+  if (tid < Hkv) bcount[(size_t)b * Hkv + tid] = item_off[(tid + 1) * k] - item_off[tid * k];
+
+  // 2. translate every mandatory page through directory -> segment
+  int mcarry = 0;
+  for (int base = 0; base < n_items; base += 1024) {
+    const int i = base + tid;
+    int nm = 0, p = -1, h = 0, np = 0, pos0 = 0;
+    unsigned missmask = 0;
+    if (i < n_items) {
+      p = selb[i];
+      h = i / k;
+      if (p >= 0 && p < n_parts) {
+        np = (plen[p] + kPageTokens - 1) / kPageTokens;
+        pos0 = item_off[i] - item_off[h * k];
+        for (int j = 0; j < np; ++j) {
+          const int page = pfirst[p] + j;
+          const int ntok = min(kPageTokens, plen[p] - kPageTokens * j);
+          const int seg = dir[h * d.ndir + (page >> 6)];
+          int slot = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
+          if (slot >= C) {
+            atomicOr(d.err, kErrState);
+            slot = -1;
+          }
+          if (slot >= 0) {
+            last[slot] = t;
+            atomicOr(&mand[slot >> 5], 1u << (slot & 31));
+            btb[h * MB + pos0 + j] = b * C + slot;
+            bnb[h * MB + pos0 + j] = ntok;
+          } else {
+            missmask |= 1u << j;
+            ++nm;
+          }
+        }
+      }
+    }
+    int tot;
+    const int ex = block_excl_scan<1024>(nm, tmp, &tot);
+    if (nm) {
+      int rnk = mcarry + ex;
+      for (int j = 0; j < np; ++j)
+        if (missmask & (1u << j))
+          misses[rnk++] = make_int4(h, pfirst[p] + j, pos0 + j,
+                                    min(kPageTokens, plen[p] - kPageTokens * j));
+    }
+    mcarry += tot;
+  }
+  const int nmiss = mcarry;
+  __syncthreads();
+
+  // 3. bucketed LRU, only when the misses outnumber the free slots
+  const int freec = d.free_count[b];
+  const int need = nmiss - freec;
+  int nfreed = 0, cut = -1;
+  if (need > 0) {
+    if (tid < kBuckets) hist[tid] = 0;
+    __syncthreads();
+    for (int c = tid; c < C; c += 1024) {
+      if (owner[c] >= 0 && !((mand[c >> 5] >> (c & 31)) & 1u)) {
+        const int bk = (kBuckets - 1) - min(kBuckets - 1, t - last[c]);
+        atomicAdd(&hist[bk], 1);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int below = 0, cv = 0;
+      while (cv < kBuckets - 1 && below + hist[cv] < need) below += hist[cv++];
+      sh_cut = cv;
+      sh_below = below;
+    }
+    __syncthreads();
+    cut = sh_cut;
+    const int rem = need - sh_below;  // taken from the cutoff bucket, lowest slots first
+    int ecarry = 0;
+    for (int base = 0; base < C; base += 1024) {
+      const int c = base + tid;
+      bool cand = false;
+      int bk = -1;
+      if (c < C && owner[c] >= 0 && !((mand[c >> 5] >> (c & 31)) & 1u)) {
+        cand = true;
+        bk = (kBuckets - 1) - min(kBuckets - 1, t - last[c]);
+      }
+      const int at = (cand && bk == cut) ? 1 : 0;
+      int tot;
+      const int ex = block_excl_scan<1024>(at, tmp, &tot);
+      if (cand && (bk < cut || (at && ecarry + ex < rem))) {
+        const int own = owner[c];
+        const int h = own / d.max_pages, page = own - h * d.max_pages;
+        const int seg = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
+        if (seg >= 0 && seg < d.n_seg) {
+          d.segments[(size_t)seg * kSegEntries + (page & 63)] = -1;
+          atomicSub(&d.seg_live[seg], 1);
+        } else {
+          atomicOr(d.err, kErrState);
+        }
+        owner[c] = -1;
+        last[c] = -1;
+      }
+      ecarry += tot;
+    }
+    __syncthreads();
+    // emptied segments leave the directory, in (head, directory index) order
+    const int ne = Hkv * d.ndir;
+    int fcarry = 0;
+    for (int base = 0; base < ne; base += 1024) {
+      const int e = base + tid;
+      int seg = -1, fl = 0;
+      if (e < ne) {
+        seg = dir[e];
+        fl = (seg >= 0 && load_device(&d.seg_live[seg]) == 0) ? 1 : 0;
+      }
+      int tot;
+      const int ex = block_excl_scan<1024>(fl, tmp, &tot);
+      if (fl) {
+        d.freed[(size_t)b * ne + fcarry + ex] = seg;
+        dir[e] = -1;
+      }
+      fcarry += tot;
+    }
+    nfreed = fcarry;
+  }
+
+  // 4. misses take the free slots in ascending slot order
+  int assigned = 0;
+  if (nmiss > 0) {
+    int acarry = 0;
+    for (int base = 0; base < C && acarry < nmiss; base += 1024) {
+      const int c = base + tid;
+      const int fr = (c < C && owner[c] < 0) ? 1 : 0;
+      int tot;
+      const int ex = block_excl_scan<1024>(fr, tmp, &tot);
+      const int r = acarry + ex;
+      if (fr && r < nmiss) {
+        const int4 m = misses[r];  // (h, page, block position, valid tokens)
+        owner[c] = m.x * d.max_pages + m.y;
+        last[c] = t;
+        btb[m.x * MB + m.z] = b * C + c;
+        bnb[m.x * MB + m.z] = m.w;
+        d.ins[(size_t)b * d.max_mand + r] = make_int4(c, m.x, m.y, 0);
+      }
+      acarry += tot;
+    }
+    assigned = min(acarry, nmiss);
+  }
+  if (tid == 0) {
+    const int ev = need > 0 ? need : 0;
+    if (assigned < nmiss) atomicOr(d.err, kErrState);
+    d.free_count[b] = freec + ev - assigned;
+    d.nmiss[b] = assigned;
+    d.nfreed[b] = nfreed;
+    long long* st = d.stats + 4 * (size_t)b;
+    st[0] += M - nmiss;
+    st[1] += nmiss;
+    st[2] += ev;
+    st[3] = cut;
+  }
+}
+
+// Shared segment pool: push every request's emptied segments (requests in
+// ascending order), then hand segments out to directory ranges that receive
+// their first resident page, in canonical insert order; then write the
+// inserts into the segments and build the batch-wide fetch list.
+__global__ __launch_bounds__(1024) void k_segments(Dev d) {
+  __shared__ int tmp[17];
+  const int tid = threadIdx.x;
+  const int ne = d.Hkv * d.ndir;
+  int top = d.seg_ctl[0];
+  for (int b = 0; b < d.B; ++b) {
+    const int nf = d.nfreed[b];
+    for (int i = tid; i < nf; i += 1024)
+      if (top + i < d.n_seg) d.seg_stack[top + i] = d.freed[(size_t)b * ne + i];
+    top = min(top + nf, d.n_seg);
+  }
+  __syncthreads();
+  int pcarry = 0;
+  for (int b = 0; b < d.B; ++b) {
+    const int nm = d.nmiss[b];
+    const int4* ins = d.ins + (size_t)b * d.max_mand;
+    int* dir = d.directory + (size_t)b * ne;
+    for (int base = 0; base < nm; base += 1024) {
+      const int r = base + tid;
+      int fl = 0, e = 0;
+      if (r < nm) {
+        const int4 m = ins[r];
+        e = m.y * d.ndir + (m.z >> 6);
+        bool first = true;
+        if (r > 0) {
+          const int4 pm = ins[r - 1];
+          first = (pm.y * d.ndir + (pm.z >> 6)) != e;
+        }
+        fl = (first && dir[e] < 0) ? 1 : 0;
+      }
+      int tot;
+      const int ex = block_excl_scan<1024>(fl, tmp, &tot);
+      if (fl) {
+        const int idx = top - 1 - (pcarry + ex);
+        if (idx >= 0) dir[e] = d.seg_stack[idx];
+        else atomicOr(d.err, kErrSegPool);
+      }
+      pcarry += tot;
+    }
+  }
+  __syncthreads();
+  int fcarry = 0;
+  for (int b = 0; b < d.B; ++b) {
+    const int nm = d.nmiss[b];
+    const int4* ins = d.ins + (size_t)b * d.max_mand;
+    const int* dir = d.directory + (size_t)b * ne;
+    for (int r = tid; r < nm; r += 1024) {
+      const int4 m = ins[r];  // (slot, h, page)
+      const int seg = dir[m.y * d.ndir + (m.z >> 6)];
+      if (seg >= 0 && seg < d.n_seg) {
+        d.segments[(size_t)seg * kSegEntries + (m.z & 63)] = m.x;
+        atomicAdd(&d.seg_live[seg], 1);
+      }
+      d.fetch[fcarry + r] = make_int4(b * d.C + m.x, b, m.y, m.z);
+    }
+    fcarry += nm;
+  }
+  if (tid == 0) {
+    d.seg_ctl[0] = max(top - pcarry, 0);
+    d.fetch_count[0] = fcarry;
+  }
+}
+
+hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(k_resolve, dim3(d.B), dim3(1024), 0, s, d, sel, t, bt, bntok, bcount);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_segments, dim3(1), dim3(1024), 0, s, d);
+  return hipGetLastError();
+}
+
+}  // namespace spin

@@ -1,0 +1,42 @@
+// Retrieve: copy the step's missed pages from pinned host memory into their
+// GPU slots ([XT] design part 2, Fig. 5 steps 3-4: the host address comes
+// from the CPU page table, then the transfer is issued; [GP] B: pages are per
+// KV head, so only the needed head's 32 KiB crosses the link).
+//
+// The GPU pulls the pages itself: each workgroup reads whole 32 KiB pages
+// through the host buffer's device-mapped address with 16-byte loads per lane
+// (eight loads in flight per lane, the full page per workgroup) and writes
+// them to HBM.  The host never reads the miss count: the grid is fixed and
+// every workgroup strides over the device-side fetch list.
+#include "device_util.h"
+#include "spin_internal.h"
+
+namespace spin {
+
+constexpr int kRetrieveWG = 256;
+constexpr int kRetrieveGrid = 1024;
+
+__global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
+  const int n = d.fetch_count[0];
+  const int tid = threadIdx.x;
+  for (int j = blockIdx.x; j < n; j += gridDim.x) {
+    const int4 f = d.fetch[j];  // (global slot, request, KV head, page)
+    if ((unsigned)f.x >= (unsigned)(d.B * d.C) || (unsigned)f.y >= (unsigned)d.B) continue;
+    if ((unsigned)f.z >= (unsigned)d.Hkv || (unsigned)f.w >= (unsigned)d.req_pages[f.y]) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        d.host_base[f.y] + ((size_t)f.z * d.req_pages[f.y] + f.w) * (size_t)kPageBytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(d.pool + (size_t)f.x * kPageElems);
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + u * kRetrieveWG + tid);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dst[u * kRetrieveWG + tid] = v[u];
+  }
+}
+
+hipError_t launch_retrieve(const Dev& d, hipStream_t s) {
+  hipLaunchKernelGGL(k_retrieve, dim3(kRetrieveGrid), dim3(kRetrieveWG), 0, s, d);
+  return hipGetLastError();
+}
+
+}  // namespace spin

@@ -1,0 +1,447 @@
+// Host side of libspin.so: configuration checks, workspace layout, the
+// per-call launch sequences, stream/event ordering, stats and snapshots.
+// All device memory is the caller's; this file only carves it up.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "spin.h"
+#include "spin_internal.h"
+
+using spin::Dev;
+
+struct spin_ctx {
+  spin_config cfg;
+  Dev dev;
+  hipEvent_t ev_resolved = nullptr;  // recorded after resolve/evict
+  hipEvent_t ev_fetched = nullptr;   // recorded after retrieve
+  int hip_err = 0;
+  int last_t = -1;
+  size_t ws_bytes = 0;
+};
+
+namespace {
+
+struct Derived {
+  int G, ndir, max_blocks, max_mand, pps, splits;
+};
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int check(const spin_config* c) {
+  if (!c) return SPIN_EINVAL;
+  if (c->head_dim != spin::kHeadDim || c->page_tokens != spin::kPageTokens ||
+      c->seg_entries != spin::kSegEntries || c->num_buckets != spin::kBuckets)
+    return SPIN_EINVAL;
+  if (c->max_batch < 1 || c->max_batch > 1024) return SPIN_EINVAL;
+  if (c->num_kv_heads < 1 || c->num_kv_heads > 16) return SPIN_EINVAL;
+  if (c->num_q_heads < c->num_kv_heads || c->num_q_heads % c->num_kv_heads) return SPIN_EINVAL;
+  if (c->num_q_heads / c->num_kv_heads > spin::kMaxGroup) return SPIN_EINVAL;
+  if (c->max_partitions < 1 || c->max_partitions > spin::kMaxPartitions) return SPIN_EINVAL;
+  if (c->max_pages_per_partition < 1 || c->max_pages_per_partition > spin::kMaxPPP) return SPIN_EINVAL;
+  if (c->max_pages < 1 || (long long)c->max_pages > (long long)c->max_partitions * c->max_pages_per_partition)
+    return SPIN_EINVAL;
+  if (c->topk < 1 || c->topk > 1024 || c->num_kv_heads * c->topk > spin::kMaxItems) return SPIN_EINVAL;
+  if (c->num_segments < 1 || c->num_segments > (1 << 28)) return SPIN_EINVAL;
+  if (c->attend_pages_per_split < 0 || c->attend_pages_per_split > 4096) return SPIN_EINVAL;
+  if (c->slots_per_request < 1 || c->slots_per_request > spin::kMaxSlots) return SPIN_EINVAL;
+  if ((long long)c->max_batch * c->slots_per_request > (1LL << 31) / 2) return SPIN_EINVAL;
+  // every page one step can need must fit in the request's slots
+  if (c->slots_per_request < c->num_kv_heads * c->topk * c->max_pages_per_partition)
+    return SPIN_ECAPACITY;
+  return SPIN_OK;
+}
+
+Derived derive(const spin_config* c) {
+  Derived d;
+  d.G = c->num_q_heads / c->num_kv_heads;
+  d.ndir = (c->max_pages + spin::kSegEntries - 1) / spin::kSegEntries;
+  d.max_blocks = c->topk * c->max_pages_per_partition;
+  d.max_mand = c->num_kv_heads * d.max_blocks;
+  int pps = c->attend_pages_per_split;
+  if (pps == 0) {
+    // aim for about 2048 workgroups over the worst-case page count
+    const long long work = (long long)c->max_batch * c->num_kv_heads * d.max_blocks;
+    pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 2047) / 2048));
+    pps = (pps + 3) / 4 * 4;
+  }
+  d.pps = pps;
+  d.splits = (d.max_blocks + pps - 1) / pps;
+  return d;
+}
+
+// Byte offsets of every workspace region (each 256-byte aligned).
+struct Layout {
+  size_t summaries, part_first, part_len, req_parts, req_pages, host_base, directory, segments,
+      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, scores, miss_tmp, ins, nmiss,
+      freed, nfreed, fetch, fetch_count, part_o, part_ml, stats, err, total;
+};
+
+Layout layout(const spin_config* c, const Derived& d) {
+  Layout L;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = up(o + bytes);
+    return at;
+  };
+  const size_t B = c->max_batch, Hkv = c->num_kv_heads, N = c->max_partitions;
+  const size_t C = c->slots_per_request, S = c->num_segments;
+  L.summaries = take(B * Hkv * N * spin::kHeadDim * sizeof(float));
+  L.part_first = take(B * N * sizeof(int));
+  L.part_len = take(B * N * sizeof(int));
+  L.req_parts = take(B * sizeof(int));
+  L.req_pages = take(B * sizeof(int));
+  L.host_base = take(B * sizeof(unsigned long long));
+  L.directory = take(B * Hkv * d.ndir * sizeof(int));
+  L.segments = take(S * spin::kSegEntries * sizeof(int));
+  L.seg_live = take(S * sizeof(int));
+  L.seg_stack = take(S * sizeof(int));
+  L.seg_ctl = take(4 * sizeof(int));
+  L.owner = take(B * C * sizeof(int));
+  L.last_use = take(B * C * sizeof(int));
+  L.free_count = take(B * sizeof(int));
+  L.scores = take(B * Hkv * N * sizeof(float));
+  L.miss_tmp = take(B * d.max_mand * sizeof(int4));
+  L.ins = take(B * d.max_mand * sizeof(int4));
+  L.nmiss = take(B * sizeof(int));
+  L.freed = take(B * Hkv * d.ndir * sizeof(int));
+  L.nfreed = take(B * sizeof(int));
+  L.fetch = take(B * d.max_mand * sizeof(int4));
+  L.fetch_count = take(4 * sizeof(int));
+  L.part_o = take(B * Hkv * d.splits * d.G * spin::kHeadDim * sizeof(float));
+  L.part_ml = take(B * Hkv * d.splits * d.G * 2 * sizeof(float));
+  L.stats = take(B * 4 * sizeof(long long));
+  L.err = take(4 * sizeof(int));
+  L.total = o;
+  return L;
+}
+
+#define HIPCHK(ctx, expr)                       \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) {                     \
+      if (ctx) (ctx)->hip_err = (int)e_;        \
+      return SPIN_EHIP;                         \
+    }                                           \
+  } while (0)
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+SPIN_API int spin_config_init(spin_config* cfg) {
+  if (!cfg) return SPIN_EINVAL;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->head_dim = spin::kHeadDim;
+  cfg->page_tokens = spin::kPageTokens;
+  cfg->seg_entries = spin::kSegEntries;
+  cfg->num_buckets = spin::kBuckets;
+  cfg->max_pages_per_partition = 1;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_config_check(const spin_config* cfg) { return check(cfg); }
+
+SPIN_API int spin_workspace_size(const spin_config* cfg, size_t* ws_bytes, size_t* pool_bytes) {
+  const int rc = check(cfg);
+  if (rc) return rc;
+  const Derived d = derive(cfg);
+  if (ws_bytes) *ws_bytes = layout(cfg, d).total;
+  if (pool_bytes) *pool_bytes = (size_t)cfg->max_batch * cfg->slots_per_request * spin::kPageBytes;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_blocks,
+                          int32_t* attend_splits) {
+  const int rc = check(cfg);
+  if (rc) return rc;
+  const Derived d = derive(cfg);
+  if (ndir) *ndir = d.ndir;
+  if (max_blocks) *max_blocks = d.max_blocks;
+  if (attend_splits) *attend_splits = d.splits;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, void* d_pool,
+                         size_t pool_bytes, void* stream, spin_ctx** out) {
+  if (!out) return SPIN_EINVAL;
+  *out = nullptr;
+  int rc = check(cfg);
+  if (rc) return rc;
+  const Derived d = derive(cfg);
+  const Layout L = layout(cfg, d);
+  const size_t need_pool = (size_t)cfg->max_batch * cfg->slots_per_request * spin::kPageBytes;
+  if (!d_ws || !d_pool || ws_bytes < L.total || pool_bytes < need_pool) return SPIN_EINVAL;
+  if (!aligned(d_ws, kAlign) || !aligned(d_pool, kAlign)) return SPIN_EINVAL;
+  spin_ctx* ctx = new (std::nothrow) spin_ctx();
+  if (!ctx) return SPIN_EINVAL;
+  ctx->cfg = *cfg;
+  ctx->ws_bytes = ws_bytes;
+  char* w = static_cast<char*>(d_ws);
+  Dev& v = ctx->dev;
+  v.B = cfg->max_batch;
+  v.Hq = cfg->num_q_heads;
+  v.Hkv = cfg->num_kv_heads;
+  v.G = d.G;
+  v.k = cfg->topk;
+  v.Nmax = cfg->max_partitions;
+  v.max_pages = cfg->max_pages;
+  v.max_ppp = cfg->max_pages_per_partition;
+  v.C = cfg->slots_per_request;
+  v.n_seg = cfg->num_segments;
+  v.ndir = d.ndir;
+  v.max_blocks = d.max_blocks;
+  v.max_mand = d.max_mand;
+  v.splits = d.splits;
+  v.pps = d.pps;
+  v.summaries = reinterpret_cast<float*>(w + L.summaries);
+  v.part_first = reinterpret_cast<int*>(w + L.part_first);
+  v.part_len = reinterpret_cast<int*>(w + L.part_len);
+  v.req_parts = reinterpret_cast<int*>(w + L.req_parts);
+  v.req_pages = reinterpret_cast<int*>(w + L.req_pages);
+  v.host_base = reinterpret_cast<unsigned long long*>(w + L.host_base);
+  v.directory = reinterpret_cast<int*>(w + L.directory);
+  v.segments = reinterpret_cast<int*>(w + L.segments);
+  v.seg_live = reinterpret_cast<int*>(w + L.seg_live);
+  v.seg_stack = reinterpret_cast<int*>(w + L.seg_stack);
+  v.seg_ctl = reinterpret_cast<int*>(w + L.seg_ctl);
+  v.owner = reinterpret_cast<int*>(w + L.owner);
+  v.last_use = reinterpret_cast<int*>(w + L.last_use);
+  v.free_count = reinterpret_cast<int*>(w + L.free_count);
+  v.scores = reinterpret_cast<float*>(w + L.scores);
+  v.miss_tmp = reinterpret_cast<int4*>(w + L.miss_tmp);
+  v.ins = reinterpret_cast<int4*>(w + L.ins);
+  v.nmiss = reinterpret_cast<int*>(w + L.nmiss);
+  v.freed = reinterpret_cast<int*>(w + L.freed);
+  v.nfreed = reinterpret_cast<int*>(w + L.nfreed);
+  v.fetch = reinterpret_cast<int4*>(w + L.fetch);
+  v.fetch_count = reinterpret_cast<int*>(w + L.fetch_count);
+  v.part_o = reinterpret_cast<float*>(w + L.part_o);
+  v.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+  v.stats = reinterpret_cast<long long*>(w + L.stats);
+  v.err = reinterpret_cast<int*>(w + L.err);
+  v.pool = static_cast<uint16_t*>(d_pool);
+  hipError_t e = hipEventCreateWithFlags(&ctx->ev_resolved, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fetched, hipEventDisableTiming);
+  if (e == hipSuccess) e = spin::launch_init(v, S(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
+  if (e != hipSuccess) {
+    spin_destroy(ctx);
+    return SPIN_EHIP;
+  }
+  *out = ctx;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_destroy(spin_ctx* ctx) {
+  if (!ctx) return SPIN_EINVAL;
+  if (ctx->ev_resolved) (void)hipEventDestroy(ctx->ev_resolved);
+  if (ctx->ev_fetched) (void)hipEventDestroy(ctx->ev_fetched);
+  delete ctx;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream) {
+  if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
+  HIPCHK(ctx, spin::launch_release(ctx->dev, req, S(stream)));
+  HIPCHK(ctx, hipStreamSynchronize(S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_tokens,
+                        const int32_t* part_lens, int32_t n_parts, void* stream) {
+  if (!ctx || req < 0 || req >= ctx->cfg.max_batch || n_tokens < 0) return SPIN_EINVAL;
+  const spin_config& c = ctx->cfg;
+  std::vector<int32_t> lens;
+  if (part_lens) {
+    if (n_parts < 0) return SPIN_EINVAL;
+    lens.assign(part_lens, part_lens + n_parts);
+    int64_t sum = 0;
+    for (int32_t L : lens) {
+      if (L < 1 || L > spin::kPageTokens * c.max_pages_per_partition) return SPIN_EINVAL;
+      sum += L;
+    }
+    if (sum != n_tokens) return SPIN_EINVAL;
+  } else {
+    const int64_t full = n_tokens / spin::kPageTokens, tail = n_tokens % spin::kPageTokens;
+    if (full + (tail ? 1 : 0) > c.max_partitions) return SPIN_EINVAL;
+    lens.assign((size_t)full, spin::kPageTokens);
+    if (tail) lens.push_back((int32_t)tail);
+  }
+  if ((int64_t)lens.size() > c.max_partitions) return SPIN_EINVAL;
+  std::vector<int32_t> first(lens.size());
+  int64_t pages = 0;
+  for (size_t i = 0; i < lens.size(); ++i) {
+    first[i] = (int32_t)pages;
+    pages += (lens[i] + spin::kPageTokens - 1) / spin::kPageTokens;
+  }
+  if (pages > c.max_pages) return SPIN_EINVAL;
+  unsigned long long base = 0;
+  if (!lens.empty()) {
+    if (!h_kv) return SPIN_EINVAL;
+    void* dptr = nullptr;
+    HIPCHK(ctx, hipHostGetDevicePointer(&dptr, const_cast<void*>(h_kv), 0));
+    if (!aligned(dptr, 16)) return SPIN_EINVAL;
+    base = reinterpret_cast<unsigned long long>(dptr);
+  }
+  hipStream_t s = S(stream);
+  Dev& v = ctx->dev;
+  const int np = (int)lens.size(), pg = (int)pages;
+  HIPCHK(ctx, spin::launch_release(v, req, s));
+  if (np) {
+    HIPCHK(ctx, hipMemcpyAsync(v.part_first + (size_t)req * v.Nmax, first.data(), np * sizeof(int),
+                               hipMemcpyHostToDevice, s));
+    HIPCHK(ctx, hipMemcpyAsync(v.part_len + (size_t)req * v.Nmax, lens.data(), np * sizeof(int),
+                               hipMemcpyHostToDevice, s));
+  }
+  HIPCHK(ctx, hipMemcpyAsync(v.req_pages + req, &pg, sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, hipMemcpyAsync(v.host_base + req, &base, sizeof(base), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, spin::launch_index(v, req, np, s));
+  // partitions become visible to select/resolve only once the summaries exist
+  HIPCHK(ctx, hipMemcpyAsync(v.req_parts + req, &np, sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, hipStreamSynchronize(s));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* d_scores,
+                         void* stream) {
+  if (!ctx || !d_q || !d_sel || !aligned(d_q, 16)) return SPIN_EINVAL;
+  float* sc = d_scores ? d_scores : ctx->dev.scores;
+  HIPCHK(ctx, spin::launch_score(ctx->dev, static_cast<const uint16_t*>(d_q), sc, S(stream)));
+  HIPCHK(ctx, spin::launch_topk(ctx->dev, sc, d_sel, S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
+                                int32_t* d_block_table, int32_t* d_block_ntok,
+                                int32_t* d_block_count, void* stream) {
+  if (!ctx || !d_sel || !d_block_table || !d_block_ntok || !d_block_count || t < 0) return SPIN_EINVAL;
+  if (t < ctx->last_t) return SPIN_EINVAL;
+  ctx->last_t = t;
+  HIPCHK(ctx, spin::launch_resolve(ctx->dev, d_sel, t, d_block_table, d_block_ntok, d_block_count,
+                                   S(stream)));
+  HIPCHK(ctx, hipEventRecord(ctx->ev_resolved, S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream) {
+  if (!ctx) return SPIN_EINVAL;
+  HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
+  HIPCHK(ctx, spin::launch_retrieve(ctx->dev, S(copy_stream)));
+  HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                         const int32_t* d_block_ntok, const int32_t* d_block_count, float* d_out,
+                         void* stream) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
+  if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
+  HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
+                                  d_block_ntok, d_block_count, d_out, S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
+                       int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
+                       float* d_out, void* stream, void* copy_stream) {
+  int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
+  if (!rc) rc = spin_resolve_evict(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream);
+  if (!rc) rc = spin_retrieve(ctx, copy_stream);
+  if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+  return rc;
+}
+
+SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* st, int64_t* per_request) {
+  if (!ctx) return SPIN_EINVAL;
+  const Dev& v = ctx->dev;
+  HIPCHK(ctx, hipDeviceSynchronize());
+  std::vector<long long> s(4 * (size_t)v.B);
+  int top = 0, err = 0;
+  HIPCHK(ctx, hipMemcpy(s.data(), v.stats, s.size() * sizeof(long long), hipMemcpyDeviceToHost));
+  HIPCHK(ctx, hipMemcpy(&top, v.seg_ctl, sizeof(int), hipMemcpyDeviceToHost));
+  HIPCHK(ctx, hipMemcpy(&err, v.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (st) {
+    std::memset(st, 0, sizeof(*st));
+    for (int b = 0; b < v.B; ++b) {
+      st->hits += s[4 * b];
+      st->misses += s[4 * b + 1];
+      st->evictions += s[4 * b + 2];
+    }
+    st->h2d_bytes = st->misses * (uint64_t)spin::kPageBytes;
+    st->live_segments = v.n_seg - top;
+    st->error_word = err;
+  }
+  if (per_request) std::memcpy(per_request, s.data(), s.size() * sizeof(long long));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_snapshot(spin_ctx* ctx, int32_t* directory, int32_t* segments, int32_t* seg_live,
+                           int32_t* seg_stack, int32_t* seg_top, int32_t* owner, int32_t* last_use,
+                           int32_t* free_count) {
+  if (!ctx) return SPIN_EINVAL;
+  const Dev& v = ctx->dev;
+  HIPCHK(ctx, hipDeviceSynchronize());
+  auto cp = [&](void* dst, const void* src, size_t n) -> hipError_t {
+    return dst ? hipMemcpy(dst, src, n, hipMemcpyDeviceToHost) : hipSuccess;
+  };
+  HIPCHK(ctx, cp(directory, v.directory, (size_t)v.B * v.Hkv * v.ndir * sizeof(int)));
+  HIPCHK(ctx, cp(segments, v.segments, (size_t)v.n_seg * spin::kSegEntries * sizeof(int)));
+  HIPCHK(ctx, cp(seg_live, v.seg_live, (size_t)v.n_seg * sizeof(int)));
+  HIPCHK(ctx, cp(seg_stack, v.seg_stack, (size_t)v.n_seg * sizeof(int)));
+  HIPCHK(ctx, cp(seg_top, v.seg_ctl, sizeof(int)));
+  HIPCHK(ctx, cp(owner, v.owner, (size_t)v.B * v.C * sizeof(int)));
+  HIPCHK(ctx, cp(last_use, v.last_use, (size_t)v.B * v.C * sizeof(int)));
+  HIPCHK(ctx, cp(free_count, v.free_count, (size_t)v.B * sizeof(int)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_read_summaries(spin_ctx* ctx, int32_t req, float* host_out) {
+  if (!ctx || !host_out || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
+  const Dev& v = ctx->dev;
+  HIPCHK(ctx, hipDeviceSynchronize());
+  int np = 0;
+  HIPCHK(ctx, hipMemcpy(&np, v.req_parts + req, sizeof(int), hipMemcpyDeviceToHost));
+  for (int h = 0; h < v.Hkv; ++h)
+    HIPCHK(ctx, hipMemcpy(host_out + (size_t)h * np * spin::kHeadDim,
+                          v.summaries + ((size_t)req * v.Hkv + h) * v.Nmax * spin::kHeadDim,
+                          (size_t)np * spin::kHeadDim * sizeof(float), hipMemcpyDeviceToHost));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_sync_status(spin_ctx* ctx) {
+  if (!ctx) return SPIN_EINVAL;
+  HIPCHK(ctx, hipDeviceSynchronize());
+  int err = 0;
+  HIPCHK(ctx, hipMemcpy(&err, ctx->dev.err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err & SPIN_DEVERR_SEGPOOL) return SPIN_ESEGPOOL;
+  if (err) return SPIN_EDEVICE;
+  return SPIN_OK;
+}
+
+SPIN_API const char* spin_strerror(int code) {
+  switch (code) {
+    case SPIN_OK: return "ok";
+    case SPIN_EINVAL: return "invalid argument or configuration";
+    case SPIN_ECAPACITY: return "slots per request below the pages one step can need";
+    case SPIN_ESEGPOOL: return "second-level segment pool exhausted";
+    case SPIN_EHIP: return "HIP runtime error";
+    case SPIN_EDEVICE: return "device error word set";
+    case SPIN_ESTATE: return "call made in the wrong state";
+    default: return "unknown error";
+  }
+}
+
+SPIN_API int spin_last_hip_error(spin_ctx* ctx) { return ctx ? ctx->hip_err : 0; }
+
+}  // extern "C"

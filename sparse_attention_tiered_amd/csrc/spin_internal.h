@@ -1,0 +1,75 @@
+// Internal declarations shared by the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spin {
+
+constexpr int kHeadDim = 128;
+constexpr int kPageTokens = 64;
+constexpr int kPageElems = 2 * kPageTokens * kHeadDim;  // bf16 elements per page
+constexpr int kPageBytes = kPageElems * 2;               // 32 KiB
+constexpr int kSegEntries = 64;
+constexpr int kBuckets = 64;
+constexpr int kMaxPartitions = 16384;
+constexpr int kMaxSlots = 65536;
+constexpr int kMaxItems = 4096;        // Hkv * topk, mandatory partitions of one request
+constexpr int kMaxPPP = 4;             // pages per partition
+constexpr int kMaxGroup = 16;          // query heads per KV head
+
+// device error-word bits (kept equal to the SPIN_DEVERR_* values of spin.h)
+constexpr int kErrPartition = 1;       // selected partition id out of range
+constexpr int kErrSegPool = 2;         // no free second-level segment
+constexpr int kErrState = 4;           // residency state inconsistent
+
+// Device-visible view of the workspace, passed by value to kernels.
+struct Dev {
+  // geometry
+  int B, Hq, Hkv, G, k, Nmax, max_pages, max_ppp, C, n_seg, ndir, max_blocks, max_mand;
+  int splits, pps;
+  // index tables (written by spin_index)
+  float* summaries;            // [B][Hkv][Nmax][128]
+  int* part_first;             // [B][Nmax] first page of partition
+  int* part_len;               // [B][Nmax] tokens
+  int* req_parts;              // [B]
+  int* req_pages;              // [B] pages per KV head
+  unsigned long long* host_base;  // [B] device-mapped address of the host KV
+  // residency state
+  int* directory;              // [B][Hkv][ndir] segment id or -1
+  int* segments;               // [n_seg][64] request-local slot or -1
+  int* seg_live;               // [n_seg]
+  int* seg_stack;              // [n_seg]
+  int* seg_ctl;                // [0] = stack top
+  int* owner;                  // [B][C] h * max_pages + page, or -1
+  int* last_use;               // [B][C]
+  int* free_count;             // [B]
+  // per-step scratch
+  float* scores;               // [B][Hkv][Nmax]
+  int4* miss_tmp;              // [B][max_mand] (h, page, block position, valid tokens)
+  int4* ins;                   // [B][max_mand] (slot, h, page, 0)
+  int* nmiss;                  // [B]
+  int* freed;                  // [B][Hkv * ndir]
+  int* nfreed;                 // [B]
+  int4* fetch;                 // [B * max_mand] (global slot, b, h, page)
+  int* fetch_count;            // [1]
+  float* part_o;               // [B * Hkv * splits][G][128]
+  float* part_ml;              // [B * Hkv * splits][G][2] (max in log2 units, sum)
+  long long* stats;            // [B][4] hits, misses, evictions, last cutoff
+  int* err;                    // [1] error bits
+  uint16_t* pool;              // [B * C][kPageElems]
+};
+
+// launchers (each returns the hipError_t of its launch)
+hipError_t launch_init(const Dev& d, hipStream_t s);
+hipError_t launch_release(const Dev& d, int req, hipStream_t s);
+hipError_t launch_index(const Dev& d, int req, int n_parts, hipStream_t s);
+hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s);
+hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);
+hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
+                          hipStream_t s);
+hipError_t launch_retrieve(const Dev& d, hipStream_t s);
+hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
+                         const int* bcount, float* out, hipStream_t s);
+
+}  // namespace spin

@@ -1,0 +1,172 @@
+"""Drive the HIP library and the CPU oracle side by side on the same seeded inputs.
+
+Stage parity: at every step the GPU's selection is checked against the
+oracle's (exact, except members whose oracle scores are within 1e-5 of the
+oracle's k-th score); then the GPU's resolve is fed the *oracle's* selection,
+so a legitimate near-tie cannot cascade into a state mismatch, and the whole
+residency state is compared bit for bit; attention outputs are compared within
+max-abs 2e-3.  Inputs flow from the generator to both sides; nothing the GPU
+produces is fed to the oracle.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+from oracle.spin_oracle import SpinOracle
+from sparse_attention_tiered_amd import binding as bd
+from sparse_attention_tiered_amd import workload as W
+
+TIE_WINDOW = 1e-5
+OUT_TOL = 2e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+class Pair:
+    """The GPU context and the oracle, indexed with the same host KV."""
+
+    def __init__(self, w: W.Workload, n_steps=None, attend_pps=0, num_segments=None,
+                 slots=None, oracle=True, threads=None):
+        t0 = time.time()
+        self.w = w
+        self.geo = geo = W.geometry(w)
+        self.draws = W.draw_queries(w, geo, n_steps)
+        self.T = self.draws.q_bits.shape[0]
+        self.host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
+        W.fill_all(w, geo, self.draws, [h[1] for h in self.host], threads)
+        C = w.slots_per_request if slots is None else slots
+        self.cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts, geo.max_pages, w.k, C,
+                                  num_segments=num_segments, max_pages_per_partition=geo.max_ppp,
+                                  attend_pages_per_split=attend_pps)
+        self.spin = bd.Spin(self.cfg)
+        for b in range(w.B):
+            lens = geo.lens[b] if w.var_len is not None else None
+            self.spin.index(b, self.host[b][0], w.ctx[b], lens)
+        self.q_dev = torch.from_numpy(self.draws.q_bits.view(np.int16)).to("cuda")
+        self.scores = torch.empty((w.B, w.Hkv, geo.max_parts), dtype=torch.float32, device="cuda")
+        self.oracle = None
+        if oracle:
+            self.oracle = SpinOracle(w.B, w.Hq, w.Hkv, w.k, C, geo.max_pages, self.cfg.num_segments)
+            for b in range(w.B):
+                self.oracle.index(b, self.host[b][1], geo.lens[b])
+        log(f"[setup] {w.name} B={w.B} ctx={w.ctx[0]} C={C} segs={self.cfg.num_segments} "
+            f"splits={self.spin.splits} in {time.time() - t0:.1f}s")
+
+    # ------------------------------------------------------------------ checks
+    def check_summaries(self):
+        for b in range(self.w.B):
+            n = len(self.geo.lens[b])
+            if n == 0:
+                continue
+            got = self.spin.summaries(b, n)
+            want = self.oracle.requests[b].summaries
+            # within 2 float32 ulp (the accumulation is exact, so normally equal)
+            np.testing.assert_array_almost_equal_nulp(got, want, nulp=2)
+
+    def check_select(self, t, sel_gpu, scores_gpu):
+        sel_o, sc_o = self.oracle.select(self.draws.q_bits[t])
+        k = self.w.k
+        flips = 0
+        for b in range(self.w.B):
+            n = len(self.geo.lens[b])
+            for h in range(self.w.Hkv):
+                g = sel_gpu[b, h]
+                o = sel_o[b, h]
+                m = min(k, n)
+                assert np.all(g[m:] == -1) and np.all(o[m:] == -1)
+                assert np.all(np.diff(g[:m]) > 0), ("GPU selection not ascending", b, h)
+                if n:
+                    s = sc_o[b][h]
+                    # float32 dot products of 128 terms against the float64 oracle
+                    tol = 1e-6 + 4e-6 * float(np.max(np.abs(s)))
+                    assert np.max(np.abs(scores_gpu[b, h, :n] - s)) < tol, ("score", b, h)
+                    assert np.all(np.isneginf(scores_gpu[b, h, n:]))
+                if set(g[:m]) != set(o[:m]):
+                    kth = np.sort(sc_o[b][h])[::-1][k - 1]
+                    for p in set(g[:m]) ^ set(o[:m]):
+                        assert abs(sc_o[b][h][p] - kth) <= TIE_WINDOW, (
+                            f"step {t} b{b} h{h}: partition {p} score {sc_o[b][h][p]} vs k-th {kth}")
+                    flips += 1
+        return sel_o, flips
+
+    def check_state(self, t):
+        snap = self.spin.snapshot()
+        o = self.oracle
+        top = int(snap["seg_top"][0])
+        assert top == len(o.free_stack), (t, top, len(o.free_stack))
+        assert np.array_equal(snap["seg_stack"][:top], np.asarray(o.free_stack, np.int32)), t
+        for name in ("directory", "segments", "seg_live", "owner", "last_use"):
+            a, b = snap[name], getattr(o, name).astype(np.int32)
+            if not np.array_equal(a, b):
+                idx = np.argwhere(a != b)[:5]
+                raise AssertionError(f"step {t}: {name} differs at {idx.tolist()}: "
+                                     f"gpu {a[tuple(idx.T)]} oracle {b[tuple(idx.T)]}")
+        free_o = np.sum(o.owner == -1, axis=1).astype(np.int32)
+        assert np.array_equal(snap["free_count"], free_o), t
+
+    def check_blocks(self, t, blocks):
+        slots, ntok, cnt = self.oracle.block_arrays(blocks, self.spin.max_blocks)
+        assert np.array_equal(self.spin.block_count.cpu().numpy(), cnt), t
+        assert np.array_equal(self.spin.block_table.cpu().numpy(), slots), t
+        assert np.array_equal(self.spin.block_ntok.cpu().numpy(), ntok), t
+
+    def check_stats(self):
+        st, per = self.spin.stats()
+        assert st.error_word == 0, st.error_word
+        for b in range(self.w.B):
+            so = self.oracle.stats[b]
+            assert (per[b, 0], per[b, 1], per[b, 2], per[b, 3]) == \
+                (so["hits"], so["misses"], so["evictions"], so["cutoff"]), (b, per[b], so)
+        return st
+
+    # ------------------------------------------------------------------ stepping
+    def run(self, steps=None, out_sample=None, check_every=1, seed=0):
+        """Full stage parity for `steps` steps.  out_sample=None compares every
+        output; an int compares that many (b, g) pairs per step, chosen with a
+        seeded generator, computed one by one by the oracle."""
+        steps = self.T if steps is None else steps
+        rng = np.random.default_rng(seed)
+        total_flips = 0
+        worst = 0.0
+        for t in range(steps):
+            q = self.q_dev[t]
+            self.spin.select(q, scores=self.scores)
+            sel_gpu = self.spin.sel.cpu().numpy()
+            sel_o, flips = self.check_select(t, sel_gpu, self.scores.cpu().numpy())
+            total_flips += flips
+            self.spin.sel.copy_(torch.from_numpy(sel_o.astype(np.int32)))
+            self.spin.resolve_evict(t)
+            blocks = self.oracle.resolve_evict(sel_o, t)
+            if t % check_every == 0 or t == steps - 1:
+                self.check_state(t)
+                self.check_blocks(t, blocks)
+            self.spin.retrieve()
+            self.oracle.retrieve()
+            out = self.spin.attend(q).cpu().numpy()
+            qb = self.draws.q_bits[t]
+            if out_sample is None:
+                want = self.oracle.attend(qb, blocks)
+                err = float(np.max(np.abs(out - want)))
+            else:
+                err = 0.0
+                for _ in range(out_sample):
+                    b = int(rng.integers(self.w.B))
+                    g = int(rng.integers(self.w.Hq))
+                    want = self.oracle.attend_one(qb, b, g, blocks)
+                    err = max(err, float(np.max(np.abs(out[b, g] - want))))
+            worst = max(worst, err)
+            assert err <= OUT_TOL, (t, err)
+        st = self.check_stats()
+        log(f"[parity] {self.w.name}: {steps} steps, hits={st.hits} misses={st.misses} "
+            f"evictions={st.evictions} tie-flips={total_flips} max|out-oracle|={worst:.2e}")
+        return st, worst
+
+    def close(self):
+        self.spin.close()
