@@ -62,6 +62,23 @@ def memcpy_h2d_gbs(nbytes=1 << 30):
     return gbs
 
 
+def hbm_read_gbs(nbytes=2 << 30):
+    """Practical HBM read ceiling: a float32 sum over nbytes (torch reduction)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    return gbs
+
+
 def cpu_baseline(w, geo, draws, host_np, budget_s=20.0):
     """The CPU oracle as it stands, on the same workload from step 0, for as
     many whole decode steps as fit in about budget_s seconds (at least one)."""
@@ -100,6 +117,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--pps", type=int, default=0, help="attention pages per split (0 = auto)")
     ap.add_argument("--single-stream", action="store_true", help="retrieve on the compute stream")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain elementwise copy of 256 MiB three times "
+                         "(reference kernel for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path shards by "
@@ -189,7 +209,7 @@ def main():
     rl = {
         "attend": {"bound": "hbm", "achieved": attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": attend_bytes,
-                   "kernels": ["k_attend_partial", "k_attend_reduce"]},
+                   "kernels": ["k_attend", "k_attend_merge"]},
         "select": {"bound": "hbm", "achieved": score_bytes / (stage_ms["select"] * 1e-3) / 1e9,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
                    "kernels": ["k_score", "k_topk"]},
@@ -219,8 +239,18 @@ def main():
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,
                       "evictions_per_step": evictions / K},
         "pcie": {"link": link, "memcpy_h2d_GBps": memcpy_gbs},
+        "hbm_practical_read_GBps": hbm_read_gbs(),
         "wall_s": wall,
     }
+    if args.copy_calibration:
+        n = 64 << 20  # 64 Mi float32 = 256 MiB read + 256 MiB written per launch
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        line["copy_calibration"] = {"kernel": "elementwise neg (torch)", "bytes_read": 4 * n,
+                                    "bytes_written": 4 * n, "launches": 3}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, geo, draws, [h[1] for h in host], args.cpu_budget)

@@ -17,10 +17,15 @@
 // second MFMA needs for P^T.  P is split into a bf16 high part and a bf16
 // residual so the PV product keeps about 16 mantissa bits of P.
 //
-// Work split: a workgroup of 4 waves takes a run of `pps` pages of one (b, h)
-// (waves interleave pages), keeps an fp32 online softmax per head, merges its
-// waves through LDS and writes one partial (max, sum, unnormalised output).
-// k_attend_reduce merges the partials of a head (log-sum-exp).
+// Work split: a workgroup of 4 waves takes a run of `pps` pages of one (b, h);
+// each wave takes a contiguous quarter of it, keeps an fp32 online softmax per
+// head, and pipelines its page loads (next keys during this page's softmax and
+// PV, next values during the next logits), with the block-table entries of
+// its pages loaded once up front.  The waves merge through LDS.  A head whose
+// pages fit in one workgroup is finished there; otherwise k_attend_merge
+// combines the split partials (log-sum-exp).  (Merging in the last workgroup
+// to finish would need a device-scope fence per workgroup, which writes back
+// the whole L2 on this chip and cost more than the second launch.)
 #include "device_util.h"
 #include "spin_internal.h"
 
@@ -32,10 +37,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t* __restrict__ q,
-                                                           const int* __restrict__ bt,
-                                                           const int* __restrict__ bntok,
-                                                           const int* __restrict__ bcount) {
+// Key tile tt, row r holds token 32 (tt/2) + 8 (r/4) + 4 (tt%2) + r%4: with
+// that order the logits come out of the MFMA in the P^T operand layout.
+__device__ __forceinline__ void load_keys(const uint16_t* K, int r, int g, bf16x8 (&ka)[4][4]) {
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tok = 32 * (tt >> 1) + 8 * (r >> 2) + 4 * (tt & 1) + (r & 3);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      ka[tt][kb] = *reinterpret_cast<const bf16x8*>(K + tok * kHeadDim + 32 * kb + 8 * g);
+  }
+}
+
+// Value tile dt, row r holds dim 16 dt + r; its k-slots are tokens 32 kt + 8 g + 0..7.
+__device__ __forceinline__ void load_values(const uint16_t* Vt, int r, int g, bf16x8 (&va)[8][2]) {
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+      va[dt][kt] = *reinterpret_cast<const bf16x8*>(Vt + (16 * dt + r) * kPageTokens + 32 * kt + 8 * g);
+}
+
+__global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
+                                                   const int* __restrict__ bt,
+                                                   const int* __restrict__ bntok,
+                                                   const int* __restrict__ bcount,
+                                                   float* __restrict__ out) {
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][132];
@@ -44,12 +71,37 @@ __global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t
   const int bh = blockIdx.x / d.splits;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
-  const int cnt = min(bcount[bh], d.max_blocks);
-  const int p_begin = split * d.pps;
-  if (p_begin >= cnt) return;  // whole workgroup: nothing to do
-  const int p_end = min(cnt, p_begin + d.pps);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cnt = max(0, min(bcount[bh], d.max_blocks));
+  const int ns = (cnt + d.pps - 1) / d.pps;  // splits that hold pages
+  const int tid = threadIdx.x;
+  const int hh = tid >> 4, dc = (tid & 15) * 8;  // merge layout: head, 8 dims
+  float* orow = out + ((size_t)b * d.Hq + (size_t)h * G) * kHeadDim;
+  if (cnt == 0) {  // no pages: the head's output is zero
+    if (split == 0 && hh < G) {
+      float4* o4 = reinterpret_cast<float4*>(orow + (size_t)hh * kHeadDim + dc);
+      o4[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      o4[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  if (split >= ns) return;
+  const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
+  const int ppw = d.pps / 4;
+  const int p0 = split * d.pps + wave * ppw;
+  const int np = max(0, min(cnt, p0 + ppw) - p0);  // this wave's pages: p0 .. p0+np-1
+
+  // block-table entries of the wave's pages, one per lane
+  int my_slot = 0, my_nt = 0;
+  if (lane < np) {
+    const int s = bt[(size_t)bh * d.max_blocks + p0 + lane];
+    const int n = bntok[(size_t)bh * d.max_blocks + p0 + lane];
+    // a malformed entry (caller-supplied table) reads slot 0 with every token masked
+    if ((unsigned)s < (unsigned)(d.B * d.C) && n > 0 && n <= kPageTokens) {
+      my_slot = s;
+      my_nt = n;
+    }
+  }
 
   // B operand of the logits MFMA: lane (r, g) holds q[head r][32 kb + 8 g + 0..7]
   bf16x8 qb[4];
@@ -65,83 +117,78 @@ __global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t
   f32x4 acc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;  // running max (log2 units) and this lane's partial sum
+  float m = -INFINITY, l = 0.f;  // running max (log2 units), this lane's partial sum
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const int* btr = bt + (size_t)bh * d.max_blocks;
-  const int* bnr = bntok + (size_t)bh * d.max_blocks;
 
-  for (int p = p_begin + wave; p < p_end; p += 4) {
-    const int slot = btr[p];
-    const int nt = bnr[p];
-    // a malformed entry (caller-supplied table) is skipped rather than read
-    if ((unsigned)slot >= (unsigned)(d.B * d.C) || nt <= 0 || nt > kPageTokens) continue;
-    const uint16_t* K = d.pool + (size_t)slot * kPageElems;
-    const uint16_t* Vt = K + kPageTokens * kHeadDim;
-    // key tile tt, row r holds token 32 (tt/2) + 8 (r/4) + 4 (tt%2) + r%4
-    bf16x8 ka[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int tok = 32 * (tt >> 1) + 8 * (r >> 2) + 4 * (tt & 1) + (r & 3);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        ka[tt][kb] = *reinterpret_cast<const bf16x8*>(K + tok * kHeadDim + 32 * kb + 8 * g);
+  if (np > 0) {
+    // two-stage pipeline: keys of page i+1 load during softmax/PV of page i,
+    // values of page i+1 load during the logits of page i+1
+    bf16x8 ka[4][4], va[8][2];
+    {
+      const uint16_t* P = d.pool + (size_t)__shfl(my_slot, 0, 64) * kPageElems;
+      load_keys(P, r, g, ka);
+      load_values(P + kPageTokens * kHeadDim, r, g, va);
     }
-    // value tile dt, row r holds dim 16 dt + r; k-slots are tokens 32 kt + 8 g + 0..7
-    bf16x8 va[8][2];
+    for (int i = 0; i < np; ++i) {
+      const int nt = __shfl(my_nt, i, 64);
+      f32x4 s[4];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+      for (int tt = 0; tt < 4; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        va[dt][kt] = *reinterpret_cast<const bf16x8*>(Vt + (16 * dt + r) * kPageTokens + 32 * kt + 8 * g);
-
-    f32x4 s[4];
+        for (int kb = 0; kb < 4; ++kb) s[tt] = mfma16x16x32(ka[tt][kb], qb[kb], s[tt]);
+      }
+      // the next page (the last iteration reloads its own page, an L2 hit, so the
+      // buffers stay single registers across the loop)
+      const uint16_t* Pn = d.pool + (size_t)__shfl(my_slot, i + 1 < np ? i + 1 : i, 64) * kPageElems;
+      // keep the key buffer single: its refill may not move above the MFMAs reading it
+      __builtin_amdgcn_sched_barrier(0);
+      load_keys(Pn, r, g, ka);
+      // s[tt][j]: head r, token 32 (tt/2) + 8 g + 4 (tt%2) + j
+      float pm = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[tt] = mfma16x16x32(ka[tt][kb], qb[kb], s[tt]);
+        for (int j = 0; j < 4; ++j) {
+          const int tok = 32 * (tt >> 1) + 8 * g + 4 * (tt & 1) + j;
+          const float x = tok < nt ? s[tt][j] * sl2 : -INFINITY;
+          s[tt][j] = x;
+          pm = fmaxf(pm, x);
+        }
+      pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
+      pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
+      const float mn = fmaxf(m, pm);
+      const bool none = mn == -INFINITY;  // nothing valid seen yet
+      const float alpha = none ? 1.f : exp2f(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+      bf16x8 phi[2], plo[2];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pv = none ? 0.f : exp2f(s[tt][j] - mn);
+          l += pv;
+          const __bf16 hi = (__bf16)pv;
+          phi[tt >> 1][4 * (tt & 1) + j] = hi;
+          plo[tt >> 1][4 * (tt & 1) + j] = (__bf16)(pv - (float)hi);
+        }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc[dt] = mfma16x16x32(va[dt][kt], phi[kt], acc[dt]);
+          acc[dt] = mfma16x16x32(va[dt][kt], plo[kt], acc[dt]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      load_values(Pn + kPageTokens * kHeadDim, r, g, va);
     }
-    // s[tt][i]: head r, token 32 (tt/2) + 8 g + 4 (tt%2) + i
-    float pm = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = 32 * (tt >> 1) + 8 * g + 4 * (tt & 1) + i;
-        const float x = tok < nt ? s[tt][i] * sl2 : -INFINITY;
-        s[tt][i] = x;
-        pm = fmaxf(pm, x);
-      }
-    pm = fmaxf(pm, __shfl_xor(pm, 16, 64));
-    pm = fmaxf(pm, __shfl_xor(pm, 32, 64));
-    const float mn = fmaxf(m, pm);  // finite: every page has a valid token
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    l *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
-    bf16x8 phi[2], plo[2];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = exp2f(s[tt][i] - mn);
-        l += pv;
-        const __bf16 hi = (__bf16)pv;
-        phi[tt >> 1][4 * (tt & 1) + i] = hi;
-        plo[tt >> 1][4 * (tt & 1) + i] = (__bf16)(pv - (float)hi);
-      }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        acc[dt] = mfma16x16x32(va[dt][kt], phi[kt], acc[dt]);
-        acc[dt] = mfma16x16x32(va[dt][kt], plo[kt], acc[dt]);
-      }
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  // acc[dt][i] = unnormalised out[head r][dim 16 dt + 4 g + i]
+  // acc[dt][j] = unnormalised out[head r][dim 16 dt + 4 g + j]
   if (g == 0) {
     sm_m[wave][r] = m;
     sm_l[wave][r] = l;
@@ -149,16 +196,16 @@ __global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm_o[wave][r][16 * dt + 4 * g + i] = acc[dt][i];
+    for (int j = 0; j < 4; ++j) sm_o[wave][r][16 * dt + 4 * g + j] = acc[dt][j];
   __syncthreads();
-  const int hh = threadIdx.x >> 4, dc = (threadIdx.x & 15) * 8;
+
+  // merge the four waves: thread (hh, dc) owns head hh, dims dc .. dc+7
+  float M = -INFINITY, L = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
   if (hh < G) {
-    float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
-    float L = 0.f, o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = sm_m[w][hh];
@@ -167,6 +214,18 @@ __global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] += sm_o[w][hh][dc + e] * f;
     }
+  }
+  if (ns == 1) {  // the whole head in one workgroup: normalise and store
+    if (hh < G) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      float4* o4 = reinterpret_cast<float4*>(orow + (size_t)hh * kHeadDim + dc);
+      o4[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+    }
+    return;
+  }
+  // several splits: publish this split's partial for k_attend_merge
+  if (hh < G) {
     const size_t pi = ((size_t)bh * d.splits + split) * G + hh;
     float4* po = reinterpret_cast<float4*>(d.part_o + pi * kHeadDim + dc);
     po[0] = make_float4(o[0], o[1], o[2], o[3]);
@@ -178,35 +237,47 @@ __global__ __launch_bounds__(kAttWG) void k_attend_partial(Dev d, const uint16_t
   }
 }
 
-// One workgroup of 128 lanes per (request, query head): merge the head's
-// split partials and normalise.
-__global__ __launch_bounds__(128) void k_attend_reduce(Dev d, const int* __restrict__ bcount,
-                                                       float* __restrict__ out) {
-  const int bq = blockIdx.x;
-  const int b = bq / d.Hq, gq = bq - b * d.Hq;
-  const int h = gq / d.G, r = gq - h * d.G;
-  const int bh = b * d.Hkv + h;
-  const int ns = (min(bcount[bh], d.max_blocks) + d.pps - 1) / d.pps;
+// One workgroup per (request, KV head) whose pages span several splits: merge
+// the split partials of its G heads (log-sum-exp) and normalise.  Heads with a
+// single split (or none) were finished by k_attend.
+__global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __restrict__ bcount,
+                                                         float* __restrict__ out) {
+  const int bh = blockIdx.x;
+  const int b = bh / d.Hkv, h = bh - b * d.Hkv;
+  const int G = d.G;
+  const int cnt = max(0, min(bcount[bh], d.max_blocks));
+  const int ns = (cnt + d.pps - 1) / d.pps;
+  if (ns <= 1) return;
+  const int hh = threadIdx.x >> 4, dc = (threadIdx.x & 15) * 8;
+  if (hh >= G) return;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, d.part_ml[2 * (((size_t)bh * d.splits + s) * d.G + r)]);
-  float L = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const size_t pi = ((size_t)bh * d.splits + s) * d.G + r;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, d.part_ml[2 * (((size_t)bh * d.splits + sp) * G + hh)]);
+  float L = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const size_t pi = ((size_t)bh * d.splits + sp) * G + hh;
     const float ms = d.part_ml[2 * pi];
     const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
     L += d.part_ml[2 * pi + 1] * f;
-    o += d.part_o[pi * kHeadDim + threadIdx.x] * f;
+    const float4* po = reinterpret_cast<const float4*>(d.part_o + pi * kHeadDim + dc);
+    const float4 a = po[0], c = po[1];
+    o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
+    o[4] += c.x * f; o[5] += c.y * f; o[6] += c.z * f; o[7] += c.w * f;
   }
-  out[(size_t)bq * kHeadDim + threadIdx.x] = L > 0.f ? o / L : 0.f;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4* o4 = reinterpret_cast<float4*>(out + ((size_t)b * d.Hq + (size_t)h * G + hh) * kHeadDim + dc);
+  o4[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
                          const int* bcount, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_attend_partial, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q,
-                     bt, bntok, bcount);
+  hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q, bt, bntok,
+                     bcount, out);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attend_reduce, dim3(d.B * d.Hq), dim3(kHeadDim), 0, s, d, bcount, out);
+  if (e != hipSuccess || d.splits == 1) return e;
+  hipLaunchKernelGGL(k_attend_merge, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ __global__ void k_init(Dev d) {
     d.host_base[i] = 0;
     d.nmiss[i] = 0;
     d.nfreed[i] = 0;
+    d.nalloc[i] = 0;
     d.stats[4 * i + 0] = 0;
     d.stats[4 * i + 1] = 0;
     d.stats[4 * i + 2] = 0;
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(1024) void k_release(Dev d, int req) {
     d.req_pages[req] = 0;
     d.nmiss[req] = 0;
     d.nfreed[req] = 0;
+    d.nalloc[req] = 0;
   }
 }
 

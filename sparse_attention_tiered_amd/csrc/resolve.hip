@@ -224,7 +224,37 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     }
     assigned = min(acarry, nmiss);
   }
+  __syncthreads();
+
+  // 5. directory ranges that need a segment from the shared pool: the first
+  //    insert of each range whose entry is empty after this request's frees
+  //    (canonical order; inserts of one range are consecutive)
+  int nalloc = 0;
+  {
+    const int ne = Hkv * d.ndir;
+    int ccarry = 0;
+    for (int base = 0; base < assigned; base += 1024) {
+      const int r = base + tid;
+      int fl = 0, e = 0;
+      if (r < assigned) {
+        const int4 m = misses[r];
+        e = m.x * d.ndir + (m.y >> 6);
+        bool first = true;
+        if (r > 0) {
+          const int4 pm = misses[r - 1];
+          first = (pm.x * d.ndir + (pm.y >> 6)) != e;
+        }
+        fl = (first && dir[e] < 0) ? 1 : 0;
+      }
+      int tot;
+      const int ex = block_excl_scan<1024>(fl, tmp, &tot);
+      if (fl) d.alloc[(size_t)b * ne + ccarry + ex] = e;
+      ccarry += tot;
+    }
+    nalloc = ccarry;
+  }
   if (tid == 0) {
+    d.nalloc[b] = nalloc;
     const int ev = need > 0 ? need : 0;
     if (assigned < nmiss) atomicOr(d.err, kErrState);
     d.free_count[b] = freec + ev - assigned;
@@ -238,70 +268,73 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   }
 }
 
-// Shared segment pool: push every request's emptied segments (requests in
-// ascending order), then hand segments out to directory ranges that receive
-// their first resident page, in canonical insert order; then write the
-// inserts into the segments and build the batch-wide fetch list.
+// Shared segment pool, one workgroup for the batch: push every request's
+// emptied segments (requests ascending), hand segments to the directory
+// ranges that k_resolve listed (requests ascending, canonical order), then
+// write the inserts into their segments and build the batch-wide fetch list.
+// Each phase is a flat loop over the batch; a request is found from a flat
+// index by binary search over the per-request prefix sums kept in LDS.
+__device__ __forceinline__ int owner_of(const int* prefix, int nb, int j) {
+  int lo = 0, hi = nb;  // largest b with prefix[b] <= j
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= j) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 __global__ __launch_bounds__(1024) void k_segments(Dev d) {
+  __shared__ int pf[1025], pa[1025], pm[1025];
   __shared__ int tmp[17];
   const int tid = threadIdx.x;
   const int ne = d.Hkv * d.ndir;
-  int top = d.seg_ctl[0];
-  for (int b = 0; b < d.B; ++b) {
-    const int nf = d.nfreed[b];
-    for (int i = tid; i < nf; i += 1024)
-      if (top + i < d.n_seg) d.seg_stack[top + i] = d.freed[(size_t)b * ne + i];
-    top = min(top + nf, d.n_seg);
+  const int B = d.B;
+  int F, A, M;
+  {
+    const int nf = tid < B ? d.nfreed[tid] : 0;
+    const int na = tid < B ? d.nalloc[tid] : 0;
+    const int nm = tid < B ? d.nmiss[tid] : 0;
+    const int xf = block_excl_scan<1024>(nf, tmp, &F);
+    const int xa = block_excl_scan<1024>(na, tmp, &A);
+    const int xm = block_excl_scan<1024>(nm, tmp, &M);
+    if (tid < B) {
+      pf[tid] = xf;
+      pa[tid] = xa;
+      pm[tid] = xm;
+    }
+    __syncthreads();
+  }
+  const int top0 = d.seg_ctl[0];
+  for (int j = tid; j < F; j += 1024) {
+    const int b = owner_of(pf, B, j);
+    const int at = top0 + j;
+    if (at < d.n_seg) d.seg_stack[at] = d.freed[(size_t)b * ne + (j - pf[b])];
+    else atomicOr(d.err, kErrState);
+  }
+  const int top1 = min(top0 + F, d.n_seg);
+  __syncthreads();
+  for (int j = tid; j < A; j += 1024) {
+    const int b = owner_of(pa, B, j);
+    const int e = d.alloc[(size_t)b * ne + (j - pa[b])];
+    const int idx = top1 - 1 - j;
+    if (idx >= 0) d.directory[(size_t)b * ne + e] = d.seg_stack[idx];
+    else atomicOr(d.err, kErrSegPool);
   }
   __syncthreads();
-  int pcarry = 0;
-  for (int b = 0; b < d.B; ++b) {
-    const int nm = d.nmiss[b];
-    const int4* ins = d.ins + (size_t)b * d.max_mand;
-    int* dir = d.directory + (size_t)b * ne;
-    for (int base = 0; base < nm; base += 1024) {
-      const int r = base + tid;
-      int fl = 0, e = 0;
-      if (r < nm) {
-        const int4 m = ins[r];
-        e = m.y * d.ndir + (m.z >> 6);
-        bool first = true;
-        if (r > 0) {
-          const int4 pm = ins[r - 1];
-          first = (pm.y * d.ndir + (pm.z >> 6)) != e;
-        }
-        fl = (first && dir[e] < 0) ? 1 : 0;
-      }
-      int tot;
-      const int ex = block_excl_scan<1024>(fl, tmp, &tot);
-      if (fl) {
-        const int idx = top - 1 - (pcarry + ex);
-        if (idx >= 0) dir[e] = d.seg_stack[idx];
-        else atomicOr(d.err, kErrSegPool);
-      }
-      pcarry += tot;
+  for (int j = tid; j < M; j += 1024) {
+    const int b = owner_of(pm, B, j);
+    const int4 m = d.ins[(size_t)b * d.max_mand + (j - pm[b])];  // (slot, h, page)
+    const int seg = d.directory[(size_t)b * ne + m.y * d.ndir + (m.z >> 6)];
+    if (seg >= 0 && seg < d.n_seg) {
+      d.segments[(size_t)seg * kSegEntries + (m.z & 63)] = m.x;
+      atomicAdd(&d.seg_live[seg], 1);
     }
-  }
-  __syncthreads();
-  int fcarry = 0;
-  for (int b = 0; b < d.B; ++b) {
-    const int nm = d.nmiss[b];
-    const int4* ins = d.ins + (size_t)b * d.max_mand;
-    const int* dir = d.directory + (size_t)b * ne;
-    for (int r = tid; r < nm; r += 1024) {
-      const int4 m = ins[r];  // (slot, h, page)
-      const int seg = dir[m.y * d.ndir + (m.z >> 6)];
-      if (seg >= 0 && seg < d.n_seg) {
-        d.segments[(size_t)seg * kSegEntries + (m.z & 63)] = m.x;
-        atomicAdd(&d.seg_live[seg], 1);
-      }
-      d.fetch[fcarry + r] = make_int4(b * d.C + m.x, b, m.y, m.z);
-    }
-    fcarry += nm;
+    d.fetch[j] = make_int4(b * d.C + m.x, b, m.y, m.z);
   }
   if (tid == 0) {
-    d.seg_ctl[0] = max(top - pcarry, 0);
-    d.fetch_count[0] = fcarry;
+    d.seg_ctl[0] = max(top1 - A, 0);
+    d.fetch_count[0] = M;
   }
 }
 

@@ -21,45 +21,56 @@ constexpr int kScorePerWG = 4 * kScorePerWave;
 
 __global__ __launch_bounds__(kScoreWG) void k_score(Dev d, const uint16_t* __restrict__ q,
                                                     float* __restrict__ scores) {
+  __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];  // the group's bf16 queries
+  __shared__ float sqbar[kHeadDim];               // their sum, times 1 / (G sqrt(128))
   const int bh = blockIdx.y;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int n = d.req_parts[b];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int grp = lane >> 3, r = lane & 7;
   const int p0 = blockIdx.x * kScorePerWG + wave * kScorePerWave;
+  const bool active = p0 < n;
   float* srow = scores + (size_t)bh * d.Nmax;
-  if (p0 >= n) {
+
+  // 1. the group's queries: one 16-byte load per thread, issued first so that
+  //    waiting for it does not wait for the summary loads behind it
+  const int nq = d.G * kHeadDim / 8;
+  uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < nq) qc = reinterpret_cast<const uint4*>(q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim)[tid];
+  // 2. the summaries, branch-free: a row past the request's partitions
+  //    re-reads row p0 and its score is replaced below; group `grp` handles
+  //    partitions p0 + 8 grp + it
+  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
+  float4 v[8][4];
+  if (active) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int p = p0 + 8 * grp + it;
+      const float* row = S + (size_t)(p < n ? p : p0) * kHeadDim + 4 * r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[it][j] = *reinterpret_cast<const float4*>(row + 32 * j);
+    }
+  }
+  // 3. mean query through LDS while the summaries are in flight
+  if (tid < nq) sq[tid] = qc;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    const uint16_t* sq16 = reinterpret_cast<const uint16_t*>(sq);
+    float sum = 0.f;
+    for (int g = 0; g < d.G; ++g) sum += __uint_as_float((uint32_t)sq16[g * kHeadDim + tid] << 16);
+    sqbar[tid] = sum * (1.0f / ((float)d.G * sqrtf((float)kHeadDim)));
+  }
+  __syncthreads();
+  if (!active) {
     if (p0 + lane < d.Nmax) srow[p0 + lane] = -INFINITY;
     return;
   }
-  // Sum of the group's queries on this lane's 16 dims: 32 j + 4 r + e.
   float qv[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) qv[e] = 0.f;
-  const uint16_t* qg = q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim;
-  for (int g = 0; g < d.G; ++g) {
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 u = *reinterpret_cast<const uint2*>(qg + (size_t)g * kHeadDim + 32 * j + 4 * r);
-      qv[4 * j + 0] += bf16_lo(u.x);
-      qv[4 * j + 1] += bf16_hi(u.x);
-      qv[4 * j + 2] += bf16_lo(u.y);
-      qv[4 * j + 3] += bf16_hi(u.y);
-    }
-  }
-  const float scale = 1.0f / ((float)d.G * sqrtf((float)kHeadDim));
-  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
-  // group `grp` handles partitions p0 + 8 grp + it, it = 0..7
-  float4 v[8][4];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int p = p0 + 8 * grp + it;
-    const bool ok = p < n;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[it][j] = ok ? *reinterpret_cast<const float4*>(S + (size_t)p * kHeadDim + 32 * j + 4 * r)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+    for (int e = 0; e < 4; ++e) qv[4 * j + e] = sqbar[32 * j + 4 * r + e];
   float acc[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -81,7 +92,7 @@ __global__ __launch_bounds__(kScoreWG) void k_score(Dev d, const uint16_t* __res
 #pragma unroll
   for (int it = 1; it < 8; ++it) mine = (r == it) ? acc[it] : mine;
   const int p = p0 + lane;
-  if (p < d.Nmax) srow[p] = (p < n) ? mine * scale : -INFINITY;
+  if (p < d.Nmax) srow[p] = (p < n) ? mine : -INFINITY;
 }
 
 // Order-preserving map of float32 to uint32 (larger float -> larger key).

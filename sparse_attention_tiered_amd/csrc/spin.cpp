@@ -47,7 +47,7 @@ int check(const spin_config* c) {
     return SPIN_EINVAL;
   if (c->topk < 1 || c->topk > 1024 || c->num_kv_heads * c->topk > spin::kMaxItems) return SPIN_EINVAL;
   if (c->num_segments < 1 || c->num_segments > (1 << 28)) return SPIN_EINVAL;
-  if (c->attend_pages_per_split < 0 || c->attend_pages_per_split > 4096) return SPIN_EINVAL;
+  if (c->attend_pages_per_split < 0 || c->attend_pages_per_split > 256) return SPIN_EINVAL;
   if (c->slots_per_request < 1 || c->slots_per_request > spin::kMaxSlots) return SPIN_EINVAL;
   if ((long long)c->max_batch * c->slots_per_request > (1LL << 31) / 2) return SPIN_EINVAL;
   // every page one step can need must fit in the request's slots
@@ -62,11 +62,12 @@ Derived derive(const spin_config* c) {
   d.ndir = (c->max_pages + spin::kSegEntries - 1) / spin::kSegEntries;
   d.max_blocks = c->topk * c->max_pages_per_partition;
   d.max_mand = c->num_kv_heads * d.max_blocks;
-  int pps = c->attend_pages_per_split;
+  int pps = (c->attend_pages_per_split + 3) / 4 * 4;  // whole pages per wave
   if (pps == 0) {
-    // aim for about 2048 workgroups over the worst-case page count
+    // about one workgroup per CU over the worst-case page count: long-lived
+    // waves keep their page pipeline full (measured best on MI355X)
     const long long work = (long long)c->max_batch * c->num_kv_heads * d.max_blocks;
-    pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 2047) / 2048));
+    pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 255) / 256));
     pps = (pps + 3) / 4 * 4;
   }
   d.pps = pps;
@@ -78,7 +79,7 @@ Derived derive(const spin_config* c) {
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, host_base, directory, segments,
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, scores, miss_tmp, ins, nmiss,
-      freed, nfreed, fetch, fetch_count, part_o, part_ml, stats, err, total;
+      freed, nfreed, alloc, nalloc, fetch, fetch_count, part_o, part_ml, stats, err, total;
 };
 
 Layout layout(const spin_config* c, const Derived& d) {
@@ -111,6 +112,8 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.nmiss = take(B * sizeof(int));
   L.freed = take(B * Hkv * d.ndir * sizeof(int));
   L.nfreed = take(B * sizeof(int));
+  L.alloc = take(B * Hkv * d.ndir * sizeof(int));
+  L.nalloc = take(B * sizeof(int));
   L.fetch = take(B * d.max_mand * sizeof(int4));
   L.fetch_count = take(4 * sizeof(int));
   L.part_o = take(B * Hkv * d.splits * d.G * spin::kHeadDim * sizeof(float));
@@ -223,6 +226,8 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.nmiss = reinterpret_cast<int*>(w + L.nmiss);
   v.freed = reinterpret_cast<int*>(w + L.freed);
   v.nfreed = reinterpret_cast<int*>(w + L.nfreed);
+  v.alloc = reinterpret_cast<int*>(w + L.alloc);
+  v.nalloc = reinterpret_cast<int*>(w + L.nalloc);
   v.fetch = reinterpret_cast<int4*>(w + L.fetch);
   v.fetch_count = reinterpret_cast<int*>(w + L.fetch_count);
   v.part_o = reinterpret_cast<float*>(w + L.part_o);

@@ -51,6 +51,8 @@ struct Dev {
   int* nmiss;                  // [B]
   int* freed;                  // [B][Hkv * ndir]
   int* nfreed;                 // [B]
+  int* alloc;                  // [B][Hkv * ndir] directory entries that need a segment
+  int* nalloc;                 // [B]
   int4* fetch;                 // [B * max_mand] (global slot, b, h, page)
   int* fetch_count;            // [1]
   float* part_o;               // [B * Hkv * splits][G][128]
