@@ -62,21 +62,26 @@ def memcpy_h2d_gbs(nbytes=1 << 30):
     return gbs
 
 
-def hbm_read_gbs(nbytes=2 << 30):
-    """Practical HBM read ceiling: a float32 sum over nbytes (torch reduction)."""
-    import torch
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    x.sum()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        x.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    gbs = 5 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del x
-    return gbs
+def counter_traffic(cfg_key, stage, bytes_per_launch):
+    """HBM-side bytes per launch of a stage from the committed rocprofv3 counter
+    summary (traffic per algorithmic byte over timed steps), or None when any
+    kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{cfg_key}_hbm_counters.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    lines = [l for l in text.splitlines() if l.startswith("machine-readable: traffic_ratio")]
+    if not lines:
+        return None
+    kv = dict(t.split("=", 1) for t in lines[-1].split()[1:])
+    for src in ("select", "resolve", "retrieve", "attend"):
+        with open(os.path.join(ROOT, "sparse_attention_tiered_amd", "csrc", f"{src}.hip"), "rb") as fh:
+            if hashlib.sha256(fh.read()).hexdigest()[:12] != kv.get(f"sha_{src}"):
+                return None
+    ratio = kv.get(f"traffic_ratio_{stage}")
+    return None if ratio is None else float(ratio) * bytes_per_launch
 
 
 def cpu_baseline(w, geo, draws, host_np, budget_s=20.0):
@@ -117,6 +122,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--pps", type=int, default=0, help="attention pages per split (0 = auto)")
     ap.add_argument("--single-stream", action="store_true", help="retrieve on the compute stream")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="attention waits for the whole retrieve (no resident-page pass)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain elementwise copy of 256 MiB three times "
                          "(reference kernel for the HBM byte counters)")
@@ -152,7 +159,12 @@ def main():
     S = torch.cuda.current_stream()
     Cs = S if args.single_stream else torch.cuda.Stream()
 
+    overlap = not args.single_stream and not args.no_overlap
+
     def step(t, ev=None):
+        # events: 0 start, 1 select done, 2 resolve done, 3 resident-page
+        # attention done (overlapped with retrieve), 4 retrieve done (copy
+        # stream), 5 attention done
         if ev is not None:
             ev[0].record(S)
         spin.select(q[t], stream=S)
@@ -163,16 +175,24 @@ def main():
             ev[2].record(S)
         spin.retrieve(copy_stream=Cs)
         if ev is not None:
-            ev[3].record(Cs)
-        spin.attend(q[t], stream=S)
+            ev[4].record(Cs)
+        if overlap:
+            spin.attend_begin(q[t], stream=S)
+            if ev is not None:
+                ev[3].record(S)
+            spin.attend_finish(q[t], stream=S)
+        else:
+            if ev is not None:
+                ev[3].record(S)
+            spin.attend(q[t], stream=S)
         if ev is not None:
-            ev[4].record(S)
+            ev[5].record(S)
 
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
     st0, _ = spin.stats()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
@@ -186,15 +206,39 @@ def main():
     st1, _ = spin.stats()
     total_ms = start.elapsed_time(end)
     K = args.steps
-    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend": 0.0}
+    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend_resident": 0.0,
+             "attend": 0.0}
     for e in evs:
         stage["select"] += e[0].elapsed_time(e[1])
         stage["resolve_evict"] += e[1].elapsed_time(e[2])
-        stage["retrieve"] += e[2].elapsed_time(e[3])
-        stage["attend"] += e[3].elapsed_time(e[4])
+        stage["retrieve"] += e[2].elapsed_time(e[4])
+        stage["attend_resident"] += e[2].elapsed_time(e[3]) if overlap else 0.0
+        # after the transfer: fetched-page attention and the merge (or the
+        # whole attention without overlap)
+        stage["attend"] += max(e[4].elapsed_time(e[5]), 0.0) if overlap else e[4].elapsed_time(e[5])
     stage_ms = {k: v / K for k, v in stage.items()}
     ms_per_step = total_ms / K
     value = w.B * w.Hq / (ms_per_step * 1e-3)
+
+    # kernel-isolated replays on the last timed step's live data (select and
+    # attention only read the residency state), so the HBM rooflines are not
+    # mixed with the transfer that overlaps them inside a step
+    last = args.warmup + K - 1
+    reps = 10
+    iso = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    torch.cuda.synchronize()
+    iso[0].record(S)
+    for _ in range(reps):
+        spin.select(q[last], stream=S)
+    iso[1].record(S)
+    iso[2].record(S)
+    for _ in range(reps):
+        spin.attend(q[last], stream=S)
+    iso[3].record(S)
+    torch.cuda.synchronize()
+    iso_select_ms = iso[0].elapsed_time(iso[1]) / reps
+    iso_attend_ms = iso[2].elapsed_time(iso[3]) / reps
+    last_pages = int(spin.block_count.sum().item())
 
     hits = st1.hits - st0.hits
     misses = st1.misses - st0.misses
@@ -204,26 +248,35 @@ def main():
     n_parts = sum(len(l) for l in geo.lens)
     score_bytes = w.Hkv * n_parts * 128 * 4 + w.B * w.Hq * 128 * 2 + w.Hkv * n_parts * 4
     retrieve_bytes = misses * PAGE_BYTES / K
+    iso_attend_bytes = last_pages * PAGE_BYTES + w.B * w.Hq * 128 * (2 + 4)
     link = pcie_link()
     memcpy_gbs = memcpy_h2d_gbs()
     rl = {
-        "attend": {"bound": "hbm", "achieved": attend_bytes / (stage_ms["attend"] * 1e-3) / 1e9,
-                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": attend_bytes,
+        "attend": {"bound": "hbm",
+                   "achieved": iso_attend_bytes / (iso_attend_ms * 1e-3) / 1e9,
+                   "launch_ms": iso_attend_ms,
+                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": iso_attend_bytes,
+                   "in_step_bytes_per_step": attend_bytes,
                    "kernels": ["k_attend", "k_attend_merge"]},
-        "select": {"bound": "hbm", "achieved": score_bytes / (stage_ms["select"] * 1e-3) / 1e9,
+        "select": {"bound": "hbm", "achieved": score_bytes / (iso_select_ms * 1e-3) / 1e9,
+                   "launch_ms": iso_select_ms,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
                    "kernels": ["k_score", "k_topk"]},
         "retrieve": {"bound": "pcie",
                      "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if misses else 0.0,
+                     "launch_ms": stage_ms["retrieve"],
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
                      "kernels": ["k_retrieve"]},
     }
     for v in rl.values():
         v["frac"] = v["achieved"] / v["peak"]
-    dominant = max(("attend", "select", "retrieve"), key=lambda k: stage_ms[k])
+    # dominant stage of the step: the transfer, or the HBM kernels run alone
+    dominant = max(("attend", "select", "retrieve"), key=lambda k: rl[k]["launch_ms"])
     roof = dict(rl[dominant])
     roof["stage"] = dominant
-    roof["traffic"] = None
+    roof["traffic"] = counter_traffic(args.config, dominant, roof["bytes_per_launch"])
+    for k, v in rl.items():
+        v["traffic"] = counter_traffic(args.config, k, v["bytes_per_launch"])
     line = {
         "metric": "sparse decode head-tokens/s + achieved HBM GB/s vs peak; H2D GB/s vs PCIe",
         "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -235,11 +288,12 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "stages_ms": stage_ms,
+        "overlap_retrieve_attend": overlap,
         "rooflines": rl,
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,
                       "evictions_per_step": evictions / K},
         "pcie": {"link": link, "memcpy_h2d_GBps": memcpy_gbs},
-        "hbm_practical_read_GBps": hbm_read_gbs(),
+        "hbm_practical_read_GBps": bd.read_stream_gbs(),
         "wall_s": wall,
     }
     if args.copy_calibration:

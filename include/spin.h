@@ -185,8 +185,25 @@ SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_
                          const int32_t* d_block_ntok, const int32_t* d_block_count,
                          float* d_out, void* stream);
 
+/* Retrieve overlapped with attention (the pages' ideal serving envelope
+ * hides the transfer; [XT] problem section, Fig. 1).  spin_attend_begin runs
+ * attention over the pages of the last spin_resolve_evict that were already
+ * resident, without waiting for spin_retrieve, and keeps per-head partials;
+ * spin_attend_finish waits for spin_retrieve, attends the pages it fetched and
+ * merges both passes (log-sum-exp) into d_out.  Both must be given the block
+ * tables written by the last spin_resolve_evict; the result equals spin_attend
+ * up to float32 rounding of the merge. */
+SPIN_API int spin_attend_begin(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                               const int32_t* d_block_ntok, const int32_t* d_block_count,
+                               void* stream);
+SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                                const int32_t* d_block_ntok, const int32_t* d_block_count,
+                                float* d_out, void* stream);
+
 /* One whole decode step: select, resolve_evict, retrieve (on copy_stream),
- * attend.  copy_stream may equal stream. */
+ * attention.  When copy_stream differs from stream, attention over the
+ * resident pages overlaps the retrieve (spin_attend_begin / _finish);
+ * otherwise it is spin_attend after the retrieve. */
 SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream);
@@ -212,6 +229,12 @@ SPIN_API int spin_read_summaries(spin_ctx* ctx, int32_t req, float* host_out);
 /* Synchronise the device and report the device error word: SPIN_OK,
  * SPIN_ESEGPOOL (segment pool exhausted) or SPIN_EDEVICE (other bits). */
 SPIN_API int spin_sync_status(spin_ctx* ctx);
+
+/* Diagnostic, not part of the decode step: read `bytes` (a multiple of 16)
+ * of the device buffer d_buf with a plain streaming kernel on `stream`;
+ * d_sink is a 4-byte device word that keeps the loads alive.  Timing it gives
+ * the practical HBM read ceiling next to the decode kernels. */
+SPIN_API int spin_read_stream(const void* d_buf, size_t bytes, void* d_sink, void* stream);
 
 SPIN_API const char* spin_strerror(int code);
 /* The hipError_t of the last failed HIP call in this context (0 if none). */

@@ -50,11 +50,14 @@ SIGNATURES = {
     "spin_resolve_evict": (c_int, [_P, _P, c_int32, _P, _P, _P, _P]),
     "spin_retrieve": (c_int, [_P, _P]),
     "spin_attend": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "spin_attend_begin": (c_int, [_P, _P, _P, _P, _P, _P]),
+    "spin_attend_finish": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spin_step": (c_int, [_P, _P, c_int32, _P, _P, _P, _P, _P, _P, _P]),
     "spin_get_stats": (c_int, [_P, POINTER(SpinStats), POINTER(c_int64)]),
     "spin_snapshot": (c_int, [_P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P]),
     "spin_read_summaries": (c_int, [_P, c_int32, POINTER(ctypes.c_float)]),
     "spin_sync_status": (c_int, [_P]),
+    "spin_read_stream": (c_int, [_P, c_size_t, _P, _P]),
     "spin_strerror": (c_char_p, [c_int]),
     "spin_last_hip_error": (c_int, [_P]),
 }
@@ -190,6 +193,20 @@ class Spin:
             self.ctx, _ptr(q), _ptr(bt), _ptr(bn), _ptr(bc), _ptr(out), _stream(stream)))
         return out
 
+    def attend_begin(self, q, stream=None):
+        """Attention over the resident pages of the last resolve (overlaps retrieve)."""
+        self._chk("spin_attend_begin", self.lib.spin_attend_begin(
+            self.ctx, _ptr(q), _ptr(self.block_table), _ptr(self.block_ntok),
+            _ptr(self.block_count), _stream(stream)))
+
+    def attend_finish(self, q, out=None, stream=None):
+        """Waits for retrieve, attends the fetched pages, merges into out."""
+        out = self.out if out is None else out
+        self._chk("spin_attend_finish", self.lib.spin_attend_finish(
+            self.ctx, _ptr(q), _ptr(self.block_table), _ptr(self.block_ntok),
+            _ptr(self.block_count), _ptr(out), _stream(stream)))
+        return out
+
     def step(self, q, t, stream=None, copy_stream=None):
         s = _stream(stream)
         cs = _stream(copy_stream) if copy_stream is not None else s
@@ -239,6 +256,25 @@ class Spin:
             self.close()
         except Exception:
             pass
+
+
+def read_stream_gbs(nbytes=4 << 30, reps=5):
+    """Practical HBM read ceiling: GB/s of spin_read_stream over nbytes."""
+    import torch
+    lib = load()
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    s = _stream(None)
+    rc = lib.spin_read_stream(c_void_p(buf.data_ptr()), nbytes, c_void_p(sink.data_ptr()), s)
+    if rc != SPIN_OK:
+        raise SpinError("spin_read_stream", rc)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        lib.spin_read_stream(c_void_p(buf.data_ptr()), nbytes, c_void_p(sink.data_ptr()), s)
+    e1.record()
+    torch.cuda.synchronize()
+    return reps * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
 def pinned_u16(n_elems: int):

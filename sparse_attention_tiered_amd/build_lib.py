@@ -28,7 +28,8 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["spin.cpp", "index.hip", "select.hip", "resolve.hip", "retrieve.hip", "attend.hip"]
+SOURCES = ["spin.cpp", "index.hip", "select.hip", "resolve.hip", "retrieve.hip", "attend.hip",
+           "diag.hip"]
 
 
 def _compile(src: str) -> str:

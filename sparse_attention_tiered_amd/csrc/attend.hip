@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
                                                    const int* __restrict__ bt,
                                                    const int* __restrict__ bntok,
                                                    const int* __restrict__ bcount,
-                                                   float* __restrict__ out) {
+                                                   float* __restrict__ out, int mode) {
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][132];
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   const int hh = tid >> 4, dc = (tid & 15) * 8;  // merge layout: head, 8 dims
   float* orow = out + ((size_t)b * d.Hq + (size_t)h * G) * kHeadDim;
   if (cnt == 0) {  // no pages: the head's output is zero
-    if (split == 0 && hh < G) {
+    if (mode == kAttendAll && split == 0 && hh < G) {
       float4* o4 = reinterpret_cast<float4*>(orow + (size_t)hh * kHeadDim + dc);
       o4[0] = make_float4(0.f, 0.f, 0.f, 0.f);
       o4[1] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -91,17 +91,22 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   const int p0 = split * d.pps + wave * ppw;
   const int np = max(0, min(cnt, p0 + ppw) - p0);  // this wave's pages: p0 .. p0+np-1
 
-  // block-table entries of the wave's pages, one per lane
+  // block-table entries of the wave's pages, one per lane; in the two
+  // overlapped passes a wave keeps only the resident or only the fetched ones
   int my_slot = 0, my_nt = 0;
+  bool keep = false;
   if (lane < np) {
-    const int s = bt[(size_t)bh * d.max_blocks + p0 + lane];
-    const int n = bntok[(size_t)bh * d.max_blocks + p0 + lane];
+    const size_t e = (size_t)bh * d.max_blocks + p0 + lane;
+    const int s = bt[e];
+    const int n = bntok[e];
     // a malformed entry (caller-supplied table) reads slot 0 with every token masked
     if ((unsigned)s < (unsigned)(d.B * d.C) && n > 0 && n <= kPageTokens) {
       my_slot = s;
       my_nt = n;
     }
+    keep = mode == kAttendAll || (d.bmiss[e] != 0) == (mode == kAttendFetched);
   }
+  unsigned long long pages = __ballot(keep);  // lanes holding this wave's pages, in order
 
   // B operand of the logits MFMA: lane (r, g) holds q[head r][32 kb + 8 g + 0..7]
   bf16x8 qb[4];
@@ -120,17 +125,22 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   float m = -INFINITY, l = 0.f;  // running max (log2 units), this lane's partial sum
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
-  if (np > 0) {
-    // two-stage pipeline: keys of page i+1 load during softmax/PV of page i,
-    // values of page i+1 load during the logits of page i+1
+  if (pages != 0) {
+    // two-stage pipeline: keys of the next page load during softmax/PV of this
+    // one, values of the next page load during the next logits
     bf16x8 ka[4][4], va[8][2];
+    int cur = __builtin_ctzll(pages);
+    pages &= pages - 1;
     {
-      const uint16_t* P = d.pool + (size_t)__shfl(my_slot, 0, 64) * kPageElems;
+      const uint16_t* P = d.pool + (size_t)__shfl(my_slot, cur, 64) * kPageElems;
       load_keys(P, r, g, ka);
       load_values(P + kPageTokens * kHeadDim, r, g, va);
     }
-    for (int i = 0; i < np; ++i) {
-      const int nt = __shfl(my_nt, i, 64);
+    while (true) {
+      const int nt = __shfl(my_nt, cur, 64);
+      // the next page (the last one reloads itself, an L2 hit, so the buffers
+      // stay single registers across the loop)
+      const int nxt = pages != 0 ? __builtin_ctzll(pages) : cur;
       f32x4 s[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -138,9 +148,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) s[tt] = mfma16x16x32(ka[tt][kb], qb[kb], s[tt]);
       }
-      // the next page (the last iteration reloads its own page, an L2 hit, so the
-      // buffers stay single registers across the loop)
-      const uint16_t* Pn = d.pool + (size_t)__shfl(my_slot, i + 1 < np ? i + 1 : i, 64) * kPageElems;
+      const uint16_t* Pn = d.pool + (size_t)__shfl(my_slot, nxt, 64) * kPageElems;
       // keep the key buffer single: its refill may not move above the MFMAs reading it
       __builtin_amdgcn_sched_barrier(0);
       load_keys(Pn, r, g, ka);
@@ -184,6 +192,9 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
         }
       __builtin_amdgcn_sched_barrier(0);
       load_values(Pn + kPageTokens * kHeadDim, r, g, va);
+      if (pages == 0) break;
+      cur = nxt;
+      pages &= pages - 1;
     }
   }
   l += __shfl_xor(l, 16, 64);
@@ -215,7 +226,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
       for (int e = 0; e < 8; ++e) o[e] += sm_o[w][hh][dc + e] * f;
     }
   }
-  if (ns == 1) {  // the whole head in one workgroup: normalise and store
+  if (mode == kAttendAll && ns == 1) {  // the whole head in one workgroup: normalise and store
     if (hh < G) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
       float4* o4 = reinterpret_cast<float4*>(orow + (size_t)hh * kHeadDim + dc);
@@ -224,9 +235,11 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
     }
     return;
   }
-  // several splits: publish this split's partial for k_attend_merge
+  // publish this split's partial for k_attend_merge (fetched-page partials
+  // sit after the resident-page ones)
   if (hh < G) {
-    const size_t pi = ((size_t)bh * d.splits + split) * G + hh;
+    const int slot_s = mode == kAttendFetched ? d.splits + split : split;
+    const size_t pi = ((size_t)bh * 2 * d.splits + slot_s) * G + hh;
     float4* po = reinterpret_cast<float4*>(d.part_o + pi * kHeadDim + dc);
     po[0] = make_float4(o[0], o[1], o[2], o[3]);
     po[1] = make_float4(o[4], o[5], o[6], o[7]);
@@ -237,26 +250,30 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   }
 }
 
-// One workgroup per (request, KV head) whose pages span several splits: merge
-// the split partials of its G heads (log-sum-exp) and normalise.  Heads with a
-// single split (or none) were finished by k_attend.
+// One workgroup per (request, KV head): merge its split partials (log-sum-exp)
+// and normalise.  `both` merges the resident-page and fetched-page passes;
+// otherwise only heads spanning several splits need it (the rest were
+// finished by k_attend).
 __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __restrict__ bcount,
-                                                         float* __restrict__ out) {
+                                                         float* __restrict__ out, int both) {
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
   const int ns = (cnt + d.pps - 1) / d.pps;
-  if (ns <= 1) return;
+  if (!both && ns <= 1) return;
   const int hh = threadIdx.x >> 4, dc = (threadIdx.x & 15) * 8;
   if (hh >= G) return;
+  const int nslot = both ? 2 * ns : ns;
+  auto slot_of = [&](int k) { return k < ns ? k : d.splits + (k - ns); };
   float M = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, d.part_ml[2 * (((size_t)bh * d.splits + sp) * G + hh)]);
+  for (int k = 0; k < nslot; ++k)
+    M = fmaxf(M, d.part_ml[2 * (((size_t)bh * 2 * d.splits + slot_of(k)) * G + hh)]);
   float L = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  for (int sp = 0; sp < ns; ++sp) {
-    const size_t pi = ((size_t)bh * d.splits + sp) * G + hh;
+  for (int k = 0; k < nslot; ++k) {
+    const size_t pi = ((size_t)bh * 2 * d.splits + slot_of(k)) * G + hh;
     const float ms = d.part_ml[2 * pi];
     const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
     L += d.part_ml[2 * pi + 1] * f;
@@ -272,12 +289,14 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
 }
 
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                         const int* bcount, float* out, hipStream_t s) {
+                         const int* bcount, float* out, int mode, hipStream_t s) {
   hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q, bt, bntok,
-                     bcount, out);
+                     bcount, out, mode);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || d.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_merge, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out);
+  if (e != hipSuccess || mode == kAttendResident) return e;
+  const int both = mode == kAttendFetched;
+  if (!both && d.splits == 1) return e;
+  hipLaunchKernelGGL(k_attend_merge, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out, both);
   return hipGetLastError();
 }
 

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
             atomicOr(&mand[slot >> 5], 1u << (slot & 31));
             btb[h * MB + pos0 + j] = b * C + slot;
             bnb[h * MB + pos0 + j] = ntok;
+            d.bmiss[((size_t)b * Hkv + h) * MB + pos0 + j] = 0;
           } else {
             missmask |= 1u << j;
             ++nm;
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         last[c] = t;
         btb[m.x * MB + m.z] = b * C + c;
         bnb[m.x * MB + m.z] = m.w;
+        d.bmiss[((size_t)b * Hkv + m.x) * MB + m.z] = 1;
         d.ins[(size_t)b * d.max_mand + r] = make_int4(c, m.x, m.y, 0);
       }
       acarry += tot;

@@ -79,7 +79,7 @@ Derived derive(const spin_config* c) {
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, host_base, directory, segments,
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, scores, miss_tmp, ins, nmiss,
-      freed, nfreed, alloc, nalloc, fetch, fetch_count, part_o, part_ml, stats, err, total;
+      freed, nfreed, alloc, nalloc, fetch, fetch_count, bmiss, part_o, part_ml, stats, err, total;
 };
 
 Layout layout(const spin_config* c, const Derived& d) {
@@ -116,8 +116,9 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.nalloc = take(B * sizeof(int));
   L.fetch = take(B * d.max_mand * sizeof(int4));
   L.fetch_count = take(4 * sizeof(int));
-  L.part_o = take(B * Hkv * d.splits * d.G * spin::kHeadDim * sizeof(float));
-  L.part_ml = take(B * Hkv * d.splits * d.G * 2 * sizeof(float));
+  L.bmiss = take(B * Hkv * d.max_blocks);
+  L.part_o = take(B * Hkv * 2 * d.splits * d.G * spin::kHeadDim * sizeof(float));
+  L.part_ml = take(B * Hkv * 2 * d.splits * d.G * 2 * sizeof(float));
   L.stats = take(B * 4 * sizeof(long long));
   L.err = take(4 * sizeof(int));
   L.total = o;
@@ -230,6 +231,7 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.nalloc = reinterpret_cast<int*>(w + L.nalloc);
   v.fetch = reinterpret_cast<int4*>(w + L.fetch);
   v.fetch_count = reinterpret_cast<int*>(w + L.fetch_count);
+  v.bmiss = reinterpret_cast<unsigned char*>(w + L.bmiss);
   v.part_o = reinterpret_cast<float*>(w + L.part_o);
   v.part_ml = reinterpret_cast<float*>(w + L.part_ml);
   v.stats = reinterpret_cast<long long*>(w + L.stats);
@@ -353,7 +355,30 @@ SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_
   if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
   HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
   HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
-                                  d_block_ntok, d_block_count, d_out, S(stream)));
+                                  d_block_ntok, d_block_count, d_out, spin::kAttendAll, S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_attend_begin(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                               const int32_t* d_block_ntok, const int32_t* d_block_count,
+                               void* stream) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count) return SPIN_EINVAL;
+  if (!aligned(d_q, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
+                                  d_block_ntok, d_block_count, nullptr, spin::kAttendResident,
+                                  S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                                const int32_t* d_block_ntok, const int32_t* d_block_count,
+                                float* d_out, void* stream) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
+  if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
+  HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
+                                  d_block_ntok, d_block_count, d_out, spin::kAttendFetched,
+                                  S(stream)));
   return SPIN_OK;
 }
 
@@ -363,7 +388,13 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
   int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
   if (!rc) rc = spin_resolve_evict(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream);
   if (!rc) rc = spin_retrieve(ctx, copy_stream);
-  if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+  if (copy_stream == stream) {
+    if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+  } else {
+    // attention over the resident pages overlaps the transfer of the others
+    if (!rc) rc = spin_attend_begin(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
+    if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+  }
   return rc;
 }
 
@@ -431,6 +462,13 @@ SPIN_API int spin_sync_status(spin_ctx* ctx) {
   HIPCHK(ctx, hipMemcpy(&err, ctx->dev.err, sizeof(int), hipMemcpyDeviceToHost));
   if (err & SPIN_DEVERR_SEGPOOL) return SPIN_ESEGPOOL;
   if (err) return SPIN_EDEVICE;
+  return SPIN_OK;
+}
+
+SPIN_API int spin_read_stream(const void* d_buf, size_t bytes, void* d_sink, void* stream) {
+  if (!d_buf || !d_sink || bytes < 16 || !aligned(d_buf, 16)) return SPIN_EINVAL;
+  if (spin::launch_read_stream(d_buf, bytes, static_cast<unsigned*>(d_sink), S(stream)) != hipSuccess)
+    return SPIN_EHIP;
   return SPIN_OK;
 }
 

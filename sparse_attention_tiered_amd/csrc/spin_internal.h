@@ -55,8 +55,9 @@ struct Dev {
   int* nalloc;                 // [B]
   int4* fetch;                 // [B * max_mand] (global slot, b, h, page)
   int* fetch_count;            // [1]
-  float* part_o;               // [B * Hkv * splits][G][128]
-  float* part_ml;              // [B * Hkv * splits][G][2] (max in log2 units, sum)
+  unsigned char* bmiss;        // [B][Hkv][max_blocks] 1 = block fetched by this step's retrieve
+  float* part_o;               // [B * Hkv][2 * splits][G][128]
+  float* part_ml;              // [B * Hkv][2 * splits][G][2] (max in log2 units, sum)
   long long* stats;            // [B][4] hits, misses, evictions, last cutoff
   int* err;                    // [1] error bits
   uint16_t* pool;              // [B * C][kPageElems]
@@ -71,7 +72,11 @@ hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t 
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
+hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
+// mode 0: every block, finished output; 1: resident blocks only, partials;
+// 2: fetched blocks only, partials, then the merge of both passes
+enum AttendMode { kAttendAll = 0, kAttendResident = 1, kAttendFetched = 2 };
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                         const int* bcount, float* out, hipStream_t s);
+                         const int* bcount, float* out, int mode, hipStream_t s);
 
 }  // namespace spin

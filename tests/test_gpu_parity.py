@@ -68,13 +68,16 @@ def test_split_sizes_agree(spin_lib):
     assert np.max(np.abs(outs[0] - outs[1])) < 1e-5 and np.max(np.abs(outs[0] - outs[2])) < 1e-5
 
 
-def test_whole_step_call_matches_stages(spin_lib):
-    """spin_step (one call, retrieve on a second stream) gives the same state and
-    outputs as the stage-by-stage calls."""
+@pytest.mark.parametrize("pps", [0, 4])
+def test_whole_step_call_matches_stages(spin_lib, pps):
+    """spin_step with a second stream (retrieve overlapped with attention over
+    the resident pages) gives the same state as the stage-by-stage calls and
+    the same outputs up to the rounding of the two-pass merge; both match the
+    oracle."""
     import torch
-    w = W.variant(W.C4, B=3, ctx=12000, k=16, steps=8)
-    a = _pair(w, slots=8 * 16 + 16, oracle=False)
-    b = _pair(w, slots=8 * 16 + 16, oracle=False)
+    w = W.variant(W.C4, B=3, ctx=12000, k=16, steps=8, ar_coef=0.5)
+    a = _pair(w, slots=8 * 16 + 16, attend_pps=pps)
+    b = _pair(w, slots=8 * 16 + 16, attend_pps=pps, oracle=False)
     side = torch.cuda.Stream()
     for t in range(w.steps):
         a.spin.step(a.q_dev[t], t, copy_stream=side)
@@ -83,12 +86,37 @@ def test_whole_step_call_matches_stages(spin_lib):
         b.spin.retrieve()
         b.spin.attend(b.q_dev[t])
         torch.cuda.synchronize()
-        assert torch.equal(a.spin.out, b.spin.out), t
+        assert torch.equal(a.spin.sel, b.spin.sel), t
+        assert torch.max(torch.abs(a.spin.out - b.spin.out)).item() < 1e-5, t
+        sel_o, blocks, out_o = a.oracle.step(a.draws.q_bits[t], t)
+        assert np.array_equal(a.spin.sel.cpu().numpy(), sel_o), t
+        assert np.max(np.abs(a.spin.out.cpu().numpy() - out_o)) < 2e-3, t
+    st, _ = a.spin.stats()
+    assert st.misses > 0 and st.hits > 0
     sa, sb = a.spin.snapshot(), b.spin.snapshot()
     for k in sa:
         assert np.array_equal(sa[k], sb[k]), k
     a.close()
     b.close()
+
+
+def test_overlapped_attention_calls(spin_lib):
+    """attend_begin / attend_finish on one stream equal spin_attend (every
+    block a hit, every block a miss, and mixed steps)."""
+    import torch
+    w = W.variant(W.C2, B=2, ctx=(9000, 5000), k=8, steps=6, ar_coef=0.3)
+    p = _pair(w, slots=8 * 8 + 8, oracle=False, attend_pps=8)
+    ref = torch.empty_like(p.spin.out)
+    for t in range(w.steps):
+        p.spin.select(p.q_dev[t])
+        p.spin.resolve_evict(t)
+        p.spin.retrieve()
+        p.spin.attend(p.q_dev[t], out=ref)
+        p.spin.attend_begin(p.q_dev[t])
+        p.spin.attend_finish(p.q_dev[t])
+        torch.cuda.synchronize()
+        assert torch.max(torch.abs(ref - p.spin.out)).item() < 1e-5, t
+    p.close()
 
 
 def test_bad_partition_id_sets_error_word(spin_lib):
