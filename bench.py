@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--single-stream", action="store_true", help="retrieve on the compute stream")
     ap.add_argument("--no-overlap", action="store_true",
                     help="attention waits for the whole retrieve (no resident-page pass)")
+    ap.add_argument("--budget-ratio", type=float, default=None,
+                    help="buffer elasticity ablation: each request's budget = mandatory pages "
+                         "x (1 + ratio), capped by its slots (0 = no buffer pages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain elementwise copy of 256 MiB three times "
                          "(reference kernel for the HBM byte counters)")
@@ -155,6 +158,12 @@ def main():
     for b in range(w.B):
         spin.index(b, host[b][0], w.ctx[b], geo.lens[b] if w.var_len is not None else None)
     log(f"[bench] index (summaries over PCIe) {time.time() - t0:.2f}s; attend splits={spin.splits}")
+    budget = w.slots_per_request
+    if args.budget_ratio is not None:
+        mand = w.Hkv * w.k * geo.max_ppp
+        budget = min(w.slots_per_request, int(round(mand * (1 + args.budget_ratio))))
+        for b in range(w.B):
+            spin.set_budget(b, budget)
     q = torch.from_numpy(draws.q_bits.view(np.int16)).to("cuda")
     S = torch.cuda.current_stream()
     Cs = S if args.single_stream else torch.cuda.Stream()
@@ -284,6 +293,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "context": w.ctx[0], "topk": w.k, "slots_per_request": w.slots_per_request,
+                   "budget_per_request": budget,
                    "partitions": "variable 16-256" if w.var_len else "fixed 64",
                    "parallelism": "single-gpu"},
         "roofline": roof,

@@ -145,6 +145,15 @@ SPIN_API int spin_destroy(spin_ctx* ctx);
 SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_tokens,
                         const int32_t* part_lens, int32_t n_parts, void* stream);
 
+/* Buffer elasticity ([XT] part 2; [GP] B): set request `req`'s budget, the
+ * most pages it may keep resident, between Hkv * topk *
+ * max_pages_per_partition (SPIN_ECAPACITY below) and slots_per_request
+ * (SPIN_EINVAL above).  Stream-ordered; nothing is evicted at once: the next
+ * spin_resolve_evict reclaims the excess with the bucketed LRU (its shortfall
+ * is resident + misses - budget).  spin_index / spin_release reset the budget
+ * to slots_per_request. */
+SPIN_API int spin_set_budget(spin_ctx* ctx, int32_t req, int32_t slots, void* stream);
+
 /* Return request `req`'s slots and second-level segments to the free state;
  * the request then has no partitions.  Synchronises `stream`. */
 SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream);

@@ -34,6 +34,7 @@ What each part follows:
                    residency check through the two-level table, mandatory vs
                    buffer pages, 64-bucket LRU reclaim oldest bucket first
                    until the demand is met; [GP] B: pages are per KV head.
+  set_budget()     [XT] part 2 buffer elasticity: per-request budget.
   retrieve()       [XT] part 2 / Fig. 5 steps 3-4: host address from the CPU
                    page table, copy of the missed pages.
   attend()         [XT] part 1 / Fig. 3: attention over the selected
@@ -140,6 +141,9 @@ class SpinOracle:
         self.last_use = np.full((B, self.C), FREE, np.int64)
         self.pool = np.zeros((B * self.C, PAGE_ELEMS), np.uint16)
         self.requests = [None] * B
+        # per-request cap on resident pages ([XT] part 2, buffer elasticity);
+        # it starts at the request's full area
+        self.budget = [slots_per_request] * B
         self.error = None
         self.stats = [dict(hits=0, misses=0, evictions=0, cutoff=-1) for _ in range(B)]
         self._pending = []   # (global slot, b, h, page) copies for retrieve()
@@ -157,6 +161,7 @@ class SpinOracle:
                     self.directory[b, h, e] = FREE
         self.owner[b, :] = FREE
         self.last_use[b, :] = FREE
+        self.budget[b] = self.C
         self.requests[b] = None
 
     def index(self, b: int, host_pages: np.ndarray, lens: np.ndarray):
@@ -215,6 +220,15 @@ class SpinOracle:
         return sel, sc
 
     # ------------------------------------------------------------------ Retrieve: residency + eviction
+    def set_budget(self, b: int, slots: int):
+        """Buffer elasticity ([XT] part 2; [GP] B): the scheduler resizes a
+        request's GPU buffer with load.  Reading: the budget caps the number of
+        resident pages of the request (at least the pages one step can need,
+        at most its slot area); shrinking evicts nothing at once, the next
+        resolve reclaims the excess through the same bucketed LRU."""
+        assert 1 <= slots <= self.C
+        self.budget[b] = int(slots)
+
     def translate(self, b: int, h: int, page: int) -> int:
         """Two-level lookup ([XT] part 3 / Fig. 6): directory entry -> segment ->
         slot.  FREE when the page is not resident."""
@@ -328,8 +342,11 @@ class SpinOracle:
                 else:
                     blocks[b][h].append([None, ntok])
                     misses.append((h, page, len(blocks[b][h]) - 1))
-            n_free = int(np.sum(self.owner[b] == FREE))
-            need = max(0, len(misses) - n_free)
+            # the shortfall against the request's budget: resident pages plus
+            # the misses, minus what the budget allows (with the budget equal
+            # to the whole area this is misses minus free slots)
+            n_resident = int(np.sum(self.owner[b] != FREE))
+            need = max(0, n_resident + len(misses) - self.budget[b])
             st = self.stats[b]
             st["hits"] += len(M) - len(misses)
             st["misses"] += len(misses)

@@ -46,6 +46,7 @@ SIGNATURES = {
     "spin_destroy": (c_int, [_P]),
     "spin_index": (c_int, [_P, c_int32, _P, c_int64, _I32P, c_int32, _P]),
     "spin_release": (c_int, [_P, c_int32, _P]),
+    "spin_set_budget": (c_int, [_P, c_int32, c_int32, _P]),
     "spin_select": (c_int, [_P, _P, _P, _P, _P]),
     "spin_resolve_evict": (c_int, [_P, _P, c_int32, _P, _P, _P, _P]),
     "spin_retrieve": (c_int, [_P, _P]),
@@ -164,6 +165,9 @@ class Spin:
             self.ctx, req, c_void_p(host_kv.data_ptr()) if host_kv is not None else None,
             int(n_tokens), lens_p, n_parts, _stream(stream)))
         self._host[req] = host_kv  # keep the pinned buffer alive
+
+    def set_budget(self, req, slots, stream=None):
+        self._chk("spin_set_budget", self.lib.spin_set_budget(self.ctx, req, int(slots), _stream(stream)))
 
     def release(self, req, stream=None):
         self._chk("spin_release", self.lib.spin_release(self.ctx, req, _stream(stream)))

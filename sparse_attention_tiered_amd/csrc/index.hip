@@ -27,6 +27,7 @@ __global__ void k_init(Dev d) {
   }
   for (size_t i = tid; i < (size_t)d.B; i += nth) {
     d.free_count[i] = d.C;
+    d.budget[i] = d.C;
     d.req_parts[i] = 0;
     d.req_pages[i] = 0;
     d.host_base[i] = 0;
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(1024) void k_release(Dev d, int req) {
   if (tid == 0) {
     d.seg_ctl[0] = min(top + carry, d.n_seg);
     d.free_count[req] = d.C;
+    d.budget[req] = d.C;
     d.req_parts[req] = 0;
     d.req_pages[req] = 0;
     d.nmiss[req] = 0;
@@ -116,6 +118,13 @@ hipError_t launch_init(const Dev& d, hipStream_t s) {
 
 hipError_t launch_release(const Dev& d, int req, hipStream_t s) {
   hipLaunchKernelGGL(k_release, dim3(1), dim3(1024), 0, s, d, req);
+  return hipGetLastError();
+}
+
+__global__ void k_set_budget(Dev d, int req, int slots) { d.budget[req] = slots; }
+
+hipError_t launch_set_budget(const Dev& d, int req, int slots, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_budget, dim3(1), dim3(1), 0, s, d, req, slots);
   return hipGetLastError();
 }
 

@@ -131,9 +131,11 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   const int nmiss = mcarry;
   __syncthreads();
 
-  // 3. bucketed LRU, only when the misses outnumber the free slots
+  // 3. bucketed LRU, only when the resident pages plus the misses exceed the
+  //    request's budget (with the budget at the whole area: when the misses
+  //    outnumber the free slots); a shrunk budget is enforced here, lazily
   const int freec = d.free_count[b];
-  const int need = nmiss - freec;
+  const int need = (C - freec) + nmiss - d.budget[b];
   int nfreed = 0, cut = -1;
   if (need > 0) {
     if (tid < kBuckets) hist[tid] = 0;

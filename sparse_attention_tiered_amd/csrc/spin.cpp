@@ -78,7 +78,7 @@ Derived derive(const spin_config* c) {
 // Byte offsets of every workspace region (each 256-byte aligned).
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, host_base, directory, segments,
-      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, scores, miss_tmp, ins, nmiss,
+      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, miss_tmp, ins, nmiss,
       freed, nfreed, alloc, nalloc, fetch, fetch_count, bmiss, part_o, part_ml, stats, err, total;
 };
 
@@ -106,6 +106,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.owner = take(B * C * sizeof(int));
   L.last_use = take(B * C * sizeof(int));
   L.free_count = take(B * sizeof(int));
+  L.budget = take(B * sizeof(int));
   L.scores = take(B * Hkv * N * sizeof(float));
   L.miss_tmp = take(B * d.max_mand * sizeof(int4));
   L.ins = take(B * d.max_mand * sizeof(int4));
@@ -221,6 +222,7 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.owner = reinterpret_cast<int*>(w + L.owner);
   v.last_use = reinterpret_cast<int*>(w + L.last_use);
   v.free_count = reinterpret_cast<int*>(w + L.free_count);
+  v.budget = reinterpret_cast<int*>(w + L.budget);
   v.scores = reinterpret_cast<float*>(w + L.scores);
   v.miss_tmp = reinterpret_cast<int4*>(w + L.miss_tmp);
   v.ins = reinterpret_cast<int4*>(w + L.ins);
@@ -261,6 +263,15 @@ SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream) {
   if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
   HIPCHK(ctx, spin::launch_release(ctx->dev, req, S(stream)));
   HIPCHK(ctx, hipStreamSynchronize(S(stream)));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_set_budget(spin_ctx* ctx, int32_t req, int32_t slots, void* stream) {
+  if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
+  const spin_config& c = ctx->cfg;
+  if (slots > c.slots_per_request) return SPIN_EINVAL;
+  if (slots < c.num_kv_heads * c.topk * c.max_pages_per_partition) return SPIN_ECAPACITY;
+  HIPCHK(ctx, spin::launch_set_budget(ctx->dev, req, slots, S(stream)));
   return SPIN_OK;
 }
 

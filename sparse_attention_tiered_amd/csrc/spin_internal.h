@@ -44,6 +44,7 @@ struct Dev {
   int* owner;                  // [B][C] h * max_pages + page, or -1
   int* last_use;               // [B][C]
   int* free_count;             // [B]
+  int* budget;                 // [B] cap on resident pages (<= C)
   // per-step scratch
   float* scores;               // [B][Hkv][Nmax]
   int4* miss_tmp;              // [B][max_mand] (h, page, block position, valid tokens)
@@ -66,6 +67,7 @@ struct Dev {
 // launchers (each returns the hipError_t of its launch)
 hipError_t launch_init(const Dev& d, hipStream_t s);
 hipError_t launch_release(const Dev& d, int req, hipStream_t s);
+hipError_t launch_set_budget(const Dev& d, int req, int slots, hipStream_t s);
 hipError_t launch_index(const Dev& d, int req, int n_parts, hipStream_t s);
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s);
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);

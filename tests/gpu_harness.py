@@ -127,7 +127,7 @@ class Pair:
         return st
 
     # ------------------------------------------------------------------ stepping
-    def run(self, steps=None, out_sample=None, check_every=1, seed=0):
+    def run(self, steps=None, out_sample=None, check_every=1, seed=0, on_step=None):
         """Full stage parity for `steps` steps.  out_sample=None compares every
         output; an int compares that many (b, g) pairs per step, chosen with a
         seeded generator, computed one by one by the oracle."""
@@ -136,6 +136,8 @@ class Pair:
         total_flips = 0
         worst = 0.0
         for t in range(steps):
+            if on_step is not None:
+                on_step(t)
             q = self.q_dev[t]
             self.spin.select(q, scores=self.scores)
             sel_gpu = self.spin.sel.cpu().numpy()

@@ -515,9 +515,37 @@ def pin_first_step_slots(om):
         assert ntok == want
 
 
+def pin_budget_shrink(om):
+    """Worked by hand.  One request, one KV head, k = 2 fixed partitions, 8
+    slots.  Steps 0-3 select {0,1}, {2,3}, {4,5}, {6,7}: eight misses fill slots
+    0..7 (last_use 0,0,1,1,2,2,3,3).  The budget then drops to 4.  Step 4
+    selects {6, 8}: page 6 hits (slot 6), page 8 misses; resident 8 + 1 miss -
+    budget 4 = 5 pages must go.  Candidates (all but slot 6): ages at t = 4 are
+    4,4,3,3,2,2,-,1 -> buckets 59,59,60,60,61,61,-,62.  Taking whole buckets
+    from the oldest: {0,1} (59), {2,3} (60) = 4, then one more from bucket 61:
+    slot 4.  Page 8 goes to the lowest free slot, 0.  Growing the budget back
+    to 8 evicts nothing more."""
+    Kp = [[np.full((64, D), 0.0, np.float32) for _ in range(10)]]
+    Vp = [[np.zeros((64, D), np.float32) for _ in range(10)]]
+    buf, lens = pack_request(Kp, Vp, 1)
+    o = make(om, 1, 1, 1, 2, 8, 10)
+    o.index(0, buf, lens)
+    for t, pair in enumerate([(0, 1), (2, 3), (4, 5), (6, 7)]):
+        o.resolve_evict(np.array([[pair]]), t)
+    assert list(o.owner[0]) == [0, 1, 2, 3, 4, 5, 6, 7]
+    o.set_budget(0, 4)
+    blocks = o.resolve_evict(np.array([[(6, 8)]]), 4)
+    assert o.stats[0]["evictions"] == 5 and o.stats[0]["cutoff"] == 61, o.stats[0]
+    assert list(o.owner[0]) == [8, -1, -1, -1, -1, 5, 6, 7], list(o.owner[0])
+    assert [s for s, _ in blocks[0][0]] == [6, 0]
+    o.set_budget(0, 8)
+    o.resolve_evict(np.array([[(5, 9)]]), 5)
+    assert o.stats[0]["evictions"] == 5 and int(np.sum(o.owner[0] != -1)) == 5
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_page_layout, pin_summary_closed_form, pin_score_closed_form,
     pin_topk_bruteforce, pin_lru_hand_example, pin_lru_properties, pin_two_level_table,
     pin_retrieve_bytes, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
-    pin_first_step_slots,
+    pin_first_step_slots, pin_budget_shrink,
 ]

@@ -141,3 +141,29 @@ def test_exhausted_segment_pool_is_reported(spin_lib):
     p.spin.retrieve()
     assert p.spin.sync_status() == bd.SPIN_ESEGPOOL
     p.close()
+
+
+def test_budget_elasticity(spin_lib):
+    """Shrinking a request's budget makes the next resolve reclaim the excess
+    with the bucketed LRU; growing it back stops eviction.  Bit-exact state
+    against the oracle every step."""
+    from sparse_attention_tiered_amd import binding as bd
+    w = W.variant(W.C4, B=3, ctx=16384, k=16, steps=24, ar_coef=0.5)
+    mand = 8 * 16
+    p = _pair(w, slots=mand * 4)
+
+    def hook(t):
+        plan = {6: [(0, mand), (1, mand + 40)], 12: [(2, mand + 1)], 16: [(0, mand * 4)]}
+        for b, slots in plan.get(t, []):
+            p.spin.set_budget(b, slots)
+            p.oracle.set_budget(b, slots)
+
+    st, _ = p.run(on_step=hook)
+    assert st.evictions > 0
+    with pytest.raises(bd.SpinError) as e:
+        p.spin.set_budget(0, mand - 1)
+    assert e.value.code == bd.SPIN_ECAPACITY
+    with pytest.raises(bd.SpinError) as e:
+        p.spin.set_budget(0, mand * 4 + 1)
+    assert e.value.code == bd.SPIN_EINVAL
+    p.close()

@@ -24,7 +24,10 @@ MUTATIONS = {
     "cutoff_bucket_high_slots_first": ("for c in cands:  # ascending slot order", "for c in reversed(cands):"),
     "mandatory_evictable": ("and c not in mandatory_slots]", "]"),
     "hit_not_refreshed": ("self.last_use[b, c] = t\n                    mand.add(c)", "mand.add(c)"),
-    "evict_one_extra": ("need = max(0, len(misses) - n_free)", "need = max(0, len(misses) - n_free + 1)"),
+    "evict_one_extra": ("need = max(0, n_resident + len(misses) - self.budget[b])",
+                        "need = max(0, n_resident + len(misses) - self.budget[b] + 1)"),
+    "budget_ignored": ("need = max(0, n_resident + len(misses) - self.budget[b])",
+                       "need = max(0, n_resident + len(misses) - self.C)"),
     "segment_never_freed": ("self.seg_live[s] == 0:\n                    self.directory[b, h, e] = FREE\n                    self.free_stack.append(int(s))",
                             "self.seg_live[s] == -5:\n                    pass"),
     "live_not_counted": ("self.seg_live[s] += 1", "pass"),
