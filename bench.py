@@ -306,6 +306,23 @@ def main():
         "hbm_practical_read_GBps": bd.read_stream_gbs(),
         "wall_s": wall,
     }
+    # metadata footprint (two-level table vs a flat one), measured now and
+    # projected to a server provisioned for the worst case: 256 requests of
+    # 1M tokens on every layer of the model, with this run's live working set
+    md = spin.metadata()
+    prov_batch, prov_ctx = 256, 1 << 20
+    prov_pages = prov_ctx // 64
+    seg_b = 64 * 4 + 8
+    flat_prov = prov_batch * w.layers * w.Hkv * prov_pages * 4
+    dir_prov = prov_batch * w.layers * w.Hkv * ((prov_pages + 63) // 64) * 4
+    two_level_prov = dir_prov + md["live_segments"] * w.layers * seg_b + w.B * w.layers * w.slots_per_request * 8
+    line["metadata"] = {
+        "measured": md,
+        "projection": {"provisioned_batch": prov_batch, "provisioned_context": prov_ctx,
+                       "layers": w.layers, "active_batch": w.B,
+                       "flat_table_bytes": flat_prov, "two_level_bytes": two_level_prov,
+                       "ratio": flat_prov / two_level_prov},
+    }
     if args.copy_calibration:
         n = 64 << 20  # 64 Mi float32 = 256 MiB read + 256 MiB written per launch
         x = torch.ones(n, dtype=torch.float32, device="cuda")

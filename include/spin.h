@@ -107,6 +107,16 @@ typedef struct spin_stats {
   int32_t error_word;      /* SPIN_DEVERR_* bits */
 } spin_stats;
 
+typedef struct spin_metadata {
+  uint64_t directory_bytes;     /* static top-level directory, GPU */
+  uint64_t segment_pool_bytes;  /* pre-allocated shared pool of second-level segments, GPU */
+  uint64_t live_segment_bytes;  /* the segments linked into the directory now */
+  uint64_t reverse_map_bytes;   /* owner + last_use per slot: scales with the GPU buffer */
+  uint64_t flat_table_bytes;    /* one flat entry per (request, KV head, page) instead */
+  int32_t live_segments;
+  int32_t num_segments;
+} spin_metadata;
+
 /* Fill *cfg with the fixed geometry (head_dim 128, page_tokens 64,
  * seg_entries 64, num_buckets 64) and zeros elsewhere. */
 SPIN_API int spin_config_init(spin_config* cfg);
@@ -231,6 +241,12 @@ SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* stats, int64_t* per_reque
 SPIN_API int spin_snapshot(spin_ctx* ctx, int32_t* directory, int32_t* segments,
                            int32_t* seg_live, int32_t* seg_stack, int32_t* seg_top,
                            int32_t* owner, int32_t* last_use, int32_t* free_count);
+
+/* Metadata footprint ([XT] part 3, Fig. 6; [GP] C): bytes of the two-level
+ * page table as provisioned and as live now, next to a flat table for the
+ * same configuration.  A segment counts 64 entries + its live count + its
+ * stack slot (264 B).  Synchronises the device. */
+SPIN_API int spin_metadata_footprint(spin_ctx* ctx, spin_metadata* out);
 
 /* Copy request req's summaries ([Hkv][n_parts][128] float32) to host memory. */
 SPIN_API int spin_read_summaries(spin_ctx* ctx, int32_t req, float* host_out);

@@ -34,6 +34,13 @@ class SpinStats(ctypes.Structure):
                 ("live_segments", c_int32), ("error_word", c_int32)]
 
 
+class SpinMetadata(ctypes.Structure):
+    _fields_ = [("directory_bytes", ctypes.c_uint64), ("segment_pool_bytes", ctypes.c_uint64),
+                ("live_segment_bytes", ctypes.c_uint64), ("reverse_map_bytes", ctypes.c_uint64),
+                ("flat_table_bytes", ctypes.c_uint64), ("live_segments", c_int32),
+                ("num_segments", c_int32)]
+
+
 _P = c_void_p
 _I32P = POINTER(c_int32)
 # name -> (restype, argtypes)
@@ -57,6 +64,7 @@ SIGNATURES = {
     "spin_get_stats": (c_int, [_P, POINTER(SpinStats), POINTER(c_int64)]),
     "spin_snapshot": (c_int, [_P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P]),
     "spin_read_summaries": (c_int, [_P, c_int32, POINTER(ctypes.c_float)]),
+    "spin_metadata_footprint": (c_int, [_P, POINTER(SpinMetadata)]),
     "spin_sync_status": (c_int, [_P]),
     "spin_read_stream": (c_int, [_P, c_size_t, _P, _P]),
     "spin_strerror": (c_char_p, [c_int]),
@@ -240,6 +248,11 @@ class Spin:
             self.ctx, p["directory"], p["segments"], p["seg_live"], p["seg_stack"], p["seg_top"],
             p["owner"], p["last_use"], p["free_count"]))
         return out
+
+    def metadata(self):
+        m = SpinMetadata()
+        self._chk("spin_metadata_footprint", self.lib.spin_metadata_footprint(self.ctx, ctypes.byref(m)))
+        return {f: getattr(m, f) for f, _ in SpinMetadata._fields_}
 
     def summaries(self, req, n_parts):
         out = np.zeros((self.cfg.num_kv_heads, n_parts, 128), np.float32)

@@ -453,6 +453,24 @@ SPIN_API int spin_snapshot(spin_ctx* ctx, int32_t* directory, int32_t* segments,
   return SPIN_OK;
 }
 
+SPIN_API int spin_metadata_footprint(spin_ctx* ctx, spin_metadata* out) {
+  if (!ctx || !out) return SPIN_EINVAL;
+  const Dev& v = ctx->dev;
+  HIPCHK(ctx, hipDeviceSynchronize());
+  int top = 0;
+  HIPCHK(ctx, hipMemcpy(&top, v.seg_ctl, sizeof(int), hipMemcpyDeviceToHost));
+  const uint64_t seg_bytes = spin::kSegEntries * 4 + 4 + 4;
+  std::memset(out, 0, sizeof(*out));
+  out->directory_bytes = (uint64_t)v.B * v.Hkv * v.ndir * 4;
+  out->segment_pool_bytes = (uint64_t)v.n_seg * seg_bytes;
+  out->live_segments = v.n_seg - top;
+  out->num_segments = v.n_seg;
+  out->live_segment_bytes = (uint64_t)out->live_segments * seg_bytes;
+  out->reverse_map_bytes = (uint64_t)v.B * v.C * 8;
+  out->flat_table_bytes = (uint64_t)v.B * v.Hkv * v.max_pages * 4;
+  return SPIN_OK;
+}
+
 SPIN_API int spin_read_summaries(spin_ctx* ctx, int32_t req, float* host_out) {
   if (!ctx || !host_out || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
   const Dev& v = ctx->dev;

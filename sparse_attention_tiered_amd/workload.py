@@ -71,6 +71,7 @@ class Workload:
     ar_coef: float = 0.9
     seed: int = 0
     D: int = HEAD_DIM
+    layers: int = 1          # attention layers of the model whose shape this is
 
     @property
     def G(self) -> int:
@@ -90,14 +91,14 @@ def _std(name, cfg_id, B, Hq, Hkv, ctx, k, steps, **kw):
 
 # The five workloads, sized as stated for the method's decode layer.
 C1 = _std("c1_tiny", 1, 1, 8, 2, 4096, 8, 16, kv_kind="hot", hot_count=4)
-C2 = _std("c2_qwen3_14b_32k", 2, 16, 40, 8, 32768, 32, 64, kv_kind="hot", hot_count=5)
+C2 = _std("c2_qwen3_14b_32k", 2, 16, 40, 8, 32768, 32, 64, kv_kind="hot", hot_count=5, layers=40)
 C3 = _std("c3_qwen3_32b_128k", 3, 8, 64, 8, 131072, 64, 128, kv_kind="drift", hot_count=20,
-          drift_every=16, drift_replace=2)
+          drift_every=16, drift_replace=2, layers=64)
 # pool capped at a quarter of the summed per-request budget: 768 slots each
 C4 = _std("c4_llama70b_128k_pressure", 4, 32, 64, 8, 131072, 64, 128, kv_kind="hot",
-          hot_count=20, slots=(8 * 6 * 64) // 4)
+          hot_count=20, slots=(8 * 6 * 64) // 4, layers=80)
 C5 = _std("c5_cluster_1m", 5, 4, 32, 8, 1 << 20, 128, 64, kv_kind="cluster",
-          var_len=(16, 256))
+          var_len=(16, 256), layers=64)
 
 WORKLOADS = {w.name: w for w in (C1, C2, C3, C4, C5)}
 ALIASES = {"c1": C1.name, "c2": C2.name, "c3": C3.name, "c4": C4.name, "c5": C5.name}

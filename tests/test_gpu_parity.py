@@ -167,3 +167,21 @@ def test_budget_elasticity(spin_lib):
         p.spin.set_budget(0, mand * 4 + 1)
     assert e.value.code == bd.SPIN_EINVAL
     p.close()
+
+
+def test_metadata_footprint(spin_lib):
+    """Two-level metadata accounting: live segments equal the oracle's linked
+    segments; static sizes follow the configuration."""
+    w = W.variant(W.C4, B=3, ctx=20000, k=16, steps=10, ar_coef=0.5)
+    p = _pair(w, slots=8 * 16 * 2)
+    p.run()
+    md = p.spin.metadata()
+    o = p.oracle
+    live = o.n_seg - len(o.free_stack)
+    assert md["live_segments"] == live > 0
+    assert md["num_segments"] == o.n_seg
+    assert md["live_segment_bytes"] == live * 264
+    assert md["directory_bytes"] == w.B * w.Hkv * o.ndir * 4
+    assert md["flat_table_bytes"] == w.B * w.Hkv * o.max_pages * 4
+    assert md["reverse_map_bytes"] == w.B * o.C * 8
+    p.close()
