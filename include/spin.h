@@ -164,6 +164,29 @@ SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_
  * to slots_per_request. */
 SPIN_API int spin_set_budget(spin_ctx* ctx, int32_t req, int32_t slots, void* stream);
 
+/* Prefill side ([XT] part 1, Fig. 3: Index, then Offload of the KV to CPU
+ * memory).  d_kv: the request's freshly computed KV in device memory,
+ * [Hkv][pages][page] (pages from n_tokens / part_lens as in spin_index).
+ * h_kv: a pinned host buffer of h_kv_bytes; it reserves h_kv_bytes / (Hkv *
+ * 32768) pages per KV head (room for spin_append; SPIN_ECAPACITY if that is
+ * below the request's pages), laid out [Hkv][reserved][page].  Copies each
+ * head's pages to its run in h_kv and builds the summaries from the device
+ * copy, then registers the request as spin_index does.  Synchronises. */
+SPIN_API int spin_offload(spin_ctx* ctx, int32_t req, const void* d_kv, void* h_kv,
+                          size_t h_kv_bytes, int64_t n_tokens, const int32_t* part_lens,
+                          int32_t n_parts, void* stream);
+
+/* Decode-time append of one token to every request with registered KV.
+ * d_k, d_v: device [max_batch][Hkv][128] bf16 (rows of requests without KV
+ * are ignored).  Reading (the pages do not say): the token fills the last
+ * page of the request's last partition; a full page starts a new one-page
+ * partition.  The token is written to the host copy and, if that page is
+ * resident, to its pool slot; the tail partition's summary is updated
+ * exactly (fp64 key sum / length).  SPIN_ECAPACITY, before anything runs, if
+ * some request has no room (partition table, max_pages or its reserved host
+ * pages).  Stream-ordered. */
+SPIN_API int spin_append(spin_ctx* ctx, const void* d_k, const void* d_v, void* stream);
+
 /* Return request `req`'s slots and second-level segments to the free state;
  * the request then has no partitions.  Synchronises `stream`. */
 SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream);

@@ -35,6 +35,8 @@ What each part follows:
                    buffer pages, 64-bucket LRU reclaim oldest bucket first
                    until the demand is met; [GP] B: pages are per KV head.
   set_budget()     [XT] part 2 buffer elasticity: per-request budget.
+  offload()        [XT] part 1 / Fig. 3: prefill KV copied to host, indexed.
+  append()         decode-time append of a token (reading stated there).
   retrieve()       [XT] part 2 / Fig. 5 steps 3-4: host address from the CPU
                    page table, copy of the missed pages.
   attend()         [XT] part 1 / Fig. 3: attention over the selected
@@ -90,7 +92,7 @@ class Request:
     how partitions map onto pages ([XT] part 1: partitions are contiguous token
     runs mapped onto the shared paged substrate; [GP] A)."""
 
-    def __init__(self, host_pages: np.ndarray, lens: np.ndarray, Hkv: int):
+    def __init__(self, host_pages: np.ndarray, lens: np.ndarray, Hkv: int, stride: int | None = None):
         self.lens = np.asarray(lens, dtype=np.int64)
         self.n_parts = len(self.lens)
         npg = [pages_of_partition(int(L)) for L in self.lens]
@@ -101,9 +103,11 @@ class Request:
             acc += n
         self.n_pages = np.asarray(npg, np.int64)
         self.pages = acc
-        # [Hkv][pages][PAGE_ELEMS] uint16, the request's full KV in host memory
-        self.host = host_pages[: Hkv * max(acc, 0) * PAGE_ELEMS].reshape(Hkv, acc, PAGE_ELEMS) \
-            if acc > 0 else np.zeros((Hkv, 0, PAGE_ELEMS), np.uint16)
+        # pages reserved per KV head in the host buffer (room to append)
+        self.stride = acc if stride is None else stride
+        # [Hkv][stride][PAGE_ELEMS] uint16, the request's full KV in host memory
+        self.host = host_pages[: Hkv * self.stride * PAGE_ELEMS].reshape(Hkv, self.stride, PAGE_ELEMS) \
+            if self.stride > 0 else np.zeros((Hkv, 0, PAGE_ELEMS), np.uint16)
         self.summaries = None  # [Hkv][n_parts][D] float32
 
     def page_tokens(self, part: int, j: int) -> int:
@@ -164,25 +168,74 @@ class SpinOracle:
         self.budget[b] = self.C
         self.requests[b] = None
 
-    def index(self, b: int, host_pages: np.ndarray, lens: np.ndarray):
+    def summary(self, req: Request, h: int, i: int) -> np.ndarray:
+        """Mean key of partition i of head h over its valid tokens, in float64,
+        stored as float32 (reading R1)."""
+        rows = []
+        for j in range(int(req.n_pages[i])):
+            K = page_keys(req.host[h, req.first_page[i] + j], self.D)
+            rows.append(K[: req.page_tokens(i, j)])
+        keys = np.concatenate(rows, axis=0)
+        return (keys.sum(axis=0) / keys.shape[0]).astype(np.float32)
+
+    def index(self, b: int, host_pages: np.ndarray, lens: np.ndarray, stride: int | None = None):
         """Index: register request b's host KV (the CPU page table) and build its
-        partition summaries.  Summary of partition i of head h = mean over the
-        partition's valid tokens of the bf16 keys, computed in float64 and stored
-        as float32 (reading R1)."""
+        partition summaries ([XT] part 1, Fig. 3)."""
         self.release(b)
-        req = Request(host_pages, lens, self.Hkv)
-        assert req.pages <= self.max_pages
+        req = Request(host_pages, lens, self.Hkv, stride)
+        assert req.pages <= self.max_pages and req.pages <= req.stride
         summ = np.zeros((self.Hkv, req.n_parts, self.D), np.float32)
         for h in range(self.Hkv):
             for i in range(req.n_parts):
-                rows = []
-                for j in range(int(req.n_pages[i])):
-                    K = page_keys(req.host[h, req.first_page[i] + j], self.D)
-                    rows.append(K[: req.page_tokens(i, j)])
-                keys = np.concatenate(rows, axis=0)
-                summ[h, i] = (keys.sum(axis=0) / keys.shape[0]).astype(np.float32)
+                summ[h, i] = self.summary(req, h, i)
         req.summaries = summ
         self.requests[b] = req
+
+    def offload(self, b: int, kv_pages: np.ndarray, lens: np.ndarray, capacity_pages: int):
+        """Prefill side ([XT] part 1, Fig. 3: Index then Offload): the request's
+        freshly computed KV ([Hkv][pages][page]) is copied to host memory, into
+        a buffer that reserves capacity_pages per KV head, and indexed."""
+        pages = sum(pages_of_partition(int(L)) for L in lens)
+        host = np.zeros((self.Hkv, capacity_pages, PAGE_ELEMS), np.uint16)
+        host[:, :pages] = np.asarray(kv_pages).reshape(self.Hkv, pages, PAGE_ELEMS)
+        self.index(b, host.reshape(-1), lens, capacity_pages)
+
+    def append(self, k_bits: np.ndarray, v_bits: np.ndarray):
+        """Decode-time append of one token per registered request (k_bits,
+        v_bits: [B][Hkv][D] bf16).  Reading (not on the pages): the token fills
+        the last page of the request's last partition; when that page is full,
+        it starts a new one-page partition.  The token is written to the host
+        copy and, if its page is resident, to the GPU-side copy too; the tail
+        partition's summary is recomputed."""
+        for b in range(self.B):
+            req = self.requests[b]
+            if req is None:
+                continue
+            tail = req.n_parts - 1
+            if req.n_parts == 0 or req.lens[tail] % PAGE_TOKENS == 0:
+                assert req.pages < min(req.stride, self.max_pages), "no room to append"
+                req.lens = np.append(req.lens, 1)
+                req.first_page = np.append(req.first_page, req.pages)
+                req.n_pages = np.append(req.n_pages, 1)
+                req.n_parts += 1
+                req.pages += 1
+                tail = req.n_parts - 1
+                req.summaries = np.concatenate(
+                    [req.summaries, np.zeros((self.Hkv, 1, self.D), np.float32)], axis=1)
+            else:
+                req.lens[tail] += 1
+            page = int(req.first_page[tail] + req.n_pages[tail] - 1)
+            slot_tok = (int(req.lens[tail]) - 1) % PAGE_TOKENS
+            for h in range(self.Hkv):
+                dst = [req.host[h, page]]
+                c = self.translate(b, h, page)
+                if c != FREE:
+                    dst.append(self.pool[b * self.C + c])
+                for pg in dst:
+                    pg[slot_tok * self.D:(slot_tok + 1) * self.D] = k_bits[b, h]
+                    vt = pg[PAGE_TOKENS * self.D:].reshape(self.D, PAGE_TOKENS)
+                    vt[:, slot_tok] = v_bits[b, h]
+                req.summaries[h, tail] = self.summary(req, h, tail)
 
     # ------------------------------------------------------------------ Select
     def scores(self, q_bits: np.ndarray) -> list:

@@ -53,6 +53,8 @@ SIGNATURES = {
     "spin_destroy": (c_int, [_P]),
     "spin_index": (c_int, [_P, c_int32, _P, c_int64, _I32P, c_int32, _P]),
     "spin_release": (c_int, [_P, c_int32, _P]),
+    "spin_offload": (c_int, [_P, c_int32, _P, _P, c_size_t, c_int64, _I32P, c_int32, _P]),
+    "spin_append": (c_int, [_P, _P, _P, _P]),
     "spin_set_budget": (c_int, [_P, c_int32, c_int32, _P]),
     "spin_select": (c_int, [_P, _P, _P, _P, _P]),
     "spin_resolve_evict": (c_int, [_P, _P, c_int32, _P, _P, _P, _P]),
@@ -176,6 +178,24 @@ class Spin:
 
     def set_budget(self, req, slots, stream=None):
         self._chk("spin_set_budget", self.lib.spin_set_budget(self.ctx, req, int(slots), _stream(stream)))
+
+    def offload(self, req, d_kv, host_kv, n_tokens, part_lens=None, stream=None):
+        """d_kv: device tensor with the request's pages; host_kv: pinned CPU tensor
+        (its size sets the pages reserved per KV head for appends)."""
+        if not host_kv.is_pinned():
+            raise ValueError("host_kv must be pinned host memory")
+        lens_p, n_parts = None, 0
+        if part_lens is not None:
+            arr = np.ascontiguousarray(part_lens, dtype=np.int32)
+            lens_p = arr.ctypes.data_as(_I32P)
+            n_parts = len(arr)
+        self._chk("spin_offload", self.lib.spin_offload(
+            self.ctx, req, _ptr(d_kv), c_void_p(host_kv.data_ptr()),
+            host_kv.numel() * host_kv.element_size(), int(n_tokens), lens_p, n_parts, _stream(stream)))
+        self._host[req] = host_kv
+
+    def append(self, d_k, d_v, stream=None):
+        self._chk("spin_append", self.lib.spin_append(self.ctx, _ptr(d_k), _ptr(d_v), _stream(stream)))
 
     def release(self, req, stream=None):
         self._chk("spin_release", self.lib.spin_release(self.ctx, req, _stream(stream)))

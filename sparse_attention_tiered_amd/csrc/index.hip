@@ -30,6 +30,7 @@ __global__ void k_init(Dev d) {
     d.budget[i] = d.C;
     d.req_parts[i] = 0;
     d.req_pages[i] = 0;
+    d.req_stride[i] = 0;
     d.host_base[i] = 0;
     d.nmiss[i] = 0;
     d.nfreed[i] = 0;
@@ -85,6 +86,8 @@ __global__ __launch_bounds__(1024) void k_release(Dev d, int req) {
     d.budget[req] = d.C;
     d.req_parts[req] = 0;
     d.req_pages[req] = 0;
+    d.req_stride[req] = 0;
+    d.host_base[req] = 0;
     d.nmiss[req] = 0;
     d.nfreed[req] = 0;
     d.nalloc[req] = 0;
@@ -92,13 +95,16 @@ __global__ __launch_bounds__(1024) void k_release(Dev d, int req) {
 }
 
 // One workgroup of 64 lanes per (partition, KV head); lane l owns dims 2l, 2l+1.
-__global__ __launch_bounds__(64) void k_index(Dev d, int req) {
+// `src` holds the request's pages as [Hkv][src_stride][page]: the device-mapped
+// host buffer (Index of an offloaded request) or device memory (Index of
+// freshly computed KV before it is offloaded).
+__global__ __launch_bounds__(64) void k_index(Dev d, int req, const char* __restrict__ src,
+                                              int src_stride) {
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int len = d.part_len[(size_t)req * d.Nmax + i];
   const int first = d.part_first[(size_t)req * d.Nmax + i];
-  const int pages = d.req_pages[req];
   const uint32_t* base = reinterpret_cast<const uint32_t*>(
-      d.host_base[req] + ((size_t)h * pages + first) * (size_t)kPageBytes);
+      src + ((size_t)h * src_stride + first) * (size_t)kPageBytes);
   double s0 = 0.0, s1 = 0.0;
 #pragma unroll 8
   for (int t = 0; t < len; ++t) {
@@ -109,6 +115,69 @@ __global__ __launch_bounds__(64) void k_index(Dev d, int req) {
   float* out = d.summaries + (((size_t)req * d.Hkv + h) * d.Nmax + i) * kHeadDim;
   out[2 * lane] = (float)(s0 / (double)len);
   out[2 * lane + 1] = (float)(s1 / (double)len);
+  if (i == gridDim.x - 1) {  // the last partition keeps its exact sum for appends
+    double* ts = d.tail_sum + ((size_t)req * d.Hkv + h) * kHeadDim;
+    ts[2 * lane] = s0;
+    ts[2 * lane + 1] = s1;
+  }
+}
+
+// Decode-time append of one token per registered request (k, v: [B][Hkv][128]
+// bf16).  The token fills the last page of the request's last partition; a
+// full page starts a new one-page partition.  The token is written to the
+// host copy and, when the page is resident, to its pool slot; the tail
+// partition's summary is its exact fp64 key sum over its length.  The host
+// has checked that every request has room.
+__global__ __launch_bounds__(256) void k_append(Dev d, const uint16_t* __restrict__ k,
+                                                const uint16_t* __restrict__ v) {
+  __shared__ int sh[5];  // new partition?, tail index, page, token slot, new length
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (d.host_base[b] == 0) return;  // no registered KV
+  const int n = d.req_parts[b];
+  if (tid == 0) {
+    const int L = n > 0 ? d.part_len[(size_t)b * d.Nmax + n - 1] : 0;
+    const bool fresh = n == 0 || (L % kPageTokens) == 0;
+    const int tail = fresh ? n : n - 1;
+    const int len = fresh ? 1 : L + 1;
+    const int first = fresh ? d.req_pages[b] : d.part_first[(size_t)b * d.Nmax + tail];
+    sh[0] = fresh;
+    sh[1] = tail;
+    sh[2] = first + (len - 1) / kPageTokens;
+    sh[3] = (len - 1) % kPageTokens;
+    sh[4] = len;
+  }
+  __syncthreads();
+  const bool fresh = sh[0];
+  const int tail = sh[1], page = sh[2], tok = sh[3], len = sh[4];
+  const int stride = d.req_stride[b];
+  for (int e = tid; e < d.Hkv * kHeadDim; e += 256) {
+    const int h = e / kHeadDim, dim = e - h * kHeadDim;
+    const uint16_t kb = k[((size_t)b * d.Hkv + h) * kHeadDim + dim];
+    const uint16_t vb = v[((size_t)b * d.Hkv + h) * kHeadDim + dim];
+    uint16_t* hp = reinterpret_cast<uint16_t*>(d.host_base[b] + ((size_t)h * stride + page) * (size_t)kPageBytes);
+    hp[tok * kHeadDim + dim] = kb;
+    hp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb;
+    const int seg = d.directory[((size_t)b * d.Hkv + h) * d.ndir + (page >> 6)];
+    const int slot = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
+    if (slot >= 0 && slot < d.C) {
+      uint16_t* pp = d.pool + ((size_t)b * d.C + slot) * kPageElems;
+      pp[tok * kHeadDim + dim] = kb;
+      pp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb;
+    }
+    double* ts = d.tail_sum + ((size_t)b * d.Hkv + h) * kHeadDim + dim;
+    const double sum = (fresh ? 0.0 : *ts) + (double)__uint_as_float((uint32_t)kb << 16);
+    *ts = sum;
+    d.summaries[(((size_t)b * d.Hkv + h) * d.Nmax + tail) * kHeadDim + dim] = (float)(sum / (double)len);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    d.part_len[(size_t)b * d.Nmax + tail] = len;
+    if (fresh) {
+      d.part_first[(size_t)b * d.Nmax + tail] = page;
+      d.req_parts[b] = n + 1;
+      d.req_pages[b] = page + 1;
+    }
+  }
 }
 
 hipError_t launch_init(const Dev& d, hipStream_t s) {
@@ -128,9 +197,16 @@ hipError_t launch_set_budget(const Dev& d, int req, int slots, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_index(const Dev& d, int req, int n_parts, hipStream_t s) {
+hipError_t launch_index(const Dev& d, int req, int n_parts, const void* src, int src_stride,
+                        hipStream_t s) {
   if (n_parts == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_index, dim3(n_parts, d.Hkv), dim3(64), 0, s, d, req);
+  hipLaunchKernelGGL(k_index, dim3(n_parts, d.Hkv), dim3(64), 0, s, d, req,
+                     static_cast<const char*>(src), src_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Dev& d, const uint16_t* k, const uint16_t* v, hipStream_t s) {
+  hipLaunchKernelGGL(k_append, dim3(d.B), dim3(256), 0, s, d, k, v);
   return hipGetLastError();
 }
 

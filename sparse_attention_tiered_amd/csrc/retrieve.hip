@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
     if ((unsigned)f.x >= (unsigned)(d.B * d.C) || (unsigned)f.y >= (unsigned)d.B) continue;
     if ((unsigned)f.z >= (unsigned)d.Hkv || (unsigned)f.w >= (unsigned)d.req_pages[f.y]) continue;
     const u32x4* src = reinterpret_cast<const u32x4*>(
-        d.host_base[f.y] + ((size_t)f.z * d.req_pages[f.y] + f.w) * (size_t)kPageBytes);
+        d.host_base[f.y] + ((size_t)f.z * d.req_stride[f.y] + f.w) * (size_t)kPageBytes);
     u32x4* dst = reinterpret_cast<u32x4*>(d.pool + (size_t)f.x * kPageElems);
     u32x4 v[8];
 #pragma unroll

@@ -13,9 +13,18 @@
 
 using spin::Dev;
 
+// Host copy of what decides an append: whether a request has registered KV,
+// its partition count, the last partition's length, its pages and the room
+// its host buffer has (pages per KV head).
+struct ReqMirror {
+  bool registered = false;
+  int n_parts = 0, last_len = 0, pages = 0, stride = 0;
+};
+
 struct spin_ctx {
   spin_config cfg;
   Dev dev;
+  std::vector<ReqMirror> req;
   hipEvent_t ev_resolved = nullptr;  // recorded after resolve/evict
   hipEvent_t ev_fetched = nullptr;   // recorded after retrieve
   int hip_err = 0;
@@ -77,7 +86,8 @@ Derived derive(const spin_config* c) {
 
 // Byte offsets of every workspace region (each 256-byte aligned).
 struct Layout {
-  size_t summaries, part_first, part_len, req_parts, req_pages, host_base, directory, segments,
+  size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
+      directory, segments,
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, miss_tmp, ins, nmiss,
       freed, nfreed, alloc, nalloc, fetch, fetch_count, bmiss, part_o, part_ml, stats, err, total;
 };
@@ -97,6 +107,8 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.part_len = take(B * N * sizeof(int));
   L.req_parts = take(B * sizeof(int));
   L.req_pages = take(B * sizeof(int));
+  L.req_stride = take(B * sizeof(int));
+  L.tail_sum = take(B * Hkv * spin::kHeadDim * sizeof(double));
   L.host_base = take(B * sizeof(unsigned long long));
   L.directory = take(B * Hkv * d.ndir * sizeof(int));
   L.segments = take(S * spin::kSegEntries * sizeof(int));
@@ -191,6 +203,7 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   if (!ctx) return SPIN_EINVAL;
   ctx->cfg = *cfg;
   ctx->ws_bytes = ws_bytes;
+  ctx->req.assign(cfg->max_batch, ReqMirror());
   char* w = static_cast<char*>(d_ws);
   Dev& v = ctx->dev;
   v.B = cfg->max_batch;
@@ -213,6 +226,8 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.part_len = reinterpret_cast<int*>(w + L.part_len);
   v.req_parts = reinterpret_cast<int*>(w + L.req_parts);
   v.req_pages = reinterpret_cast<int*>(w + L.req_pages);
+  v.req_stride = reinterpret_cast<int*>(w + L.req_stride);
+  v.tail_sum = reinterpret_cast<double*>(w + L.tail_sum);
   v.host_base = reinterpret_cast<unsigned long long*>(w + L.host_base);
   v.directory = reinterpret_cast<int*>(w + L.directory);
   v.segments = reinterpret_cast<int*>(w + L.segments);
@@ -263,6 +278,7 @@ SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream) {
   if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
   HIPCHK(ctx, spin::launch_release(ctx->dev, req, S(stream)));
   HIPCHK(ctx, hipStreamSynchronize(S(stream)));
+  ctx->req[req] = ReqMirror();
   return SPIN_OK;
 }
 
@@ -275,11 +291,15 @@ SPIN_API int spin_set_budget(spin_ctx* ctx, int32_t req, int32_t slots, void* st
   return SPIN_OK;
 }
 
-SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_tokens,
-                        const int32_t* part_lens, int32_t n_parts, void* stream) {
-  if (!ctx || req < 0 || req >= ctx->cfg.max_batch || n_tokens < 0) return SPIN_EINVAL;
-  const spin_config& c = ctx->cfg;
-  std::vector<int32_t> lens;
+namespace {
+
+// Partition lengths of a request: part_lens, or fixed 64-token partitions
+// covering n_tokens.  Returns SPIN_OK and fills lens/first/pages.
+int partition_table(const spin_config& c, int64_t n_tokens, const int32_t* part_lens,
+                    int32_t n_parts, std::vector<int32_t>& lens, std::vector<int32_t>& first,
+                    int64_t& pages) {
+  if (n_tokens < 0) return SPIN_EINVAL;
+  lens.clear();
   if (part_lens) {
     if (n_parts < 0) return SPIN_EINVAL;
     lens.assign(part_lens, part_lens + n_parts);
@@ -296,13 +316,56 @@ SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_
     if (tail) lens.push_back((int32_t)tail);
   }
   if ((int64_t)lens.size() > c.max_partitions) return SPIN_EINVAL;
-  std::vector<int32_t> first(lens.size());
-  int64_t pages = 0;
+  first.resize(lens.size());
+  pages = 0;
   for (size_t i = 0; i < lens.size(); ++i) {
     first[i] = (int32_t)pages;
     pages += (lens[i] + spin::kPageTokens - 1) / spin::kPageTokens;
   }
   if (pages > c.max_pages) return SPIN_EINVAL;
+  return SPIN_OK;
+}
+
+// Register request `req`: release it, write its partition table, host base
+// and host stride, then build the summaries from `src` ([Hkv][src_stride]
+// pages; device-mapped host or device memory).  Leaves the stream busy.
+int register_request(spin_ctx* ctx, int32_t req, unsigned long long host_base, int stride,
+                     const std::vector<int32_t>& lens, const std::vector<int32_t>& first,
+                     int pages, const void* src, int src_stride, hipStream_t s) {
+  Dev& v = ctx->dev;
+  const int np = (int)lens.size();
+  HIPCHK(ctx, spin::launch_release(v, req, s));
+  if (np) {
+    HIPCHK(ctx, hipMemcpyAsync(v.part_first + (size_t)req * v.Nmax, first.data(), np * sizeof(int),
+                               hipMemcpyHostToDevice, s));
+    HIPCHK(ctx, hipMemcpyAsync(v.part_len + (size_t)req * v.Nmax, lens.data(), np * sizeof(int),
+                               hipMemcpyHostToDevice, s));
+  }
+  HIPCHK(ctx, hipMemcpyAsync(v.req_pages + req, &pages, sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, hipMemcpyAsync(v.req_stride + req, &stride, sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, hipMemcpyAsync(v.host_base + req, &host_base, sizeof(host_base), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, spin::launch_index(v, req, np, src, src_stride, s));
+  // partitions become visible to select/resolve only once the summaries exist
+  HIPCHK(ctx, hipMemcpyAsync(v.req_parts + req, &np, sizeof(int), hipMemcpyHostToDevice, s));
+  HIPCHK(ctx, hipStreamSynchronize(s));
+  ReqMirror& m = ctx->req[req];
+  m.registered = host_base != 0;
+  m.n_parts = np;
+  m.last_len = np ? lens.back() : 0;
+  m.pages = pages;
+  m.stride = stride;
+  return SPIN_OK;
+}
+
+}  // namespace
+
+SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_tokens,
+                        const int32_t* part_lens, int32_t n_parts, void* stream) {
+  if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
+  std::vector<int32_t> lens, first;
+  int64_t pages = 0;
+  int rc = partition_table(ctx->cfg, n_tokens, part_lens, n_parts, lens, first, pages);
+  if (rc) return rc;
   unsigned long long base = 0;
   if (!lens.empty()) {
     if (!h_kv) return SPIN_EINVAL;
@@ -311,22 +374,60 @@ SPIN_API int spin_index(spin_ctx* ctx, int32_t req, const void* h_kv, int64_t n_
     if (!aligned(dptr, 16)) return SPIN_EINVAL;
     base = reinterpret_cast<unsigned long long>(dptr);
   }
+  return register_request(ctx, req, base, (int)pages, lens, first, (int)pages,
+                          reinterpret_cast<const void*>(base), (int)pages, S(stream));
+}
+
+SPIN_API int spin_offload(spin_ctx* ctx, int32_t req, const void* d_kv, void* h_kv,
+                          size_t h_kv_bytes, int64_t n_tokens, const int32_t* part_lens,
+                          int32_t n_parts, void* stream) {
+  if (!ctx || req < 0 || req >= ctx->cfg.max_batch || !h_kv) return SPIN_EINVAL;
+  const spin_config& c = ctx->cfg;
+  std::vector<int32_t> lens, first;
+  int64_t pages = 0;
+  int rc = partition_table(c, n_tokens, part_lens, n_parts, lens, first, pages);
+  if (rc) return rc;
+  const size_t head_bytes = (size_t)c.num_kv_heads * spin::kPageBytes;
+  const int64_t capacity = (int64_t)(h_kv_bytes / head_bytes);
+  if (capacity < pages || capacity < 1 || capacity > (1 << 30)) return SPIN_ECAPACITY;
+  if (pages > 0 && (!d_kv || !aligned(d_kv, 16))) return SPIN_EINVAL;
+  void* dptr = nullptr;
+  HIPCHK(ctx, hipHostGetDevicePointer(&dptr, h_kv, 0));
+  if (!aligned(dptr, 16)) return SPIN_EINVAL;
   hipStream_t s = S(stream);
-  Dev& v = ctx->dev;
-  const int np = (int)lens.size(), pg = (int)pages;
-  HIPCHK(ctx, spin::launch_release(v, req, s));
-  if (np) {
-    HIPCHK(ctx, hipMemcpyAsync(v.part_first + (size_t)req * v.Nmax, first.data(), np * sizeof(int),
-                               hipMemcpyHostToDevice, s));
-    HIPCHK(ctx, hipMemcpyAsync(v.part_len + (size_t)req * v.Nmax, lens.data(), np * sizeof(int),
-                               hipMemcpyHostToDevice, s));
+  if (pages > 0)  // Offload: each head's pages to its reserved run in host memory
+    HIPCHK(ctx, hipMemcpy2DAsync(h_kv, (size_t)capacity * spin::kPageBytes, d_kv,
+                                 (size_t)pages * spin::kPageBytes, (size_t)pages * spin::kPageBytes,
+                                 c.num_kv_heads, hipMemcpyDeviceToHost, s));
+  // Index from the device copy (HBM), while the host copy is written
+  return register_request(ctx, req, reinterpret_cast<unsigned long long>(dptr), (int)capacity, lens,
+                          first, (int)pages, d_kv, (int)pages, s);
+}
+
+SPIN_API int spin_append(spin_ctx* ctx, const void* d_k, const void* d_v, void* stream) {
+  if (!ctx || !d_k || !d_v) return SPIN_EINVAL;
+  const spin_config& c = ctx->cfg;
+  // every registered request must have room for the token before anything runs
+  for (const ReqMirror& m : ctx->req) {
+    if (!m.registered) continue;
+    const bool fresh = m.n_parts == 0 || m.last_len % spin::kPageTokens == 0;
+    if (fresh && (m.n_parts >= c.max_partitions || m.pages >= std::min(m.stride, c.max_pages)))
+      return SPIN_ECAPACITY;
+    if (!fresh && m.last_len >= spin::kPageTokens * c.max_pages_per_partition) return SPIN_ECAPACITY;
   }
-  HIPCHK(ctx, hipMemcpyAsync(v.req_pages + req, &pg, sizeof(int), hipMemcpyHostToDevice, s));
-  HIPCHK(ctx, hipMemcpyAsync(v.host_base + req, &base, sizeof(base), hipMemcpyHostToDevice, s));
-  HIPCHK(ctx, spin::launch_index(v, req, np, s));
-  // partitions become visible to select/resolve only once the summaries exist
-  HIPCHK(ctx, hipMemcpyAsync(v.req_parts + req, &np, sizeof(int), hipMemcpyHostToDevice, s));
-  HIPCHK(ctx, hipStreamSynchronize(s));
+  HIPCHK(ctx, spin::launch_append(ctx->dev, static_cast<const uint16_t*>(d_k),
+                                  static_cast<const uint16_t*>(d_v), S(stream)));
+  for (ReqMirror& m : ctx->req) {
+    if (!m.registered) continue;
+    const bool fresh = m.n_parts == 0 || m.last_len % spin::kPageTokens == 0;
+    if (fresh) {
+      ++m.n_parts;
+      ++m.pages;
+      m.last_len = 1;
+    } else {
+      ++m.last_len;
+    }
+  }
   return SPIN_OK;
 }
 

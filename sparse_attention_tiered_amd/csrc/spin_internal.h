@@ -34,6 +34,8 @@ struct Dev {
   int* part_len;               // [B][Nmax] tokens
   int* req_parts;              // [B]
   int* req_pages;              // [B] pages per KV head
+  int* req_stride;             // [B] pages reserved per KV head in the host buffer
+  double* tail_sum;            // [B][Hkv][128] key sum of each request's last partition
   unsigned long long* host_base;  // [B] device-mapped address of the host KV
   // residency state
   int* directory;              // [B][Hkv][ndir] segment id or -1
@@ -68,7 +70,9 @@ struct Dev {
 hipError_t launch_init(const Dev& d, hipStream_t s);
 hipError_t launch_release(const Dev& d, int req, hipStream_t s);
 hipError_t launch_set_budget(const Dev& d, int req, int slots, hipStream_t s);
-hipError_t launch_index(const Dev& d, int req, int n_parts, hipStream_t s);
+hipError_t launch_index(const Dev& d, int req, int n_parts, const void* src, int src_stride,
+                        hipStream_t s);
+hipError_t launch_append(const Dev& d, const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s);
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,

@@ -33,36 +33,59 @@ class Pair:
     """The GPU context and the oracle, indexed with the same host KV."""
 
     def __init__(self, w: W.Workload, n_steps=None, attend_pps=0, num_segments=None,
-                 slots=None, oracle=True, threads=None):
+                 slots=None, oracle=True, threads=None, offload_extra_pages=None):
         t0 = time.time()
         self.w = w
         self.geo = geo = W.geometry(w)
         self.draws = W.draw_queries(w, geo, n_steps)
         self.T = self.draws.q_bits.shape[0]
-        self.host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
-        W.fill_all(w, geo, self.draws, [h[1] for h in self.host], threads)
         C = w.slots_per_request if slots is None else slots
-        self.cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts, geo.max_pages, w.k, C,
+        extra = offload_extra_pages or 0
+        max_parts, max_pages = geo.max_parts + extra, geo.max_pages + extra
+        self.cfg = bd.make_config(w.B, w.Hq, w.Hkv, max_parts, max_pages, w.k, C,
                                   num_segments=num_segments, max_pages_per_partition=geo.max_ppp,
                                   attend_pages_per_split=attend_pps)
         self.spin = bd.Spin(self.cfg)
-        for b in range(w.B):
-            lens = geo.lens[b] if w.var_len is not None else None
-            self.spin.index(b, self.host[b][0], w.ctx[b], lens)
-        self.q_dev = torch.from_numpy(self.draws.q_bits.view(np.int16)).to("cuda")
-        self.scores = torch.empty((w.B, w.Hkv, geo.max_parts), dtype=torch.float32, device="cuda")
         self.oracle = None
         if oracle:
-            self.oracle = SpinOracle(w.B, w.Hq, w.Hkv, w.k, C, geo.max_pages, self.cfg.num_segments)
+            self.oracle = SpinOracle(w.B, w.Hq, w.Hkv, w.k, C, max_pages, self.cfg.num_segments)
+        if offload_extra_pages is None:
+            # the full KV starts in pinned host memory and is indexed there
+            self.host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
+            W.fill_all(w, geo, self.draws, [h[1] for h in self.host], threads)
             for b in range(w.B):
-                self.oracle.index(b, self.host[b][1], geo.lens[b])
+                lens = geo.lens[b] if w.var_len is not None else None
+                self.spin.index(b, self.host[b][0], w.ctx[b], lens)
+                if oracle:
+                    self.oracle.index(b, self.host[b][1], geo.lens[b])
+        else:
+            # prefill side: the KV starts in device memory and is offloaded
+            kv = W.host_kv_numpy(w, geo, self.draws, threads)
+            self.host = []
+            for b in range(w.B):
+                cap = geo.pages[b] + extra
+                t = torch.zeros(w.Hkv * cap * W.PAGE_ELEMS, dtype=torch.int16, pin_memory=True)
+                self.host.append((t, t.numpy().view(np.uint16)))
+                pages = kv[b][: w.Hkv * geo.pages[b] * W.PAGE_ELEMS]
+                d_kv = torch.from_numpy(pages.view(np.int16)).to("cuda")
+                lens = geo.lens[b] if w.var_len is not None else None
+                self.spin.offload(b, d_kv, t, w.ctx[b], lens)
+                if oracle:
+                    self.oracle.offload(b, pages.reshape(w.Hkv, geo.pages[b], -1), geo.lens[b], cap)
+        self.q_dev = torch.from_numpy(self.draws.q_bits.view(np.int16)).to("cuda")
+        self.scores = torch.empty((w.B, w.Hkv, max_parts), dtype=torch.float32, device="cuda")
         log(f"[setup] {w.name} B={w.B} ctx={w.ctx[0]} C={C} segs={self.cfg.num_segments} "
             f"splits={self.spin.splits} in {time.time() - t0:.1f}s")
 
     # ------------------------------------------------------------------ checks
+    def n_parts(self, b):
+        """Partitions of request b now (appends add some)."""
+        r = self.oracle.requests[b] if self.oracle is not None else None
+        return r.n_parts if r is not None else len(self.geo.lens[b])
+
     def check_summaries(self):
         for b in range(self.w.B):
-            n = len(self.geo.lens[b])
+            n = self.n_parts(b)
             if n == 0:
                 continue
             got = self.spin.summaries(b, n)
@@ -75,7 +98,7 @@ class Pair:
         k = self.w.k
         flips = 0
         for b in range(self.w.B):
-            n = len(self.geo.lens[b])
+            n = self.n_parts(b)
             for h in range(self.w.Hkv):
                 g = sel_gpu[b, h]
                 o = sel_o[b, h]
@@ -127,7 +150,25 @@ class Pair:
         return st
 
     # ------------------------------------------------------------------ stepping
-    def run(self, steps=None, out_sample=None, check_every=1, seed=0, on_step=None):
+    def append_token(self, t):
+        """One seeded token per request, appended on both sides."""
+        rng = np.random.default_rng([777, t])
+        kv = rng.standard_normal((2, self.w.B, self.w.Hkv, 128), dtype=np.float32)
+        bits = W.to_bf16_bits(kv)
+        dk = torch.from_numpy(bits[0].view(np.int16)).to("cuda")
+        dv = torch.from_numpy(bits[1].view(np.int16)).to("cuda")
+        self.spin.append(dk, dv)
+        self.oracle.append(bits[0], bits[1])
+
+    def check_host(self):
+        """The pinned host buffers (written by the offload copy and the append
+        kernel) equal the oracle's own host copies byte for byte."""
+        for b in range(self.w.B):
+            req = self.oracle.requests[b]
+            gpu = self.host[b][1][: req.host.size].reshape(req.host.shape)
+            assert np.array_equal(gpu, req.host), b
+
+    def run(self, steps=None, out_sample=None, check_every=1, seed=0, on_step=None, append=False):
         """Full stage parity for `steps` steps.  out_sample=None compares every
         output; an int compares that many (b, g) pairs per step, chosen with a
         seeded generator, computed one by one by the oracle."""
@@ -138,6 +179,8 @@ class Pair:
         for t in range(steps):
             if on_step is not None:
                 on_step(t)
+            if append:
+                self.append_token(t)
             q = self.q_dev[t]
             self.spin.select(q, scores=self.scores)
             sel_gpu = self.spin.sel.cpu().numpy()

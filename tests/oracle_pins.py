@@ -543,9 +543,56 @@ def pin_budget_shrink(om):
     assert o.stats[0]["evictions"] == 5 and int(np.sum(o.owner[0] != -1)) == 5
 
 
+def pin_offload_append(om):
+    """Offload a request of 94 tokens (partitions 64 + 30) into a host buffer
+    with room for 6 pages per head, make every page resident, then append 40
+    tokens: 34 fill partition 1 to 64 tokens, the next 6 start partition 2.
+    Lengths, host bytes, exact summaries (means of the known keys), and
+    attention over all 134 tokens equal to dense SDPA: the last holds only if
+    the append also updated the resident GPU-side copy of the tail page."""
+    rng = np.random.default_rng(31)
+    Hkv, Hq, lens = 2, 4, [64, 30]
+    Kp, Vp = random_parts(rng, Hkv, lens)
+    buf, la = pack_request(Kp, Vp, Hkv, pad_value=0.0)
+    o = make(om, 1, Hq, Hkv, 4, Hkv * 4 + 2, 6)
+    o.offload(0, buf.reshape(Hkv, 2, -1), la, 6)
+    q = bf16_exact(rng.standard_normal((1, Hq, D)).astype(np.float32))
+    sel, _ = o.select(bits(q))
+    o.resolve_evict(sel, 0)
+    o.retrieve()
+    Klog = [np.concatenate(Kp[h], 0) for h in range(Hkv)]
+    Vlog = [np.concatenate(Vp[h], 0) for h in range(Hkv)]
+    for i in range(40):
+        kn = bf16_exact(rng.standard_normal((1, Hkv, D)).astype(np.float32))
+        vn = bf16_exact(rng.standard_normal((1, Hkv, D)).astype(np.float32))
+        o.append(bits(kn), bits(vn))
+        for h in range(Hkv):
+            Klog[h] = np.concatenate([Klog[h], kn[0, h][None]], 0)
+            Vlog[h] = np.concatenate([Vlog[h], vn[0, h][None]], 0)
+    req = o.requests[0]
+    assert list(req.lens) == [64, 64, 6] and list(req.first_page) == [0, 1, 2] and req.pages == 3
+    bounds = [(0, 64), (64, 128), (128, 134)]
+    for h in range(Hkv):
+        for i, (a, e) in enumerate(bounds):
+            want = (Klog[h][a:e].astype(np.float64).sum(0) / (e - a)).astype(np.float32)
+            assert np.array_equal(req.summaries[h, i], want), (h, i)
+        # the last appended token sits in slot 5 of page 2: key row 5, value column 5
+        pg = req.host[h, 2]
+        assert np.array_equal(pg[5 * D:6 * D], bits(Klog[h][133:134]).reshape(-1))
+        assert np.array_equal(pg[64 * D:].reshape(D, 64)[:, 5], bits(Vlog[h][133:134]).reshape(-1))
+    sel, _ = o.select(bits(q))
+    blocks = o.resolve_evict(sel, 1)
+    o.retrieve()
+    out = o.attend(bits(q), blocks)
+    for g in range(Hq):
+        h = g // (Hq // Hkv)
+        want = dense_attention(q[0, g], Klog[h], Vlog[h])
+        assert np.allclose(out[0, g], want, rtol=0, atol=2e-6), (g, np.abs(out[0, g] - want).max())
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_page_layout, pin_summary_closed_form, pin_score_closed_form,
     pin_topk_bruteforce, pin_lru_hand_example, pin_lru_properties, pin_two_level_table,
     pin_retrieve_bytes, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
-    pin_first_step_slots, pin_budget_shrink,
+    pin_first_step_slots, pin_budget_shrink, pin_offload_append,
 ]

@@ -185,3 +185,38 @@ def test_metadata_footprint(spin_lib):
     assert md["flat_table_bytes"] == w.B * w.Hkv * o.max_pages * 4
     assert md["reverse_map_bytes"] == w.B * o.C * 8
     p.close()
+
+
+@pytest.mark.parametrize("name", ["fixed", "variable"])
+def test_offload_and_append(spin_lib, name):
+    """Prefill-side Offload + Index from device KV, then one appended token per
+    request per step: host bytes, summaries, selection, residency state and
+    outputs match the oracle every step (ragged requests, a partial tail)."""
+    if name == "fixed":
+        w = W.variant(W.C4, B=3, ctx=(5000, 3000, 64 * 20), k=8, steps=40, ar_coef=0.5)
+        slots = 8 * 8 + 24
+    else:
+        w = W.variant(W.C5, B=2, ctx=(9000, 4321), k=8, steps=30, n_centroids=64)
+        slots = 8 * 8 * 4 + 24
+    p = _pair(w, slots=slots, offload_extra_pages=3)
+    p.check_host()
+    p.check_summaries()
+    st, _ = p.run(append=True)
+    p.check_host()
+    p.check_summaries()
+    assert st.misses > 0
+    p.close()
+
+
+def test_append_capacity_is_checked(spin_lib):
+    import torch
+    from sparse_attention_tiered_amd import binding as bd
+    w = W.variant(W.C1, ctx=(64 * 3,), steps=1)
+    p = _pair(w, slots=2 * 8 + 4, offload_extra_pages=1, oracle=False)
+    dk = torch.zeros((1, 2, 128), dtype=torch.int16, device="cuda")
+    for _ in range(64):      # fills the one reserved page
+        p.spin.append(dk, dk)
+    with pytest.raises(bd.SpinError) as e:
+        p.spin.append(dk, dk)
+    assert e.value.code == bd.SPIN_ECAPACITY
+    p.close()

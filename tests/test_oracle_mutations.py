@@ -41,6 +41,12 @@ MUTATIONS = {
     "values_not_transposed": (".reshape(D, PAGE_TOKENS).T", ".reshape(PAGE_TOKENS, D)"),
     "attend_no_scale": ("logits = (K @ q[h * self.G + j]) / math.sqrt(self.D)", "logits = (K @ q[h * self.G + j])"),
     "attend_wrong_kv_head": ("logits = (K @ q[h * self.G + j])", "logits = (K @ q[j * self.Hkv + h])"),
+    "append_skips_resident_copy": ("                if c != FREE:\n                    dst.append(self.pool[b * self.C + c])",
+                                   "                if c == -12345:\n                    dst.append(self.pool[b * self.C + c])"),
+    "append_slot_off_by_one": ("slot_tok = (int(req.lens[tail]) - 1) % PAGE_TOKENS",
+                               "slot_tok = int(req.lens[tail]) % PAGE_TOKENS"),
+    "append_never_new_partition": ("if req.n_parts == 0 or req.lens[tail] % PAGE_TOKENS == 0:",
+                                   "if req.n_parts == 0:"),
     "retrieve_wrong_head": ("self.pool[gslot] = self.requests[b].host[h, page]",
                             "self.pool[gslot] = self.requests[b].host[0, page]"),
 }
