@@ -47,6 +47,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return res;
 }
 
+// Largest b in [0, nb) with prefix[b] <= j (prefix ascending, prefix[0] = 0):
+// the request that owns flat index j of a per-request concatenation.
+__device__ __forceinline__ int owner_of(const int* prefix, int nb, int j) {
+  int lo = 0, hi = nb;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= j) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Relaxed device-scope load that does not use a stale L1 line.
 __device__ __forceinline__ int load_device(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -43,7 +43,6 @@ __global__ void k_init(Dev d) {
   if (tid == 0) {
     d.seg_ctl[0] = d.n_seg;
     d.err[0] = 0;
-    d.fetch_count[0] = 0;
   }
 }
 

@@ -275,18 +275,10 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
 // Shared segment pool, one workgroup for the batch: push every request's
 // emptied segments (requests ascending), hand segments to the directory
 // ranges that k_resolve listed (requests ascending, canonical order), then
-// write the inserts into their segments and build the batch-wide fetch list.
-// Each phase is a flat loop over the batch; a request is found from a flat
-// index by binary search over the per-request prefix sums kept in LDS.
-__device__ __forceinline__ int owner_of(const int* prefix, int nb, int j) {
-  int lo = 0, hi = nb;  // largest b with prefix[b] <= j
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= j) lo = mid;
-    else hi = mid;
-  }
-  return lo;
-}
+// write the inserts into their segments.  Each phase is a flat loop over the
+// batch; a request is found from a flat index by binary search over the
+// per-request prefix sums kept in LDS.  The retrieve does not wait for this
+// pass: it reads the insert lists k_resolve wrote.
 
 __global__ __launch_bounds__(1024) void k_segments(Dev d) {
   __shared__ int pf[1025], pa[1025], pm[1025];
@@ -334,19 +326,17 @@ __global__ __launch_bounds__(1024) void k_segments(Dev d) {
       d.segments[(size_t)seg * kSegEntries + (m.z & 63)] = m.x;
       atomicAdd(&d.seg_live[seg], 1);
     }
-    d.fetch[j] = make_int4(b * d.C + m.x, b, m.y, m.z);
   }
-  if (tid == 0) {
-    d.seg_ctl[0] = max(top1 - A, 0);
-    d.fetch_count[0] = M;
-  }
+  if (tid == 0) d.seg_ctl[0] = max(top1 - A, 0);
 }
 
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_resolve, dim3(d.B), dim3(1024), 0, s, d, sel, t, bt, bntok, bcount);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_segments(const Dev& d, hipStream_t s) {
   hipLaunchKernelGGL(k_segments, dim3(1), dim3(1024), 0, s, d);
   return hipGetLastError();
 }

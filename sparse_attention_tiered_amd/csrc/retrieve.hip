@@ -7,7 +7,8 @@
 // through the host buffer's device-mapped address with 16-byte loads per lane
 // (eight loads in flight per lane, the full page per workgroup) and writes
 // them to HBM.  The host never reads the miss count: the grid is fixed and
-// every workgroup strides over the device-side fetch list.
+// every workgroup strides over the batch's insert lists, which k_resolve
+// writes, so the transfer does not wait for the segment-pool pass.
 #include "device_util.h"
 #include "spin_internal.h"
 
@@ -22,15 +23,39 @@ constexpr int kRetrieveWG = 256;
 constexpr int kRetrieveGrid = 64;
 
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
-  const int n = d.fetch_count[0];
+  __shared__ int pm[1025];
+  __shared__ int tmp[5];
   const int tid = threadIdx.x;
-  for (int j = blockIdx.x; j < n; j += gridDim.x) {
-    const int4 f = d.fetch[j];  // (global slot, request, KV head, page)
-    if ((unsigned)f.x >= (unsigned)(d.B * d.C) || (unsigned)f.y >= (unsigned)d.B) continue;
-    if ((unsigned)f.z >= (unsigned)d.Hkv || (unsigned)f.w >= (unsigned)d.req_pages[f.y]) continue;
+  // where each request's misses start in the batch-wide concatenation of the
+  // insert lists k_resolve wrote (requests ascending, canonical order)
+  int M;
+  {
+    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
+    int loc[per], sum = 0;
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int b = tid * per + u;
+      loc[u] = b < d.B ? d.nmiss[b] : 0;
+      sum += loc[u];
+    }
+    int ex = block_excl_scan<kRetrieveWG>(sum, tmp, &M);
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int b = tid * per + u;
+      if (b < d.B) pm[b] = ex;
+      ex += loc[u];
+    }
+    __syncthreads();
+  }
+  for (int j = blockIdx.x; j < M; j += gridDim.x) {
+    const int b = owner_of(pm, d.B, j);
+    const int4 m = d.ins[(size_t)b * d.max_mand + (j - pm[b])];  // (slot, KV head, page)
+    if ((unsigned)m.x >= (unsigned)d.C || (unsigned)m.y >= (unsigned)d.Hkv ||
+        (unsigned)m.z >= (unsigned)d.req_pages[b])
+      continue;
     const u32x4* src = reinterpret_cast<const u32x4*>(
-        d.host_base[f.y] + ((size_t)f.z * d.req_stride[f.y] + f.w) * (size_t)kPageBytes);
-    u32x4* dst = reinterpret_cast<u32x4*>(d.pool + (size_t)f.x * kPageElems);
+        d.host_base[b] + ((size_t)m.y * d.req_stride[b] + m.z) * (size_t)kPageBytes);
+    u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)b * d.C + m.x) * kPageElems);
     u32x4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = src[u * kRetrieveWG + tid];

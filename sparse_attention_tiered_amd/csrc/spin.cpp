@@ -89,7 +89,7 @@ struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
       directory, segments,
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, miss_tmp, ins, nmiss,
-      freed, nfreed, alloc, nalloc, fetch, fetch_count, bmiss, part_o, part_ml, stats, err, total;
+      freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, stats, err, total;
 };
 
 Layout layout(const spin_config* c, const Derived& d) {
@@ -127,8 +127,6 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.nfreed = take(B * sizeof(int));
   L.alloc = take(B * Hkv * d.ndir * sizeof(int));
   L.nalloc = take(B * sizeof(int));
-  L.fetch = take(B * d.max_mand * sizeof(int4));
-  L.fetch_count = take(4 * sizeof(int));
   L.bmiss = take(B * Hkv * d.max_blocks);
   L.part_o = take(B * Hkv * 2 * d.splits * d.G * spin::kHeadDim * sizeof(float));
   L.part_ml = take(B * Hkv * 2 * d.splits * d.G * 2 * sizeof(float));
@@ -246,8 +244,6 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.nfreed = reinterpret_cast<int*>(w + L.nfreed);
   v.alloc = reinterpret_cast<int*>(w + L.alloc);
   v.nalloc = reinterpret_cast<int*>(w + L.nalloc);
-  v.fetch = reinterpret_cast<int4*>(w + L.fetch);
-  v.fetch_count = reinterpret_cast<int*>(w + L.fetch_count);
   v.bmiss = reinterpret_cast<unsigned char*>(w + L.bmiss);
   v.part_o = reinterpret_cast<float*>(w + L.part_o);
   v.part_ml = reinterpret_cast<float*>(w + L.part_ml);
@@ -446,8 +442,14 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
   if (!ctx || !d_sel || !d_block_table || !d_block_ntok || !d_block_count || t < 0) return SPIN_EINVAL;
   if (t < ctx->last_t) return SPIN_EINVAL;
   ctx->last_t = t;
+  // the previous step's transfer reads the insert lists this call rewrites
+  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
   HIPCHK(ctx, spin::launch_resolve(ctx->dev, d_sel, t, d_block_table, d_block_ntok, d_block_count,
                                    S(stream)));
+  // The transfer needs only k_resolve's insert lists, but the segment-pool
+  // pass is latency-bound and runs several times slower next to the PCIe
+  // pulls (measured), so it finishes before the transfer starts.
+  HIPCHK(ctx, spin::launch_segments(ctx->dev, S(stream)));
   HIPCHK(ctx, hipEventRecord(ctx->ev_resolved, S(stream)));
   return SPIN_OK;
 }

@@ -56,8 +56,6 @@ struct Dev {
   int* nfreed;                 // [B]
   int* alloc;                  // [B][Hkv * ndir] directory entries that need a segment
   int* nalloc;                 // [B]
-  int4* fetch;                 // [B * max_mand] (global slot, b, h, page)
-  int* fetch_count;            // [1]
   unsigned char* bmiss;        // [B][Hkv][max_blocks] 1 = block fetched by this step's retrieve
   float* part_o;               // [B * Hkv][2 * splits][G][128]
   float* part_ml;              // [B * Hkv][2 * splits][G][2] (max in log2 units, sum)
@@ -77,6 +75,7 @@ hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStrea
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s);
+hipError_t launch_segments(const Dev& d, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 // mode 0: every block, finished output; 1: resident blocks only, partials;

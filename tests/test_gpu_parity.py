@@ -220,3 +220,25 @@ def test_append_capacity_is_checked(spin_lib):
         p.spin.append(dk, dk)
     assert e.value.code == bd.SPIN_ECAPACITY
     p.close()
+
+
+def test_size_limits(spin_lib):
+    """The kernels' size limits at once: 16384 partitions per head (top-k keys
+    fill 64 KiB of LDS), top-k 1024, 65536 slots per request (the resolve
+    kernel's LDS bitmask), 16 query heads per KV head."""
+    w = W.variant(W.C1, name="limits", Hq=16, Hkv=1, ctx=(16384 * 64,), k=1024, steps=3, hot_count=8)
+    p = _pair(w, slots=65536)
+    p.check_summaries()
+    st, _ = p.run(out_sample=16)
+    assert st.misses > 0
+    p.close()
+
+
+def test_tight_budget_with_limits(spin_lib):
+    """Eviction at k = 1024 with variable partitions of up to 4 pages."""
+    w = W.variant(W.C5, name="limits_var", B=1, Hq=16, Hkv=1, ctx=(300000,), k=1024, steps=4,
+                  n_centroids=32, ar_coef=0.2)
+    p = _pair(w, slots=1024 * 4 + 16)
+    st, _ = p.run(out_sample=16)
+    assert st.evictions > 0
+    p.close()
