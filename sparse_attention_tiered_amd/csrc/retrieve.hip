@@ -20,6 +20,8 @@ constexpr int kRetrieveWG = 256;
 // MI355X, 16-128 workgroups pull 56.5-57.4 GB/s of scattered pages, as fast as
 // a bulk DMA copy, while 256+ workgroups drop to 55 GB/s.  A small grid also
 // leaves the other CUs to the attention pass that overlaps the transfer.
+// (96 and 128 workgroups, and half- or quarter-page work units, measured no
+// better for a few misses per step and worse for thousands.)
 constexpr int kRetrieveGrid = 64;
 
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {

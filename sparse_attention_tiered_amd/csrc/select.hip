@@ -101,91 +101,191 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exact top-k per (request, KV head) by MSB-first radix select over 8-bit
-// digits of the order-preserving keys, in LDS.  One workgroup per list.
+// Exact top-k per (request, KV head), one workgroup per list, in LDS.
+//
+// Scores are spread into 2048 buckets linearly between their minimum and
+// maximum.  The map is monotone, so every score in a higher bucket beats every
+// score in a lower one: one histogram and one suffix scan find the bucket
+// holding the k-th score, everything above it is taken, and only that
+// bucket's few candidates are ranked exactly (higher score first, lower id on
+// ties).  A crowded boundary bucket (many equal or nearly equal scores) falls
+// back to an MSB-first radix select over order-preserving keys of its members.
+constexpr int kTopkBins = 2048;
+constexpr int kTopkCand = 256;  // largest boundary bucket ranked pairwise
+
+__device__ __forceinline__ int topk_bucket(float v, float mn, float scale) {
+  return min(kTopkBins - 1, (int)((v - mn) * scale));
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ scores,
                                              int* __restrict__ sel) {
-  __shared__ uint32_t keys[kMaxPartitions];
-  __shared__ int hist[256];
+  static_assert(NT * 2 >= kTopkBins && NT >= kTopkCand, "one thread per bucket pair");
+  __shared__ float vals[kMaxPartitions];
+  __shared__ int hist[kTopkBins];
+  __shared__ int cand[kTopkCand];
+  __shared__ float candv[kTopkCand];
+  __shared__ uint32_t chosen[kMaxPartitions / 32];
   __shared__ int tmp[NT / 64 + 1];
-  __shared__ int sh_digit, sh_kk;
+  __shared__ float rmin[NT / 64], rmax[NT / 64];
+  __shared__ int sh[4];  // boundary bucket, count above it, fill counter / radix state
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv;
   const int n = d.req_parts[b];
   const int k = d.k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int* out = sel + (size_t)bh * k;
   if (n <= k) {
     for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
   const float* srow = scores + (size_t)bh * d.Nmax;
-  for (int i = tid; i < n; i += NT) keys[i] = float_key(srow[i]);
-  uint32_t prefix = 0, mask = 0;
-  int kk = k;  // how many still to take among keys matching `prefix`
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += NT) hist[i] = 0;
-    __syncthreads();
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < n; i += NT) {
+    const float v = srow[i];
+    vals[i] = v;
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
+  for (int i = tid; i < (n + 31) / 32; i += NT) chosen[i] = 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  }
+  if (lane == 0) {
+    rmin[wv] = mn;
+    rmax[wv] = mx;
+  }
+  if (tid == 0) sh[2] = 0;
+  __syncthreads();
+  mn = rmin[0];
+  mx = rmax[0];
+  for (int w = 1; w < NT / 64; ++w) {
+    mn = fminf(mn, rmin[w]);
+    mx = fmaxf(mx, rmax[w]);
+  }
+  // a range too narrow for a finite scale puts everything in bucket 0
+  float scale = (float)kTopkBins / (mx - mn);
+  if (!(scale < 3.0e38f)) scale = 0.f;
+  for (int i = tid; i < n; i += NT) atomicAdd(&hist[topk_bucket(vals[i], mn, scale)], 1);
+  __syncthreads();
+  // counts from the top: thread t holds buckets 2047-2t and 2046-2t
+  {
+    const int hi = kTopkBins - 1 - 2 * tid, lo = hi - 1;
+    const int a = tid < kTopkBins / 2 ? hist[hi] : 0;
+    const int c = tid < kTopkBins / 2 ? hist[lo] : 0;
+    int tot;
+    const int before = block_excl_scan<NT>(a + c, tmp, &tot);
+    if (tid < kTopkBins / 2 && before < k && before + a + c >= k) {
+      const bool in_hi = before + a >= k;
+      sh[0] = in_hi ? hi : lo;
+      sh[1] = in_hi ? before : before + a;
+    }
+  }
+  __syncthreads();
+  const int cut = sh[0];
+  const int need = k - sh[1];  // >= 1: taken from the boundary bucket
+  const int m = hist[cut];     // its members
+  if (m <= kTopkCand) {
     for (int i = tid; i < n; i += NT) {
-      const uint32_t key = keys[i];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      const float v = vals[i];
+      const int bk = topk_bucket(v, mn, scale);
+      if (bk > cut) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+      if (bk == cut) {
+        const int slot = atomicAdd(&sh[2], 1);
+        if (slot < kTopkCand) {
+          cand[slot] = i;
+          candv[slot] = v;
+        }
+      }
     }
     __syncthreads();
-    if (tid < 64) {
-      // lane l holds digits 255-4l .. 252-4l (descending)
-      int c[4], cs = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = hist[255 - 4 * tid - j];
-        cs += c[j];
+    if (tid < m) {
+      const int me = cand[tid];
+      const float v = candv[tid];
+      int rank = 0;
+      for (int j = 0; j < m; ++j) {
+        const int o = cand[j];
+        const float w = candv[j];
+        rank += (w > v || (w == v && o < me)) ? 1 : 0;
       }
-      const int inc = wave_incl_scan(cs);
-      const unsigned long long hit = __ballot(inc >= kk);
-      const int L = __ffsll((long long)hit) - 1;
-      if (tid == L) {
-        int above = inc - cs;
-        int dg = 255 - 4 * tid;
+      if (rank < need) atomicOr(&chosen[me >> 5], 1u << (me & 31));
+    }
+  } else {
+    // radix select among the boundary bucket's members; key 0 marks the rest
+    // (no finite score maps to 0)
+    uint32_t* keys = reinterpret_cast<uint32_t*>(vals);
+    for (int i = tid; i < n; i += NT) {
+      const float v = vals[i];
+      const int bk = topk_bucket(v, mn, scale);
+      if (bk > cut) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+      keys[i] = bk == cut ? float_key(v + 0.f) : 0u;  // -0 ranks as +0
+    }
+    uint32_t prefix = 0, mask = 0;
+    int kk = need;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      __syncthreads();
+      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += NT) {
+        const uint32_t key = keys[i];
+        if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        int c4[4], cs = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (above + c[j] >= kk) {
-            dg = 255 - 4 * tid - j;
-            break;
-          }
-          above += c[j];
+          c4[j] = hist[255 - 4 * tid - j];
+          cs += c4[j];
         }
-        sh_digit = dg;
-        sh_kk = kk - above;
+        const int inc = wave_incl_scan(cs);
+        const unsigned long long hitm = __ballot(inc >= kk);
+        const int L = __ffsll((long long)hitm) - 1;
+        if (tid == L) {
+          int ab = inc - cs, dg = 255 - 4 * tid;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (ab + c4[j] >= kk) {
+              dg = 255 - 4 * tid - j;
+              break;
+            }
+            ab += c4[j];
+          }
+          sh[3] = dg;
+          sh[2] = kk - ab;
+        }
       }
+      __syncthreads();
+      prefix |= (uint32_t)sh[3] << shift;
+      mask |= 0xFFu << shift;
+      kk = sh[2];
     }
-    __syncthreads();
-    prefix |= (uint32_t)sh_digit << shift;
-    mask |= 0xFFu << shift;
-    kk = sh_kk;
-    __syncthreads();
+    // members above the k-th key, then the kk lowest ids equal to it
+    const int E = (n + NT - 1) / NT;
+    const int lo = tid * E, hi = min(n, lo + E);
+    int n_eq = 0;
+    for (int i = lo; i < hi; ++i) n_eq += keys[i] == prefix;
+    int tot;
+    int er = block_excl_scan<NT>(n_eq, tmp, &tot);
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t key = keys[i];
+      const bool take = key > prefix || (key == prefix && er++ < kk);
+      if (take) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+    }
   }
-  // prefix is the k-th largest key; take every larger key and the kk lowest
-  // indices among keys equal to it.
-  const uint32_t T = prefix;
+  __syncthreads();
+  // output in ascending partition id
   const int E = (n + NT - 1) / NT;
   const int lo = tid * E, hi = min(n, lo + E);
-  int n_eq = 0;
-  for (int i = lo; i < hi; ++i) n_eq += keys[i] == T;
-  int tot;
-  int eq_rank = block_excl_scan<NT>(n_eq, tmp, &tot);
   int n_take = 0;
-  for (int i = lo, er = eq_rank; i < hi; ++i) {
-    const uint32_t key = keys[i];
-    if (key > T) ++n_take;
-    else if (key == T) n_take += (er++ < kk);
-  }
+  for (int i = lo; i < hi; ++i) n_take += (chosen[i >> 5] >> (i & 31)) & 1u;
+  int tot;
   int pos = block_excl_scan<NT>(n_take, tmp, &tot);
-  for (int i = lo, er = eq_rank; i < hi; ++i) {
-    const uint32_t key = keys[i];
-    bool take = key > T;
-    if (key == T) take = er++ < kk;
-    if (take && pos < k) out[pos++] = i;
-  }
+  for (int i = lo; i < hi; ++i)
+    if (((chosen[i >> 5] >> (i & 31)) & 1u) && pos < k) out[pos++] = i;
 }
 
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s) {

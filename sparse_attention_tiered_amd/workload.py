@@ -48,7 +48,9 @@ class Workload:
     ``kv_kind`` picks the key structure: "hot" (a few partitions per head pushed
     toward the group's initial query direction), "drift" (a hot set that
     changes over time and pulls the queries with it), "cluster" (keys scattered
-    around seeded centroids), or "plain".
+    around seeded centroids), "ties" (every key of a head is one seeded vector,
+    the hot partitions shifted as in "hot", so scores tie exactly within the
+    two groups), or "plain".
     """
 
     name: str
@@ -233,7 +235,7 @@ def draw_queries(w: Workload, geo: Geometry, n_steps: int | None = None) -> Draw
         for h in range(w.Hkv):
             sets = _hot_sets(w, b, h, n_parts, n_epochs)
             d.hot[(b, h)] = sets
-            if w.kv_kind == "hot":
+            if w.kv_kind in ("hot", "ties"):
                 d.hot_dir[(b, h)] = _unit(state[b, h * G:(h + 1) * G].sum(0)).astype(np.float32)
             elif w.kv_kind == "drift":
                 ever = np.unique(np.concatenate(sets)) if sets else np.zeros(0, np.int64)
@@ -270,6 +272,10 @@ def _fill_head(w: Workload, b: int, h: int, lens: np.ndarray, out: np.ndarray, d
         assign = _rng(w, b, h, _ASSIGN).integers(0, w.n_centroids, size=len(lens))
         K *= np.float32(w.cluster_std)
         K += np.repeat(cent[assign], lens, axis=0)
+    elif w.kv_kind == "ties":
+        K[:] = K[0]
+        for p in draws.hot[(b, h)][0]:
+            K[starts[p]:starts[p] + lens[p]] += np.float32(w.hot_shift) * draws.hot_dir[(b, h)]
     elif w.kv_kind in ("hot", "drift"):
         sets = draws.hot[(b, h)]
         if w.kv_kind == "hot":

@@ -242,3 +242,31 @@ def test_tight_budget_with_limits(spin_lib):
     st, _ = p.run(out_sample=16)
     assert st.evictions > 0
     p.close()
+
+
+# every key of a head is one vector (hot partitions shifted): scores tie
+# exactly inside each group, so the lower-id rule alone decides the selection
+TIES = {
+    # the boundary falls among ~500 equal scores (the crowded-bucket path)
+    "ties_crowded": W.variant(W.C2, name="ties_crowded", B=2, Hq=8, Hkv=2, ctx=(32768, 20000),
+                              k=8, steps=4, kv_kind="ties", hot_count=5),
+    # the boundary falls among the 40 equal hot scores
+    "ties_in_hot": W.variant(W.C2, name="ties_in_hot", B=2, Hq=8, Hkv=2, ctx=(32768, 9000),
+                             k=8, steps=4, kv_kind="ties", hot_count=40),
+    # every score of a head equal (a zero-width score range)
+    "ties_flat": W.variant(W.C2, name="ties_flat", B=1, Hq=8, Hkv=2, ctx=(20000,),
+                           k=16, steps=3, kv_kind="ties", hot_count=0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(TIES))
+def test_exact_ties_take_lower_ids(spin_lib, name):
+    w = TIES[name]
+    p = _pair(w, slots=w.Hkv * w.k * 2)
+    for t in range(p.T):
+        p.spin.select(p.q_dev[t], scores=p.scores)
+        sel_o, _ = p.oracle.select(p.draws.q_bits[t])
+        assert np.array_equal(p.spin.sel.cpu().numpy(), sel_o.astype(np.int32)), t
+    st, _ = p.run()
+    assert st.misses > 0
+    p.close()
