@@ -143,7 +143,7 @@ def main():
     from sparse_attention_tiered_amd import workload as W
 
     w = W.get(args.config)
-    n_steps = max(w.steps, args.warmup + args.steps)
+    n_steps = max(w.steps, args.warmup + 2 * args.steps)
     t0 = time.time()
     geo = W.geometry(w)
     draws = W.draw_queries(w, geo, n_steps)
@@ -171,9 +171,10 @@ def main():
     overlap = not args.single_stream and not args.no_overlap
 
     def step(t, ev=None):
-        # events: 0 start, 1 select done, 2 resolve done, 3 resident-page
-        # attention done (overlapped with retrieve), 4 retrieve done (copy
-        # stream), 5 attention done
+        # events (instrumented pass only): 0 start, 1 select done, 2 resolve
+        # done (S); 3 retrieve start, 4 retrieve done (copy stream); 5
+        # resident-page attention done (overlapped with retrieve), 6 attention
+        # done (S)
         if ev is not None:
             ev[0].record(S)
         spin.select(q[t], stream=S)
@@ -182,57 +183,75 @@ def main():
         spin.resolve_evict(t, stream=S)
         if ev is not None:
             ev[2].record(S)
+            if Cs is not S:
+                Cs.wait_stream(S)
+            ev[3].record(Cs)
         spin.retrieve(copy_stream=Cs)
         if ev is not None:
             ev[4].record(Cs)
         if overlap:
             spin.attend_begin(q[t], stream=S)
             if ev is not None:
-                ev[3].record(S)
+                ev[5].record(S)
             spin.attend_finish(q[t], stream=S)
         else:
             if ev is not None:
-                ev[3].record(S)
+                ev[5].record(S)
             spin.attend(q[t], stream=S)
         if ev is not None:
-            ev[5].record(S)
+            ev[6].record(S)
 
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
     st0, _ = spin.stats()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    K = args.steps
+    # timed pass: the steps alone (a timing event costs the GPU several
+    # microseconds, so the per-stage events go in a second pass)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(S)
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for i in range(K):
+        if overlap or args.single_stream:
+            # the library's whole-step call (one entry into the library)
+            spin.step(q[args.warmup + i], args.warmup + i, stream=S, copy_stream=Cs)
+        else:
+            step(args.warmup + i)
     end.record(S)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     st1, _ = spin.stats()
     total_ms = start.elapsed_time(end)
-    K = args.steps
-    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend_resident": 0.0,
-             "attend": 0.0}
-    for e in evs:
-        stage["select"] += e[0].elapsed_time(e[1])
-        stage["resolve_evict"] += e[1].elapsed_time(e[2])
-        stage["retrieve"] += e[2].elapsed_time(e[4])
-        stage["attend_resident"] += e[2].elapsed_time(e[3]) if overlap else 0.0
-        # after the transfer: fetched-page attention and the merge (or the
-        # whole attention without overlap)
-        stage["attend"] += max(e[4].elapsed_time(e[5]), 0.0) if overlap else e[4].elapsed_time(e[5])
-    stage_ms = {k: v / K for k, v in stage.items()}
     ms_per_step = total_ms / K
     value = w.B * w.Hq / (ms_per_step * 1e-3)
 
-    # kernel-isolated replays on the last timed step's live data (select and
+    # instrumented pass: the next K steps with an event between stages
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(args.warmup + K + i, evs[i])
+    torch.cuda.synchronize()
+    st2, _ = spin.stats()
+    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend_resident": 0.0,
+             "attend": 0.0}
+    instr_ms = 0.0
+    for e in evs:
+        stage["select"] += e[0].elapsed_time(e[1])
+        stage["resolve_evict"] += e[1].elapsed_time(e[2])
+        stage["retrieve"] += e[3].elapsed_time(e[4])
+        stage["attend_resident"] += e[2].elapsed_time(e[5]) if overlap else 0.0
+        # after the transfer: fetched-page attention and the merge (or the
+        # whole attention without overlap)
+        stage["attend"] += max(e[4].elapsed_time(e[6]), 0.0) if overlap else e[4].elapsed_time(e[6])
+        instr_ms += e[0].elapsed_time(e[6])
+    stage_ms = {k: v / K for k, v in stage.items()}
+
+    # kernel-isolated replays on the last step's live data (select and
     # attention only read the residency state), so the HBM rooflines are not
     # mixed with the transfer that overlaps them inside a step
-    last = args.warmup + K - 1
+    last = args.warmup + 2 * K - 1
     reps = 10
     iso = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
@@ -256,7 +275,8 @@ def main():
     attend_bytes = (hits + misses) * PAGE_BYTES / K + w.B * w.Hq * 128 * (2 + 4)
     n_parts = sum(len(l) for l in geo.lens)
     score_bytes = w.Hkv * n_parts * 128 * 4 + w.B * w.Hq * 128 * 2 + w.Hkv * n_parts * 4
-    retrieve_bytes = misses * PAGE_BYTES / K
+    # the transfer's bytes per launch in the instrumented pass it is timed in
+    retrieve_bytes = (st2.misses - st1.misses) * PAGE_BYTES / K
     iso_attend_bytes = last_pages * PAGE_BYTES + w.B * w.Hq * 128 * (2 + 4)
     link = pcie_link()
     memcpy_gbs = memcpy_h2d_gbs()
@@ -272,7 +292,7 @@ def main():
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
                    "kernels": ["k_score", "k_topk"]},
         "retrieve": {"bound": "pcie",
-                     "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if misses else 0.0,
+                     "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if retrieve_bytes else 0.0,
                      "launch_ms": stage_ms["retrieve"],
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
                      "kernels": ["k_retrieve"]},
@@ -298,6 +318,7 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "stages_ms": stage_ms,
+        "ms_per_step_instrumented": instr_ms / K,
         "overlap_retrieve_attend": overlap,
         "rooflines": rl,
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,

@@ -52,7 +52,11 @@
  * call reports as SPIN_EDEVICE; the residency state is then undefined until
  * the requests are indexed again.  A context is not thread-safe; use one per
  * (compute stream, copy stream) pair.  Streams are hipStream_t values passed
- * as void* (NULL = the null stream).
+ * as void* (NULL = the null stream).  resolve_evict, attention and every call
+ * that changes a request (index, offload, append, release) wait for the
+ * latest spin_retrieve; the context remembers which stream already waited for
+ * it and does not wait there twice, so a stream given to a context must not
+ * be destroyed (and its handle reused) before the context is.
  */
 #ifndef SPIN_H
 #define SPIN_H
@@ -208,7 +212,8 @@ SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* 
  * resident, non-mandatory slots; whole buckets from 0 upward, lower slot
  * first in the last bucket.  Misses take the free slots in ascending order.
  * Emptied segments return to the shared pool; first inserts into an empty
- * directory range take one.  Writes the block tables and the fetch list.
+ * directory range take one.  Writes the block tables and the insert lists
+ * spin_retrieve reads (so it waits for the previous spin_retrieve).
  * t must not decrease between calls. */
 SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
                                 int32_t* d_block_table, int32_t* d_block_ntok,

@@ -26,10 +26,17 @@
 
 namespace spin {
 
+// the emptied-segment flags of a request's whole directory fit the slot bitmask
+static_assert(kMaxKvHeads * (kMaxPartitions * kMaxPPP / kSegEntries) <= kMaxSlots, "");
+
+// slot codes besides the recency buckets 0..63 of eviction candidates
+constexpr uint8_t kCodeVictim = 0xFD, kCodeFree = 0xFE, kCodePinned = 0xFF;
+
 __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__ sel, int t,
                                                   int* __restrict__ bt, int* __restrict__ bntok,
                                                   int* __restrict__ bcount) {
   __shared__ uint32_t mand[kMaxSlots / 32];
+  __shared__ uint8_t code[kMaxSlots];  // per slot: recency bucket, or a kCode* mark
   __shared__ int item_off[kMaxItems + 1];
   __shared__ int hist[kBuckets];
   __shared__ int tmp[17];
@@ -95,11 +102,19 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       if (p >= 0 && p < n_parts) {
         np = (plen[p] + kPageTokens - 1) / kPageTokens;
         pos0 = item_off[i] - item_off[h * k];
-        for (int j = 0; j < np; ++j) {
-          const int page = pfirst[p] + j;
-          const int ntok = min(kPageTokens, plen[p] - kPageTokens * j);
-          const int seg = dir[h * d.ndir + (page >> 6)];
-          int slot = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
+        const int pf0 = pfirst[p], pl = plen[p];
+        int slots[kMaxPPP];
+#pragma unroll
+        for (int j = 0; j < kMaxPPP; ++j) {
+          const int page = pf0 + j;
+          const int seg = j < np ? dir[h * d.ndir + (page >> 6)] : -1;
+          slots[j] = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxPPP; ++j) {
+          if (j >= np) break;
+          const int ntok = min(kPageTokens, pl - kPageTokens * j);
+          int slot = slots[j];
           if (slot >= C) {
             atomicOr(d.err, kErrState);
             slot = -1;
@@ -133,20 +148,52 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
 
   // 3. bucketed LRU, only when the resident pages plus the misses exceed the
   //    request's budget (with the budget at the whole area: when the misses
-  //    outnumber the free slots); a shrunk budget is enforced here, lazily
+  //    outnumber the free slots); a shrunk budget is enforced here, lazily.
+  //
+  //    One coalesced sweep turns the request's slots into one-byte codes in
+  //    LDS (recency bucket of an eviction candidate, or free / pinned) and
+  //    builds the histogram; every ordered decision after it (the victims of
+  //    the cutoff bucket, the free slots the misses take) is one workgroup
+  //    scan over contiguous per-thread slot ranges of those codes, and the
+  //    global updates run afterwards, one slot or one miss per thread.
   const int freec = d.free_count[b];
   const int need = (C - freec) + nmiss - d.budget[b];
   int nfreed = 0, cut = -1;
-  if (need > 0) {
-    if (tid < kBuckets) hist[tid] = 0;
-    __syncthreads();
-    for (int c = tid; c < C; c += 1024) {
-      if (owner[c] >= 0 && !((mand[c >> 5] >> (c & 31)) & 1u)) {
-        const int bk = (kBuckets - 1) - min(kBuckets - 1, t - last[c]);
-        atomicAdd(&hist[bk], 1);
+  if (tid < kBuckets) hist[tid] = 0;
+  __syncthreads();
+  if (need > 0 || nmiss > 0) {
+    constexpr int U = 8;  // slots per thread whose loads are in flight together
+    for (int c0 = tid; c0 < C; c0 += 1024 * U) {
+      int ow[U], lu[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 1024 * u;
+        ow[u] = c < C ? owner[c] : -1;
+        lu[u] = (c < C && need > 0) ? last[c] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 1024 * u;
+        if (c >= C) break;
+        uint8_t v;
+        if (ow[u] < 0) {
+          v = kCodeFree;
+        } else if ((mand[c >> 5] >> (c & 31)) & 1u) {
+          v = kCodePinned;
+        } else if (need > 0) {
+          v = (uint8_t)((kBuckets - 1) - min(kBuckets - 1, t - lu[u]));
+          atomicAdd(&hist[v], 1);
+        } else {
+          v = kCodePinned;  // nothing is evicted this step
+        }
+        code[c] = v;
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  const int E = (C + 1023) / 1024;  // contiguous slots per thread
+  const int lo = min(C, tid * E), hi = min(C, lo + E);
+  if (need > 0) {
     if (tid == 0) {
       int below = 0, cv = 0;
       while (cv < kBuckets - 1 && below + hist[cv] < need) below += hist[cv++];
@@ -156,77 +203,79 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     __syncthreads();
     cut = sh_cut;
     const int rem = need - sh_below;  // taken from the cutoff bucket, lowest slots first
-    int ecarry = 0;
-    for (int base = 0; base < C; base += 1024) {
-      const int c = base + tid;
-      bool cand = false;
-      int bk = -1;
-      if (c < C && owner[c] >= 0 && !((mand[c >> 5] >> (c & 31)) & 1u)) {
-        cand = true;
-        bk = (kBuckets - 1) - min(kBuckets - 1, t - last[c]);
-      }
-      const int at = (cand && bk == cut) ? 1 : 0;
+    {
+      int at = 0;
+      for (int c = lo; c < hi; ++c) at += code[c] == cut;
       int tot;
-      const int ex = block_excl_scan<1024>(at, tmp, &tot);
-      if (cand && (bk < cut || (at && ecarry + ex < rem))) {
-        const int own = owner[c];
-        const int h = own / d.max_pages, page = own - h * d.max_pages;
-        const int seg = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
-        if (seg >= 0 && seg < d.n_seg) {
-          d.segments[(size_t)seg * kSegEntries + (page & 63)] = -1;
-          atomicSub(&d.seg_live[seg], 1);
-        } else {
-          atomicOr(d.err, kErrState);
-        }
-        owner[c] = -1;
-        last[c] = -1;
+      int rank = block_excl_scan<1024>(at, tmp, &tot);
+      for (int c = lo; c < hi; ++c) {
+        const int v = code[c];
+        if (v < cut || (v == cut && rank++ < rem)) code[c] = kCodeVictim;
       }
-      ecarry += tot;
     }
     __syncthreads();
-    // emptied segments leave the directory, in (head, directory index) order
-    const int ne = Hkv * d.ndir;
-    int fcarry = 0;
-    for (int base = 0; base < ne; base += 1024) {
-      const int e = base + tid;
-      int seg = -1, fl = 0;
-      if (e < ne) {
-        seg = dir[e];
-        fl = (seg >= 0 && load_device(&d.seg_live[seg]) == 0) ? 1 : 0;
+    for (int c = tid; c < C; c += 1024) {
+      if (code[c] != kCodeVictim) continue;
+      const int own = owner[c];
+      const int h = own / d.max_pages, page = own - h * d.max_pages;
+      const int seg = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
+      if (seg >= 0 && seg < d.n_seg) {
+        d.segments[(size_t)seg * kSegEntries + (page & 63)] = -1;
+        atomicSub(&d.seg_live[seg], 1);
+      } else {
+        atomicOr(d.err, kErrState);
       }
-      int tot;
-      const int ex = block_excl_scan<1024>(fl, tmp, &tot);
-      if (fl) {
-        d.freed[(size_t)b * ne + fcarry + ex] = seg;
+      owner[c] = -1;
+      last[c] = -1;
+      code[c] = kCodeFree;
+    }
+    __syncthreads();
+    // emptied segments leave the directory, in (head, directory index) order:
+    // flag them (a bit per directory entry, reusing the mandatory bitmask,
+    // which is no longer read), then list them with one ordered scan
+    const int ne = Hkv * d.ndir;
+    for (int i = tid; i < (ne + 31) / 32; i += 1024) mand[i] = 0;
+    __syncthreads();
+    for (int e = tid; e < ne; e += 1024) {
+      const int seg = dir[e];
+      if (seg >= 0 && load_device(&d.seg_live[seg]) == 0) atomicOr(&mand[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    const int Ed = (ne + 1023) / 1024;
+    const int elo = min(ne, tid * Ed), ehi = min(ne, elo + Ed);
+    int nf = 0;
+    for (int e = elo; e < ehi; ++e) nf += (mand[e >> 5] >> (e & 31)) & 1u;
+    int r = block_excl_scan<1024>(nf, tmp, &nfreed);
+    for (int e = elo; e < ehi; ++e)
+      if ((mand[e >> 5] >> (e & 31)) & 1u) {
+        d.freed[(size_t)b * ne + r++] = dir[e];
         dir[e] = -1;
       }
-      fcarry += tot;
-    }
-    nfreed = fcarry;
   }
 
-  // 4. misses take the free slots in ascending slot order
+  // 4. misses take the free slots in ascending slot order: the rank of each
+  //    free slot goes to the insert list, then one thread per miss fills it
   int assigned = 0;
+  int4* insb = d.ins + (size_t)b * d.max_mand;
   if (nmiss > 0) {
-    int acarry = 0;
-    for (int base = 0; base < C && acarry < nmiss; base += 1024) {
-      const int c = base + tid;
-      const int fr = (c < C && owner[c] < 0) ? 1 : 0;
-      int tot;
-      const int ex = block_excl_scan<1024>(fr, tmp, &tot);
-      const int r = acarry + ex;
-      if (fr && r < nmiss) {
-        const int4 m = misses[r];  // (h, page, block position, valid tokens)
-        owner[c] = m.x * d.max_pages + m.y;
-        last[c] = t;
-        btb[m.x * MB + m.z] = b * C + c;
-        bnb[m.x * MB + m.z] = m.w;
-        d.bmiss[((size_t)b * Hkv + m.x) * MB + m.z] = 1;
-        d.ins[(size_t)b * d.max_mand + r] = make_int4(c, m.x, m.y, 0);
-      }
-      acarry += tot;
+    int fr = 0;
+    for (int c = lo; c < hi; ++c) fr += code[c] == kCodeFree;
+    int tot;
+    int r = block_excl_scan<1024>(fr, tmp, &tot);
+    for (int c = lo; c < hi && r < nmiss; ++c)
+      if (code[c] == kCodeFree) insb[r++].x = c;
+    assigned = min(tot, nmiss);
+    __syncthreads();
+    for (int j = tid; j < assigned; j += 1024) {
+      const int c = insb[j].x;
+      const int4 m = misses[j];  // (h, page, block position, valid tokens)
+      owner[c] = m.x * d.max_pages + m.y;
+      last[c] = t;
+      btb[m.x * MB + m.z] = b * C + c;
+      bnb[m.x * MB + m.z] = m.w;
+      d.bmiss[((size_t)b * Hkv + m.x) * MB + m.z] = 1;
+      insb[j] = make_int4(c, m.x, m.y, 0);
     }
-    assigned = min(acarry, nmiss);
   }
   __syncthreads();
 

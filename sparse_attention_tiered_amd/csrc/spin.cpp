@@ -27,12 +27,30 @@ struct spin_ctx {
   std::vector<ReqMirror> req;
   hipEvent_t ev_resolved = nullptr;  // recorded after resolve/evict
   hipEvent_t ev_fetched = nullptr;   // recorded after retrieve
+  // Which recording of ev_fetched is the latest (0: none yet), the stream it
+  // was recorded on, and the stream that last waited for that recording: a
+  // stream already ordered after the transfer needs no second wait (each wait
+  // costs the GPU several microseconds even when the event has completed).
+  uint64_t fetched_gen = 0, waited_gen = 0;
+  hipStream_t fetched_on = nullptr, waited_on = nullptr;
   int hip_err = 0;
   int last_t = -1;
   size_t ws_bytes = 0;
 };
 
 namespace {
+
+// Orders stream s after the latest transfer (see spin_ctx::fetched_gen).
+hipError_t wait_fetched(spin_ctx* ctx, hipStream_t s) {
+  if (ctx->fetched_gen == 0 || s == ctx->fetched_on) return hipSuccess;
+  if (s == ctx->waited_on && ctx->waited_gen == ctx->fetched_gen) return hipSuccess;
+  const hipError_t e = hipStreamWaitEvent(s, ctx->ev_fetched, 0);
+  if (e == hipSuccess) {
+    ctx->waited_on = s;
+    ctx->waited_gen = ctx->fetched_gen;
+  }
+  return e;
+}
 
 struct Derived {
   int G, ndir, max_blocks, max_mand, pps, splits;
@@ -47,7 +65,7 @@ int check(const spin_config* c) {
       c->seg_entries != spin::kSegEntries || c->num_buckets != spin::kBuckets)
     return SPIN_EINVAL;
   if (c->max_batch < 1 || c->max_batch > 1024) return SPIN_EINVAL;
-  if (c->num_kv_heads < 1 || c->num_kv_heads > 16) return SPIN_EINVAL;
+  if (c->num_kv_heads < 1 || c->num_kv_heads > spin::kMaxKvHeads) return SPIN_EINVAL;
   if (c->num_q_heads < c->num_kv_heads || c->num_q_heads % c->num_kv_heads) return SPIN_EINVAL;
   if (c->num_q_heads / c->num_kv_heads > spin::kMaxGroup) return SPIN_EINVAL;
   if (c->max_partitions < 1 || c->max_partitions > spin::kMaxPartitions) return SPIN_EINVAL;
@@ -272,6 +290,7 @@ SPIN_API int spin_destroy(spin_ctx* ctx) {
 
 SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream) {
   if (!ctx || req < 0 || req >= ctx->cfg.max_batch) return SPIN_EINVAL;
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_release(ctx->dev, req, S(stream)));
   HIPCHK(ctx, hipStreamSynchronize(S(stream)));
   ctx->req[req] = ReqMirror();
@@ -330,6 +349,7 @@ int register_request(spin_ctx* ctx, int32_t req, unsigned long long host_base, i
                      int pages, const void* src, int src_stride, hipStream_t s) {
   Dev& v = ctx->dev;
   const int np = (int)lens.size();
+  HIPCHK(ctx, wait_fetched(ctx, s));
   HIPCHK(ctx, spin::launch_release(v, req, s));
   if (np) {
     HIPCHK(ctx, hipMemcpyAsync(v.part_first + (size_t)req * v.Nmax, first.data(), np * sizeof(int),
@@ -411,6 +431,7 @@ SPIN_API int spin_append(spin_ctx* ctx, const void* d_k, const void* d_v, void* 
       return SPIN_ECAPACITY;
     if (!fresh && m.last_len >= spin::kPageTokens * c.max_pages_per_partition) return SPIN_ECAPACITY;
   }
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_append(ctx->dev, static_cast<const uint16_t*>(d_k),
                                   static_cast<const uint16_t*>(d_v), S(stream)));
   for (ReqMirror& m : ctx->req) {
@@ -443,7 +464,7 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
   if (t < ctx->last_t) return SPIN_EINVAL;
   ctx->last_t = t;
   // the previous step's transfer reads the insert lists this call rewrites
-  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_resolve(ctx->dev, d_sel, t, d_block_table, d_block_ntok, d_block_count,
                                    S(stream)));
   // The transfer needs only k_resolve's insert lists, but the segment-pool
@@ -459,6 +480,8 @@ SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream) {
   HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
   HIPCHK(ctx, spin::launch_retrieve(ctx->dev, S(copy_stream)));
   HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
+  ++ctx->fetched_gen;
+  ctx->fetched_on = S(copy_stream);
   return SPIN_OK;
 }
 
@@ -467,7 +490,7 @@ SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_
                          void* stream) {
   if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
   if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
-  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
                                   d_block_ntok, d_block_count, d_out, spin::kAttendAll, S(stream)));
   return SPIN_OK;
@@ -489,7 +512,7 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
                                 float* d_out, void* stream) {
   if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
   if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
-  HIPCHK(ctx, hipStreamWaitEvent(S(stream), ctx->ev_fetched, 0));
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
                                   d_block_ntok, d_block_count, d_out, spin::kAttendFetched,
                                   S(stream)));

@@ -17,6 +17,7 @@ constexpr int kMaxSlots = 65536;
 constexpr int kMaxItems = 4096;        // Hkv * topk, mandatory partitions of one request
 constexpr int kMaxPPP = 4;             // pages per partition
 constexpr int kMaxGroup = 16;          // query heads per KV head
+constexpr int kMaxKvHeads = 16;
 
 // device error-word bits (kept equal to the SPIN_DEVERR_* values of spin.h)
 constexpr int kErrPartition = 1;       // selected partition id out of range

@@ -270,3 +270,15 @@ def test_exact_ties_take_lower_ids(spin_lib, name):
     st, _ = p.run()
     assert st.misses > 0
     p.close()
+
+
+def test_max_batch(spin_lib):
+    """1024 requests (the batch limit) of ragged, tiny contexts under a budget
+    of mandatory + 1 page: the batch-wide prefix sums of the transfer and of
+    the shared segment pool at their largest."""
+    ctx = tuple(64 * 3 - (b % 7) * 20 for b in range(1024))
+    w = W.variant(W.C1, name="max_batch", B=1024, Hq=4, Hkv=2, ctx=ctx, k=2, steps=4, ar_coef=0.2)
+    p = _pair(w, slots=2 * 2 + 1)
+    st, _ = p.run()
+    assert st.misses > 0 and st.evictions > 0
+    p.close()
