@@ -4,7 +4,12 @@ A step is one pass of the whole decode path for a batch: select (score +
 top-k), two-level resolve with bucketed-LRU eviction, retrieve of missed pages
 from pinned host memory (on a second stream), and paged sparse attention.
 Inputs (host KV, queries for every step) are resident before the timed
-region.  Prints one JSON line.
+region.  Runs step 0 (all misses) with stage events, W-1 more warm-up steps,
+K timed steps (the whole-step call, no events inside: `value`), K more steps
+with an event between stages (stage times, the transfer's rate), then
+isolated replays of select and attention on the last step's data, warm and
+after a 512 MB read that evicts the memory-side cache (cold).  Prints one
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config c4] [--gpus 1]
 """
@@ -142,6 +147,8 @@ def main():
     from sparse_attention_tiered_amd import binding as bd
     from sparse_attention_tiered_amd import workload as W
 
+    if args.warmup < 1:
+        ap.error("--warmup must be at least 1 (step 0 is timed on its own)")
     w = W.get(args.config)
     n_steps = max(w.steps, args.warmup + 2 * args.steps)
     t0 = time.time()
@@ -201,7 +208,16 @@ def main():
         if ev is not None:
             ev[6].record(S)
 
-    for t in range(args.warmup):
+    # step 0 (every mandatory page a miss) with stage events, reported on its own
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    step(0, ev0)
+    torch.cuda.synchronize()
+    st_s0, _ = spin.stats()
+    s0_ret_ms = ev0[3].elapsed_time(ev0[4])
+    step0 = {"ms": ev0[0].elapsed_time(ev0[6]), "misses": st_s0.misses,
+             "retrieve_ms": s0_ret_ms,
+             "retrieve_GBps": st_s0.misses * PAGE_BYTES / (s0_ret_ms * 1e-3) / 1e9}
+    for t in range(1, args.warmup):
         step(t)
     torch.cuda.synchronize()
     st0, _ = spin.stats()
@@ -228,16 +244,24 @@ def main():
     value = w.B * w.Hq / (ms_per_step * 1e-3)
 
     # instrumented pass: the next K steps with an event between stages
+    # (the device counters are read after every step: the transfer's bytes per step)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
     torch.cuda.synchronize()
+    step_miss = []
+    prev = st1.misses
     for i in range(K):
         step(args.warmup + K + i, evs[i])
-    torch.cuda.synchronize()
-    st2, _ = spin.stats()
+        st_i, _ = spin.stats()
+        step_miss.append(st_i.misses - prev)
+        prev = st_i.misses
+    st2 = st_i
     stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend_resident": 0.0,
              "attend": 0.0}
     instr_ms = 0.0
+    step_ms, ret_ms = [], []
     for e in evs:
+        step_ms.append(e[0].elapsed_time(e[6]))
+        ret_ms.append(e[3].elapsed_time(e[4]))
         stage["select"] += e[0].elapsed_time(e[1])
         stage["resolve_evict"] += e[1].elapsed_time(e[2])
         stage["retrieve"] += e[3].elapsed_time(e[4])
@@ -266,7 +290,33 @@ def main():
     torch.cuda.synchronize()
     iso_select_ms = iso[0].elapsed_time(iso[1]) / reps
     iso_attend_ms = iso[2].elapsed_time(iso[3]) / reps
+    # cold replays: a 512 MB read before each one fills the 256 MB memory-side
+    # cache with clean lines of another buffer, so the kernel reads HBM (a write
+    # would leave dirty lines whose write-back the kernel would pay for); an
+    # event pair brackets the kernel alone (the pair's own cost, timed with
+    # nothing between, is reported beside it)
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    bd.read_stream(scratch, sink, S)  # written back once; later reads leave it clean
+
+    def cold(fn):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(reps)]
+        for a, b in pairs:
+            bd.read_stream(scratch, sink, S)
+            a.record(S)
+            fn()
+            b.record(S)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in pairs) / reps
+
+    cold_select_ms = cold(lambda: spin.select(q[last], stream=S))
+    cold_attend_ms = cold(lambda: spin.attend(q[last], stream=S))
+    event_pair_ms = cold(lambda: None)
+    del scratch, sink
     last_pages = int(spin.block_count.sum().item())
+    # valid tokens of every (request, KV head) block table of the last step
+    attended_tokens = int(spin.block_ntok.sum().item())
 
     hits = st1.hits - st0.hits
     misses = st1.misses - st0.misses
@@ -297,6 +347,21 @@ def main():
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
                      "kernels": ["k_retrieve"]},
     }
+    # the transfer over the steps that move at least 8 MB (small transfers are
+    # dominated by a fixed latency), and step 0 on its own
+    big = [i for i in range(K) if step_miss[i] * PAGE_BYTES >= 8e6]
+    rl["retrieve"]["steps_ge_8MB"] = len(big)
+    rl["retrieve"]["achieved_ge_8MB"] = (
+        sum(step_miss[i] for i in big) * PAGE_BYTES / (sum(ret_ms[i] for i in big) * 1e-3) / 1e9
+        if big else None)
+    rl["retrieve"]["step0"] = step0
+    rl["attend"]["cold"] = {"launch_ms": cold_attend_ms,
+                            "achieved": iso_attend_bytes / (cold_attend_ms * 1e-3) / 1e9}
+    rl["select"]["cold"] = {"launch_ms": cold_select_ms,
+                            "achieved": score_bytes / (cold_select_ms * 1e-3) / 1e9}
+    for k in ("attend", "select"):
+        rl[k]["cold"]["frac"] = rl[k]["cold"]["achieved"] / HBM_PEAK_GBS
+        rl[k]["cold"]["event_pair_ms"] = event_pair_ms
     for v in rl.values():
         v["frac"] = v["achieved"] / v["peak"]
     # dominant stage of the step: the transfer, or the HBM kernels run alone
@@ -319,6 +384,8 @@ def main():
         "roofline": roof,
         "stages_ms": stage_ms,
         "ms_per_step_instrumented": instr_ms / K,
+        "median_step_ms_instrumented": float(np.median(step_ms)),
+        "attended_head_tokens_per_s": attended_tokens / (iso_attend_ms * 1e-3),
         "overlap_retrieve_attend": overlap,
         "rooflines": rl,
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,

@@ -295,6 +295,16 @@ class Spin:
             pass
 
 
+def read_stream(buf, sink, stream=None):
+    """Enqueue spin_read_stream over the bytes of device tensor `buf` (a
+    multiple of 16 bytes); `sink` is a device int32 tensor of 4 elements."""
+    lib = load()
+    rc = lib.spin_read_stream(c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                              c_void_p(sink.data_ptr()), _stream(stream))
+    if rc != SPIN_OK:
+        raise SpinError("spin_read_stream", rc)
+
+
 def read_stream_gbs(nbytes=4 << 30, reps=5):
     """Practical HBM read ceiling: GB/s of spin_read_stream over nbytes."""
     import torch

@@ -282,3 +282,33 @@ def test_max_batch(spin_lib):
     st, _ = p.run()
     assert st.misses > 0 and st.evictions > 0
     p.close()
+
+
+def test_streams_change_between_steps(spin_lib):
+    """The whole-step call with the stream roles moving every step (this
+    step's copy stream computes the next one) matches the oracle, and is
+    bit-identical to the same steps on one fixed stream pair: every wait for
+    a transfer lands where it must."""
+    import torch
+
+    w = W.variant(W.C1, name="rotating", steps=12, ar_coef=0.2)
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    fixed = (torch.cuda.Stream(), torch.cuda.Stream())
+    a = _pair(w, slots=2 * 8 + 4)
+    b = _pair(w, slots=2 * 8 + 4, oracle=False)
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        s, c = streams[t % 3], streams[(t + 1) % 3]
+        a.spin.step(a.q_dev[t], t, stream=s, copy_stream=c)
+        b.spin.step(b.q_dev[t], t, stream=fixed[0], copy_stream=fixed[1])
+        torch.cuda.synchronize()
+        sel_o, blocks, out_o = a.oracle.step(a.draws.q_bits[t], t)
+        assert np.array_equal(a.spin.sel.cpu().numpy(), sel_o.astype(np.int32)), t
+        out = a.spin.out.cpu().numpy()
+        assert np.max(np.abs(out - out_o)) <= 2e-3, t
+        assert np.array_equal(out.view(np.uint32), b.spin.out.cpu().numpy().view(np.uint32)), t
+        a.check_state(t)
+    st, _ = a.spin.stats()
+    assert st.error_word == 0 and st.evictions > 0
+    a.close()
+    b.close()
