@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--budget-ratio", type=float, default=None,
                     help="buffer elasticity ablation: each request's budget = mandatory pages "
                          "x (1 + ratio), capped by its slots (0 = no buffer pages)")
+    ap.add_argument("--host-segments", action="store_true",
+                    help="keep the second-level segment tables in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain elementwise copy of 256 MiB three times "
                          "(reference kernel for the HBM byte counters)")
@@ -159,7 +161,8 @@ def main():
     log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s "
         f"({sum(h[0].numel() * 2 for h in host) / 1e9:.2f} GB pinned host KV)")
     cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts, geo.max_pages, w.k, w.slots_per_request,
-                         max_pages_per_partition=geo.max_ppp, attend_pages_per_split=args.pps)
+                         max_pages_per_partition=geo.max_ppp, attend_pages_per_split=args.pps,
+                         host_segments=args.host_segments)
     spin = bd.Spin(cfg)
     t0 = time.time()
     for b in range(w.B):
@@ -380,6 +383,7 @@ def main():
                    "context": w.ctx[0], "topk": w.k, "slots_per_request": w.slots_per_request,
                    "budget_per_request": budget,
                    "partitions": "variable 16-256" if w.var_len else "fixed 64",
+                   "segment_tables": "host" if args.host_segments else "gpu",
                    "parallelism": "single-gpu"},
         "roofline": roof,
         "stages_ms": stage_ms,
@@ -404,12 +408,18 @@ def main():
     flat_prov = prov_batch * w.layers * w.Hkv * prov_pages * 4
     dir_prov = prov_batch * w.layers * w.Hkv * ((prov_pages + 63) // 64) * 4
     two_level_prov = dir_prov + md["live_segments"] * w.layers * seg_b + w.B * w.layers * w.slots_per_request * 8
+    # with the segment tables in host memory the GPU keeps the directory, the
+    # segments' live counts and stack, and the reverse maps
+    two_level_gpu_hs = dir_prov + md["live_segments"] * w.layers * 8 + w.B * w.layers * w.slots_per_request * 8
     line["metadata"] = {
         "measured": md,
+        "segments_in_host_memory": bool(args.host_segments),
         "projection": {"provisioned_batch": prov_batch, "provisioned_context": prov_ctx,
                        "layers": w.layers, "active_batch": w.B,
                        "flat_table_bytes": flat_prov, "two_level_bytes": two_level_prov,
-                       "ratio": flat_prov / two_level_prov},
+                       "ratio": flat_prov / two_level_prov,
+                       "two_level_gpu_bytes_segments_in_host": two_level_gpu_hs,
+                       "ratio_segments_in_host": flat_prov / two_level_gpu_hs},
     }
     if args.copy_calibration:
         n = 64 << 20  # 64 Mi float32 = 256 MiB read + 256 MiB written per launch

@@ -100,6 +100,9 @@ typedef struct spin_config {
   int32_t seg_entries;             /* must be 64 */
   int32_t num_buckets;             /* must be 64 */
   int32_t attend_pages_per_split;  /* attention split size in pages; 0 = automatic */
+  int32_t segments_in_host_memory; /* 0: segments in the GPU workspace; 1: the segment
+                                      tables in caller-provided pinned host memory
+                                      (spin_create_ex) */
 } spin_config;
 
 typedef struct spin_stats {
@@ -119,6 +122,9 @@ typedef struct spin_metadata {
   uint64_t flat_table_bytes;    /* one flat entry per (request, KV head, page) instead */
   int32_t live_segments;
   int32_t num_segments;
+  uint64_t host_segment_bytes;  /* segment tables held in host memory (0 unless
+                                   segments_in_host_memory); segment_pool_bytes
+                                   then counts only the GPU part (live counts, stack) */
 } spin_metadata;
 
 /* Fill *cfg with the fixed geometry (head_dim 128, page_tokens 64,
@@ -134,6 +140,10 @@ SPIN_API int spin_config_check(const spin_config* cfg);
 /* Bytes of device workspace and of the page pool the caller must provide. */
 SPIN_API int spin_workspace_size(const spin_config* cfg, size_t* ws_bytes, size_t* pool_bytes);
 
+/* Bytes of pinned host memory spin_create_ex needs for the segment tables
+ * (num_segments * 64 * 4 when segments_in_host_memory, else 0). */
+SPIN_API int spin_host_segment_bytes(const spin_config* cfg, size_t* bytes);
+
 /* Derived sizes: directory entries per (request, head) = ceil(max_pages/64),
  * max_blocks = topk * max_pages_per_partition, and attention splits per head. */
 SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_blocks,
@@ -144,6 +154,23 @@ SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_bl
  * stack).  Synchronises `stream`. */
 SPIN_API int spin_create(const spin_config* cfg, void* d_workspace, size_t ws_bytes,
                          void* d_pool, size_t pool_bytes, void* stream, spin_ctx** out);
+
+/* spin_create with the second-level segment tables in host memory (the tier
+ * split of the hierarchical metadata in [GP] C, where the second level sits
+ * in host memory; [XT] part 3 keeps it on the GPU, which spin_create does).
+ * h_segments: pinned host memory (hipHostMalloc or a pinned torch tensor) of
+ * at least spin_host_segment_bytes() bytes, owned by the caller, outliving
+ * the context; the kernels read and write it through its device-mapped
+ * address.  The directory, the segments' live counts and the free stack stay
+ * in the workspace.  cfg->segments_in_host_memory must be 1 (and h_segments
+ * NULL when it is 0, which makes this spin_create).  Same results as
+ * spin_create, bit for bit. */
+SPIN_API int spin_create_ex(const spin_config* cfg, void* d_workspace, size_t ws_bytes,
+                            void* d_pool, size_t pool_bytes, void* h_segments,
+                            size_t h_segment_bytes, void* stream, spin_ctx** out);
+
+/* Waits for the latest spin_retrieve, then frees the context (not the
+ * caller's memory). */
 SPIN_API int spin_destroy(spin_ctx* ctx);
 
 /* Index + Offload registration of request `req` ([XT] part 1, Fig. 3; [GP] A).

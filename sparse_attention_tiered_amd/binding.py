@@ -25,7 +25,7 @@ class SpinConfig(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "max_batch", "num_q_heads", "num_kv_heads", "head_dim", "page_tokens", "max_partitions",
         "max_pages", "max_pages_per_partition", "topk", "slots_per_request", "num_segments",
-        "seg_entries", "num_buckets", "attend_pages_per_split")]
+        "seg_entries", "num_buckets", "attend_pages_per_split", "segments_in_host_memory")]
 
 
 class SpinStats(ctypes.Structure):
@@ -38,7 +38,7 @@ class SpinMetadata(ctypes.Structure):
     _fields_ = [("directory_bytes", ctypes.c_uint64), ("segment_pool_bytes", ctypes.c_uint64),
                 ("live_segment_bytes", ctypes.c_uint64), ("reverse_map_bytes", ctypes.c_uint64),
                 ("flat_table_bytes", ctypes.c_uint64), ("live_segments", c_int32),
-                ("num_segments", c_int32)]
+                ("num_segments", c_int32), ("host_segment_bytes", ctypes.c_uint64)]
 
 
 _P = c_void_p
@@ -49,7 +49,10 @@ SIGNATURES = {
     "spin_config_check": (c_int, [POINTER(SpinConfig)]),
     "spin_workspace_size": (c_int, [POINTER(SpinConfig), POINTER(c_size_t), POINTER(c_size_t)]),
     "spin_derived": (c_int, [POINTER(SpinConfig), _I32P, _I32P, _I32P]),
+    "spin_host_segment_bytes": (c_int, [POINTER(SpinConfig), POINTER(c_size_t)]),
     "spin_create": (c_int, [POINTER(SpinConfig), _P, c_size_t, _P, c_size_t, _P, POINTER(_P)]),
+    "spin_create_ex": (c_int, [POINTER(SpinConfig), _P, c_size_t, _P, c_size_t, _P, c_size_t, _P,
+                               POINTER(_P)]),
     "spin_destroy": (c_int, [_P]),
     "spin_index": (c_int, [_P, c_int32, _P, c_int64, _I32P, c_int32, _P]),
     "spin_release": (c_int, [_P, c_int32, _P]),
@@ -100,7 +103,8 @@ class SpinError(RuntimeError):
 
 
 def make_config(B, Hq, Hkv, max_partitions, max_pages, topk, slots_per_request,
-                num_segments=None, max_pages_per_partition=1, attend_pages_per_split=0):
+                num_segments=None, max_pages_per_partition=1, attend_pages_per_split=0,
+                host_segments=False):
     lib = load()
     c = SpinConfig()
     lib.spin_config_init(ctypes.byref(c))
@@ -110,6 +114,7 @@ def make_config(B, Hq, Hkv, max_partitions, max_pages, topk, slots_per_request,
     ndir = (max_pages + 63) // 64
     c.num_segments = num_segments if num_segments is not None else min(B * slots_per_request, B * Hkv * ndir)
     c.attend_pages_per_split = attend_pages_per_split
+    c.segments_in_host_memory = 1 if host_segments else 0
     return c
 
 
@@ -150,9 +155,21 @@ class Spin:
         self.block_count = torch.zeros((B, Hkv), **i32)
         self.out = torch.zeros((B, Hq, 128), dtype=torch.float32, device=self.device)
         h = c_void_p()
-        self._chk("spin_create", self.lib.spin_create(
-            ctypes.byref(cfg), c_void_p(self.ws.data_ptr()), self.ws_bytes,
-            c_void_p(self.pool.data_ptr()), self.pool_bytes, _stream(stream), ctypes.byref(h)))
+        hs = c_size_t()
+        self._chk("spin_host_segment_bytes",
+                  self.lib.spin_host_segment_bytes(ctypes.byref(cfg), ctypes.byref(hs)))
+        self.host_segments = None
+        if hs.value:
+            # second-level segment tables in pinned host memory
+            self.host_segments = torch.empty(hs.value // 4, dtype=torch.int32, pin_memory=True)
+            self._chk("spin_create_ex", self.lib.spin_create_ex(
+                ctypes.byref(cfg), c_void_p(self.ws.data_ptr()), self.ws_bytes,
+                c_void_p(self.pool.data_ptr()), self.pool_bytes,
+                c_void_p(self.host_segments.data_ptr()), hs.value, _stream(stream), ctypes.byref(h)))
+        else:
+            self._chk("spin_create", self.lib.spin_create(
+                ctypes.byref(cfg), c_void_p(self.ws.data_ptr()), self.ws_bytes,
+                c_void_p(self.pool.data_ptr()), self.pool_bytes, _stream(stream), ctypes.byref(h)))
         self.ctx = h
         self._host = {}
 

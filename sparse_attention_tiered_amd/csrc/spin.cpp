@@ -36,6 +36,7 @@ struct spin_ctx {
   int hip_err = 0;
   int last_t = -1;
   size_t ws_bytes = 0;
+  int32_t* h_segments = nullptr;  // host address of the segment tables, if in host memory
 };
 
 namespace {
@@ -75,6 +76,7 @@ int check(const spin_config* c) {
   if (c->topk < 1 || c->topk > 1024 || c->num_kv_heads * c->topk > spin::kMaxItems) return SPIN_EINVAL;
   if (c->num_segments < 1 || c->num_segments > (1 << 28)) return SPIN_EINVAL;
   if (c->attend_pages_per_split < 0 || c->attend_pages_per_split > 256) return SPIN_EINVAL;
+  if (c->segments_in_host_memory != 0 && c->segments_in_host_memory != 1) return SPIN_EINVAL;
   if (c->slots_per_request < 1 || c->slots_per_request > spin::kMaxSlots) return SPIN_EINVAL;
   if ((long long)c->max_batch * c->slots_per_request > (1LL << 31) / 2) return SPIN_EINVAL;
   // every page one step can need must fit in the request's slots
@@ -129,7 +131,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.tail_sum = take(B * Hkv * spin::kHeadDim * sizeof(double));
   L.host_base = take(B * sizeof(unsigned long long));
   L.directory = take(B * Hkv * d.ndir * sizeof(int));
-  L.segments = take(S * spin::kSegEntries * sizeof(int));
+  L.segments = take(c->segments_in_host_memory ? 0 : S * spin::kSegEntries * sizeof(int));
   L.seg_live = take(S * sizeof(int));
   L.seg_stack = take(S * sizeof(int));
   L.seg_ctl = take(4 * sizeof(int));
@@ -193,6 +195,16 @@ SPIN_API int spin_workspace_size(const spin_config* cfg, size_t* ws_bytes, size_
   return SPIN_OK;
 }
 
+SPIN_API int spin_host_segment_bytes(const spin_config* cfg, size_t* bytes) {
+  const int rc = check(cfg);
+  if (rc) return rc;
+  if (bytes)
+    *bytes = cfg->segments_in_host_memory
+                 ? (size_t)cfg->num_segments * spin::kSegEntries * sizeof(int32_t)
+                 : 0;
+  return SPIN_OK;
+}
+
 SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_blocks,
                           int32_t* attend_splits) {
   const int rc = check(cfg);
@@ -206,10 +218,27 @@ SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_bl
 
 SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, void* d_pool,
                          size_t pool_bytes, void* stream, spin_ctx** out) {
+  return spin_create_ex(cfg, d_ws, ws_bytes, d_pool, pool_bytes, nullptr, 0, stream, out);
+}
+
+SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes, void* d_pool,
+                            size_t pool_bytes, void* h_seg, size_t h_seg_bytes, void* stream,
+                            spin_ctx** out) {
   if (!out) return SPIN_EINVAL;
   *out = nullptr;
   int rc = check(cfg);
   if (rc) return rc;
+  // the segment tables: in the workspace, or in the caller's pinned host memory
+  int32_t* seg_dev = nullptr;
+  if (cfg->segments_in_host_memory) {
+    const size_t need_seg = (size_t)cfg->num_segments * spin::kSegEntries * sizeof(int32_t);
+    if (!h_seg || h_seg_bytes < need_seg) return SPIN_EINVAL;
+    void* p = nullptr;
+    if (hipHostGetDevicePointer(&p, h_seg, 0) != hipSuccess || !aligned(p, 16)) return SPIN_EINVAL;
+    seg_dev = static_cast<int32_t*>(p);
+  } else if (h_seg) {
+    return SPIN_EINVAL;
+  }
   const Derived d = derive(cfg);
   const Layout L = layout(cfg, d);
   const size_t need_pool = (size_t)cfg->max_batch * cfg->slots_per_request * spin::kPageBytes;
@@ -246,7 +275,8 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
   v.tail_sum = reinterpret_cast<double*>(w + L.tail_sum);
   v.host_base = reinterpret_cast<unsigned long long*>(w + L.host_base);
   v.directory = reinterpret_cast<int*>(w + L.directory);
-  v.segments = reinterpret_cast<int*>(w + L.segments);
+  v.segments = seg_dev ? seg_dev : reinterpret_cast<int*>(w + L.segments);
+  ctx->h_segments = seg_dev ? static_cast<int32_t*>(h_seg) : nullptr;
   v.seg_live = reinterpret_cast<int*>(w + L.seg_live);
   v.seg_stack = reinterpret_cast<int*>(w + L.seg_stack);
   v.seg_ctl = reinterpret_cast<int*>(w + L.seg_ctl);
@@ -282,6 +312,7 @@ SPIN_API int spin_create(const spin_config* cfg, void* d_ws, size_t ws_bytes, vo
 
 SPIN_API int spin_destroy(spin_ctx* ctx) {
   if (!ctx) return SPIN_EINVAL;
+  if (ctx->fetched_gen) (void)hipEventSynchronize(ctx->ev_fetched);
   if (ctx->ev_resolved) (void)hipEventDestroy(ctx->ev_resolved);
   if (ctx->ev_fetched) (void)hipEventDestroy(ctx->ev_fetched);
   delete ctx;
@@ -569,7 +600,11 @@ SPIN_API int spin_snapshot(spin_ctx* ctx, int32_t* directory, int32_t* segments,
     return dst ? hipMemcpy(dst, src, n, hipMemcpyDeviceToHost) : hipSuccess;
   };
   HIPCHK(ctx, cp(directory, v.directory, (size_t)v.B * v.Hkv * v.ndir * sizeof(int)));
-  HIPCHK(ctx, cp(segments, v.segments, (size_t)v.n_seg * spin::kSegEntries * sizeof(int)));
+  const size_t seg_n = (size_t)v.n_seg * spin::kSegEntries * sizeof(int);
+  if (ctx->h_segments && segments)
+    std::memcpy(segments, ctx->h_segments, seg_n);
+  else
+    HIPCHK(ctx, cp(segments, v.segments, seg_n));
   HIPCHK(ctx, cp(seg_live, v.seg_live, (size_t)v.n_seg * sizeof(int)));
   HIPCHK(ctx, cp(seg_stack, v.seg_stack, (size_t)v.n_seg * sizeof(int)));
   HIPCHK(ctx, cp(seg_top, v.seg_ctl, sizeof(int)));
@@ -588,7 +623,12 @@ SPIN_API int spin_metadata_footprint(spin_ctx* ctx, spin_metadata* out) {
   const uint64_t seg_bytes = spin::kSegEntries * 4 + 4 + 4;
   std::memset(out, 0, sizeof(*out));
   out->directory_bytes = (uint64_t)v.B * v.Hkv * v.ndir * 4;
-  out->segment_pool_bytes = (uint64_t)v.n_seg * seg_bytes;
+  if (ctx->h_segments) {
+    out->host_segment_bytes = (uint64_t)v.n_seg * spin::kSegEntries * 4;
+    out->segment_pool_bytes = (uint64_t)v.n_seg * 8;
+  } else {
+    out->segment_pool_bytes = (uint64_t)v.n_seg * seg_bytes;
+  }
   out->live_segments = v.n_seg - top;
   out->num_segments = v.n_seg;
   out->live_segment_bytes = (uint64_t)out->live_segments * seg_bytes;

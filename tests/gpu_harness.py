@@ -33,7 +33,8 @@ class Pair:
     """The GPU context and the oracle, indexed with the same host KV."""
 
     def __init__(self, w: W.Workload, n_steps=None, attend_pps=0, num_segments=None,
-                 slots=None, oracle=True, threads=None, offload_extra_pages=None):
+                 slots=None, oracle=True, threads=None, offload_extra_pages=None,
+                 host_segments=False):
         t0 = time.time()
         self.w = w
         self.geo = geo = W.geometry(w)
@@ -44,7 +45,7 @@ class Pair:
         max_parts, max_pages = geo.max_parts + extra, geo.max_pages + extra
         self.cfg = bd.make_config(w.B, w.Hq, w.Hkv, max_parts, max_pages, w.k, C,
                                   num_segments=num_segments, max_pages_per_partition=geo.max_ppp,
-                                  attend_pages_per_split=attend_pps)
+                                  attend_pages_per_split=attend_pps, host_segments=host_segments)
         self.spin = bd.Spin(self.cfg)
         self.oracle = None
         if oracle:

@@ -47,11 +47,32 @@ def test_config_checks(spin_lib):
     ("head_dim", 64), ("page_tokens", 32), ("num_q_heads", 14), ("num_kv_heads", 0),
     ("max_partitions", 0), ("max_partitions", 20000), ("topk", 0), ("max_pages_per_partition", 5),
     ("num_segments", 0), ("seg_entries", 32), ("num_buckets", 32), ("max_batch", 0),
+    ("segments_in_host_memory", 2),
 ])
 def test_config_rejects(spin_lib, field, value):
     c = bd.make_config(B=2, Hq=16, Hkv=4, max_partitions=128, max_pages=128, topk=8, slots_per_request=4 * 8 * 6)
     setattr(c, field, value)
     assert spin_lib.spin_config_check(ctypes.byref(c)) != bd.SPIN_OK
+
+
+def test_host_segment_sizes(spin_lib):
+    """Segment tables in host memory: their host bytes, and a workspace
+    smaller by exactly those bytes (rounded to the 256-byte region alignment)."""
+    kw = dict(B=4, Hq=32, Hkv=8, max_partitions=2048, max_pages=2048, topk=64,
+              slots_per_request=8 * 6 * 64)
+    dev, host = bd.make_config(**kw), bd.make_config(**kw, host_segments=True)
+    hb = ctypes.c_size_t()
+    assert spin_lib.spin_host_segment_bytes(ctypes.byref(dev), ctypes.byref(hb)) == 0 and hb.value == 0
+    assert spin_lib.spin_host_segment_bytes(ctypes.byref(host), ctypes.byref(hb)) == 0
+    assert hb.value == host.num_segments * 64 * 4
+    ws_d, ws_h, pool = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    spin_lib.spin_workspace_size(ctypes.byref(dev), ctypes.byref(ws_d), ctypes.byref(pool))
+    spin_lib.spin_workspace_size(ctypes.byref(host), ctypes.byref(ws_h), ctypes.byref(pool))
+    assert ws_d.value - ws_h.value == (hb.value + 255) // 256 * 256
+    # spin_create_ex rejects a missing host buffer before touching any device
+    out = ctypes.c_void_p()
+    assert spin_lib.spin_create_ex(ctypes.byref(host), None, 0, None, 0, None, 0, None,
+                                   ctypes.byref(out)) == bd.SPIN_EINVAL
 
 
 def test_null_arguments_are_rejected(spin_lib):

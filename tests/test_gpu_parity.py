@@ -208,6 +208,33 @@ def test_offload_and_append(spin_lib, name):
     p.close()
 
 
+@pytest.mark.parametrize("name", ["c4_pressure", "churn", "c5_variable"])
+def test_host_segment_tables(spin_lib, name):
+    """Second-level segment tables in pinned host memory (the kernels reach
+    them through the device-mapped address): the same residency state bit for
+    bit, the same outputs, every step."""
+    w, kw = SMALL[name]
+    p = _pair(w, host_segments=True, **kw)
+    st, _ = p.run()
+    assert st.evictions > 0
+    md = p.spin.metadata()
+    assert md["host_segment_bytes"] == p.cfg.num_segments * 64 * 4
+    assert md["segment_pool_bytes"] == p.cfg.num_segments * 8
+    p.close()
+
+
+def test_host_segment_tables_with_append(spin_lib):
+    """Offload, then a token appended per step, with the segment tables in
+    host memory (the append kernel reads them to find a resident tail page)."""
+    w = W.variant(W.C4, B=3, ctx=(5000, 3000, 64 * 20), k=8, steps=20, ar_coef=0.5)
+    p = _pair(w, slots=8 * 8 + 24, offload_extra_pages=3, host_segments=True)
+    st, _ = p.run(append=True)
+    p.check_host()
+    p.check_summaries()
+    assert st.misses > 0
+    p.close()
+
+
 def test_append_capacity_is_checked(spin_lib):
     import torch
     from sparse_attention_tiered_amd import binding as bd
