@@ -113,8 +113,11 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 constexpr int kTopkBins = 2048;
 constexpr int kTopkCand = 256;  // largest boundary bucket ranked pairwise
 
+// Clamped in float before the conversion, so any input (an infinite or NaN
+// score from corrupt keys) still lands in a valid bucket.
 __device__ __forceinline__ int topk_bucket(float v, float mn, float scale) {
-  return min(kTopkBins - 1, (int)((v - mn) * scale));
+  const float f = fminf(fmaxf((v - mn) * scale, 0.f), (float)(kTopkBins - 1));
+  return (int)f;
 }
 
 template <int NT>
