@@ -120,134 +120,124 @@ __device__ __forceinline__ int topk_bucket(float v, float mn, float scale) {
   return (int)f;
 }
 
+// LDS of one top-k workgroup.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ scores,
-                                             int* __restrict__ sel) {
+struct TopkLds {
+  float vals[kMaxPartitions];  // the scores; reused for radix keys
+  int hist[kTopkBins];
+  int cand[kTopkCand];
+  float candv[kTopkCand];
+  uint32_t chosen[kMaxPartitions / 32];
+  int tmp[NT / 64 + 1];
+  float rmin[NT / 64], rmax[NT / 64];
+  int sh[4];  // boundary bucket, count above it, fill counter / radix state
+};
+
+// The selection itself, once the n > k scores of the list sit in L.vals and
+// each thread holds the min / max of the scores it wrote: writes the k chosen
+// ids, ascending, to out.  Every thread of the workgroup calls it.
+template <int NT>
+__device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, int* out) {
   static_assert(NT * 2 >= kTopkBins && NT >= kTopkCand, "one thread per bucket pair");
-  __shared__ float vals[kMaxPartitions];
-  __shared__ int hist[kTopkBins];
-  __shared__ int cand[kTopkCand];
-  __shared__ float candv[kTopkCand];
-  __shared__ uint32_t chosen[kMaxPartitions / 32];
-  __shared__ int tmp[NT / 64 + 1];
-  __shared__ float rmin[NT / 64], rmax[NT / 64];
-  __shared__ int sh[4];  // boundary bucket, count above it, fill counter / radix state
-  const int bh = blockIdx.x;
-  const int b = bh / d.Hkv;
-  const int n = d.req_parts[b];
-  const int k = d.k;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int* out = sel + (size_t)bh * k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
-    return;
-  }
-  const float* srow = scores + (size_t)bh * d.Nmax;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < n; i += NT) {
-    const float v = srow[i];
-    vals[i] = v;
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
-  }
-  for (int i = tid; i < kTopkBins; i += NT) hist[i] = 0;
-  for (int i = tid; i < (n + 31) / 32; i += NT) chosen[i] = 0;
+  for (int i = tid; i < kTopkBins; i += NT) L.hist[i] = 0;
+  for (int i = tid; i < (n + 31) / 32; i += NT) L.chosen[i] = 0;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     mn = fminf(mn, __shfl_xor(mn, o, 64));
     mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   }
   if (lane == 0) {
-    rmin[wv] = mn;
-    rmax[wv] = mx;
+    L.rmin[wv] = mn;
+    L.rmax[wv] = mx;
   }
-  if (tid == 0) sh[2] = 0;
+  if (tid == 0) L.sh[2] = 0;
   __syncthreads();
-  mn = rmin[0];
-  mx = rmax[0];
+  mn = L.rmin[0];
+  mx = L.rmax[0];
   for (int w = 1; w < NT / 64; ++w) {
-    mn = fminf(mn, rmin[w]);
-    mx = fmaxf(mx, rmax[w]);
+    mn = fminf(mn, L.rmin[w]);
+    mx = fmaxf(mx, L.rmax[w]);
   }
   // a range too narrow for a finite scale puts everything in bucket 0
   float scale = (float)kTopkBins / (mx - mn);
   if (!(scale < 3.0e38f)) scale = 0.f;
-  for (int i = tid; i < n; i += NT) atomicAdd(&hist[topk_bucket(vals[i], mn, scale)], 1);
+  for (int i = tid; i < n; i += NT) atomicAdd(&L.hist[topk_bucket(L.vals[i], mn, scale)], 1);
   __syncthreads();
   // counts from the top: thread t holds buckets 2047-2t and 2046-2t
   {
     const int hi = kTopkBins - 1 - 2 * tid, lo = hi - 1;
-    const int a = tid < kTopkBins / 2 ? hist[hi] : 0;
-    const int c = tid < kTopkBins / 2 ? hist[lo] : 0;
+    const int a = tid < kTopkBins / 2 ? L.hist[hi] : 0;
+    const int c = tid < kTopkBins / 2 ? L.hist[lo] : 0;
     int tot;
-    const int before = block_excl_scan<NT>(a + c, tmp, &tot);
+    const int before = block_excl_scan<NT>(a + c, L.tmp, &tot);
     if (tid < kTopkBins / 2 && before < k && before + a + c >= k) {
       const bool in_hi = before + a >= k;
-      sh[0] = in_hi ? hi : lo;
-      sh[1] = in_hi ? before : before + a;
+      L.sh[0] = in_hi ? hi : lo;
+      L.sh[1] = in_hi ? before : before + a;
     }
   }
   __syncthreads();
-  const int cut = sh[0];
-  const int need = k - sh[1];  // >= 1: taken from the boundary bucket
-  const int m = hist[cut];     // its members
+  const int cut = L.sh[0];
+  const int need = k - L.sh[1];  // >= 1: taken from the boundary bucket
+  const int m = L.hist[cut];     // its members
   if (m <= kTopkCand) {
     for (int i = tid; i < n; i += NT) {
-      const float v = vals[i];
+      const float v = L.vals[i];
       const int bk = topk_bucket(v, mn, scale);
-      if (bk > cut) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+      if (bk > cut) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
       if (bk == cut) {
-        const int slot = atomicAdd(&sh[2], 1);
+        const int slot = atomicAdd(&L.sh[2], 1);
         if (slot < kTopkCand) {
-          cand[slot] = i;
-          candv[slot] = v;
+          L.cand[slot] = i;
+          L.candv[slot] = v;
         }
       }
     }
     __syncthreads();
     if (tid < m) {
-      const int me = cand[tid];
-      const float v = candv[tid];
+      const int me = L.cand[tid];
+      const float v = L.candv[tid];
       int rank = 0;
       for (int j = 0; j < m; ++j) {
-        const int o = cand[j];
-        const float w = candv[j];
+        const int o = L.cand[j];
+        const float w = L.candv[j];
         rank += (w > v || (w == v && o < me)) ? 1 : 0;
       }
-      if (rank < need) atomicOr(&chosen[me >> 5], 1u << (me & 31));
+      if (rank < need) atomicOr(&L.chosen[me >> 5], 1u << (me & 31));
     }
   } else {
     // radix select among the boundary bucket's members; key 0 marks the rest
     // (no finite score maps to 0)
-    uint32_t* keys = reinterpret_cast<uint32_t*>(vals);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(L.vals);
     for (int i = tid; i < n; i += NT) {
-      const float v = vals[i];
+      const float v = L.vals[i];
       const int bk = topk_bucket(v, mn, scale);
-      if (bk > cut) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+      if (bk > cut) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
       keys[i] = bk == cut ? float_key(v + 0.f) : 0u;  // -0 ranks as +0
     }
     uint32_t prefix = 0, mask = 0;
     int kk = need;
     for (int shift = 24; shift >= 0; shift -= 8) {
       __syncthreads();
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
+      for (int i = tid; i < 256; i += NT) L.hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += NT) {
         const uint32_t key = keys[i];
-        if (key != 0u && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        if (key != 0u && (key & mask) == prefix) atomicAdd(&L.hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
       if (tid < 64) {
         int c4[4], cs = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          c4[j] = hist[255 - 4 * tid - j];
+          c4[j] = L.hist[255 - 4 * tid - j];
           cs += c4[j];
         }
         const int inc = wave_incl_scan(cs);
         const unsigned long long hitm = __ballot(inc >= kk);
-        const int L = __ffsll((long long)hitm) - 1;
-        if (tid == L) {
+        const int lead = __ffsll((long long)hitm) - 1;
+        if (tid == lead) {
           int ab = inc - cs, dg = 255 - 4 * tid;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -257,14 +247,14 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
             }
             ab += c4[j];
           }
-          sh[3] = dg;
-          sh[2] = kk - ab;
+          L.sh[3] = dg;
+          L.sh[2] = kk - ab;
         }
       }
       __syncthreads();
-      prefix |= (uint32_t)sh[3] << shift;
+      prefix |= (uint32_t)L.sh[3] << shift;
       mask |= 0xFFu << shift;
-      kk = sh[2];
+      kk = L.sh[2];
     }
     // members above the k-th key, then the kk lowest ids equal to it
     const int E = (n + NT - 1) / NT;
@@ -272,11 +262,11 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
     int n_eq = 0;
     for (int i = lo; i < hi; ++i) n_eq += keys[i] == prefix;
     int tot;
-    int er = block_excl_scan<NT>(n_eq, tmp, &tot);
+    int er = block_excl_scan<NT>(n_eq, L.tmp, &tot);
     for (int i = lo; i < hi; ++i) {
       const uint32_t key = keys[i];
       const bool take = key > prefix || (key == prefix && er++ < kk);
-      if (take) atomicOr(&chosen[i >> 5], 1u << (i & 31));
+      if (take) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
     }
   }
   __syncthreads();
@@ -284,16 +274,138 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
   const int E = (n + NT - 1) / NT;
   const int lo = tid * E, hi = min(n, lo + E);
   int n_take = 0;
-  for (int i = lo; i < hi; ++i) n_take += (chosen[i >> 5] >> (i & 31)) & 1u;
+  for (int i = lo; i < hi; ++i) n_take += (L.chosen[i >> 5] >> (i & 31)) & 1u;
   int tot;
-  int pos = block_excl_scan<NT>(n_take, tmp, &tot);
+  int pos = block_excl_scan<NT>(n_take, L.tmp, &tot);
   for (int i = lo; i < hi; ++i)
-    if (((chosen[i >> 5] >> (i & 31)) & 1u) && pos < k) out[pos++] = i;
+    if (((L.chosen[i >> 5] >> (i & 31)) & 1u) && pos < k) out[pos++] = i;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ scores,
+                                             int* __restrict__ sel) {
+  __shared__ TopkLds<NT> L;
+  const int bh = blockIdx.x;
+  const int n = d.req_parts[bh / d.Hkv];
+  const int k = d.k;
+  const int tid = threadIdx.x;
+  int* out = sel + (size_t)bh * k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* srow = scores + (size_t)bh * d.Nmax;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < n; i += NT) {
+    const float v = srow[i];
+    L.vals[i] = v;
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+  topk_select<NT>(L, n, k, mn, mx, out);
+}
+
+// Scoring and top-k of one (request, KV head) in one 1024-thread workgroup,
+// for batches with enough heads to occupy the chip: the scores go straight
+// into the top-k's LDS (and to `scores`), with no second launch and no
+// re-read.  Each row's dot product is computed exactly as in k_score (same
+// lanes, same order of operations), so both paths give the same scores.
+constexpr int kFusedRows = 4;  // rows in flight per 8-lane group
+
+__global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __restrict__ q,
+                                                       float* __restrict__ scores,
+                                                       int* __restrict__ sel) {
+  __shared__ TopkLds<1024> L;
+  __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];
+  __shared__ float sqbar[kHeadDim];
+  const int bh = blockIdx.x;
+  const int b = bh / d.Hkv, h = bh - b * d.Hkv;
+  const int n = d.req_parts[b];
+  const int k = d.k;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 3, r = lane & 7;
+  float* srow = scores + (size_t)bh * d.Nmax;
+  int* out = sel + (size_t)bh * k;
+  for (int p = n + tid; p < d.Nmax; p += 1024) srow[p] = -INFINITY;
+
+  const int nq = d.G * kHeadDim / 8;
+  if (tid < nq) sq[tid] = reinterpret_cast<const uint4*>(q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim)[tid];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    const uint16_t* sq16 = reinterpret_cast<const uint16_t*>(sq);
+    float sum = 0.f;
+    for (int g = 0; g < d.G; ++g) sum += __uint_as_float((uint32_t)sq16[g * kHeadDim + tid] << 16);
+    sqbar[tid] = sum * (1.0f / ((float)d.G * sqrtf((float)kHeadDim)));
+  }
+  __syncthreads();
+  float qv[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[4 * j + e] = sqbar[32 * j + 4 * r + e];
+
+  // wave `wave` of a pass covers rows base + 32 wave + 4 grp + it, it < 4
+  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
+  float mn = INFINITY, mx = -INFINITY;
+  constexpr int kRowsPerPass = 16 * 8 * kFusedRows;
+  for (int base = 0; base < n; base += kRowsPerPass) {
+    const int p0 = base + wave * 8 * kFusedRows + kFusedRows * grp;
+    float4 v[kFusedRows][4];
+#pragma unroll
+    for (int it = 0; it < kFusedRows; ++it) {
+      const int p = p0 + it;
+      const float* row = S + (size_t)(p < n ? p : 0) * kHeadDim + 4 * r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[it][j] = *reinterpret_cast<const float4*>(row + 32 * j);
+    }
+    float acc[kFusedRows];
+#pragma unroll
+    for (int it = 0; it < kFusedRows; ++it) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a = fmaf(v[it][j].x, qv[4 * j + 0], a);
+        a = fmaf(v[it][j].y, qv[4 * j + 1], a);
+        a = fmaf(v[it][j].z, qv[4 * j + 2], a);
+        a = fmaf(v[it][j].w, qv[4 * j + 3], a);
+      }
+      a += __shfl_xor(a, 1, 64);
+      a += __shfl_xor(a, 2, 64);
+      a += __shfl_xor(a, 4, 64);
+      acc[it] = a;
+    }
+    // lane r < 4 of the group writes row p0 + r
+    if (r < kFusedRows) {
+      float mine = acc[0];
+#pragma unroll
+      for (int it = 1; it < kFusedRows; ++it) mine = (r == it) ? acc[it] : mine;
+      const int p = p0 + r;
+      if (p < n) {
+        L.vals[p] = mine;
+        srow[p] = mine;
+        mn = fminf(mn, mine);
+        mx = fmaxf(mx, mine);
+      }
+    }
+  }
+  if (n <= k) {
+    for (int i = tid; i < k; i += 1024) out[i] = i < n ? i : -1;
+    return;
+  }
+  __syncthreads();
+  topk_select<1024>(L, n, k, mn, mx, out);
 }
 
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s) {
   dim3 grid((d.Nmax + kScorePerWG - 1) / kScorePerWG, d.B * d.Hkv);
   hipLaunchKernelGGL(k_score, grid, dim3(kScoreWG), 0, s, d, q, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, int* sel,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_select_fused, dim3(d.B * d.Hkv), dim3(1024), 0, s, d, q, scores, sel);
   return hipGetLastError();
 }
 

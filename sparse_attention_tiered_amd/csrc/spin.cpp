@@ -483,8 +483,13 @@ SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* 
                          void* stream) {
   if (!ctx || !d_q || !d_sel || !aligned(d_q, 16)) return SPIN_EINVAL;
   float* sc = d_scores ? d_scores : ctx->dev.scores;
-  HIPCHK(ctx, spin::launch_score(ctx->dev, static_cast<const uint16_t*>(d_q), sc, S(stream)));
-  HIPCHK(ctx, spin::launch_topk(ctx->dev, sc, d_sel, S(stream)));
+  const uint16_t* q = static_cast<const uint16_t*>(d_q);
+  if (ctx->dev.B * ctx->dev.Hkv >= spin::kFusedSelectMinLists) {
+    HIPCHK(ctx, spin::launch_select_fused(ctx->dev, q, sc, d_sel, S(stream)));
+  } else {
+    HIPCHK(ctx, spin::launch_score(ctx->dev, q, sc, S(stream)));
+    HIPCHK(ctx, spin::launch_topk(ctx->dev, sc, d_sel, S(stream)));
+  }
   return SPIN_OK;
 }
 

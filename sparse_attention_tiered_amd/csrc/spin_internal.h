@@ -74,6 +74,11 @@ hipError_t launch_index(const Dev& d, int req, int n_parts, const void* src, int
 hipError_t launch_append(const Dev& d, const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s);
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);
+hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, int* sel,
+                               hipStream_t s);
+// batches of at least this many (request, KV head) lists score and select in
+// one kernel, one workgroup per list (enough workgroups to stream HBM)
+constexpr int kFusedSelectMinLists = 128;
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s);
 hipError_t launch_segments(const Dev& d, hipStream_t s);

@@ -42,6 +42,9 @@ SMALL = {
                         dict(slots=2 * 8 + 12)),
     "fewer_parts_than_k": (W.variant(W.C2, B=3, Hq=8, Hkv=2, ctx=(300, 0, 64 * 40), k=8, steps=6),
                            dict(slots=2 * 8 * 2)),
+    # 128 (request, KV head) lists: scoring and top-k in one kernel
+    "fused_select": (W.variant(W.C4, B=16, ctx=tuple(2000 + 300 * b for b in range(16)), k=8, steps=10,
+                               ar_coef=0.3), dict(slots=8 * 8 + 16)),
 }
 
 
@@ -283,6 +286,9 @@ TIES = {
     # every score of a head equal (a zero-width score range)
     "ties_flat": W.variant(W.C2, name="ties_flat", B=1, Hq=8, Hkv=2, ctx=(20000,),
                            k=16, steps=3, kv_kind="ties", hot_count=0),
+    # 128 lists (the fused score + top-k kernel), ties inside the hot group
+    "ties_fused": W.variant(W.C2, name="ties_fused", B=32, Hq=16, Hkv=4, ctx=(4096,) * 32,
+                            k=8, steps=3, kv_kind="ties", hot_count=20),
 }
 
 
