@@ -341,6 +341,9 @@ def test_streams_change_between_steps(spin_lib):
         assert np.max(np.abs(out - out_o)) <= 2e-3, t
         assert np.array_equal(out.view(np.uint32), b.spin.out.cpu().numpy().view(np.uint32)), t
         a.check_state(t)
+        sa, sb = a.spin.snapshot(), b.spin.snapshot()
+        for key in sa:
+            assert np.array_equal(sa[key], sb[key]), (t, key)
     st, _ = a.spin.stats()
     assert st.error_word == 0 and st.evictions > 0
     a.close()
