@@ -132,6 +132,8 @@ def main():
     ap.add_argument("--budget-ratio", type=float, default=None,
                     help="buffer elasticity ablation: each request's budget = mandatory pages "
                          "x (1 + ratio), capped by its slots (0 = no buffer pages)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one captured HIP graph (spin_step_at)")
     ap.add_argument("--host-segments", action="store_true",
                     help="keep the second-level segment tables in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -151,6 +153,8 @@ def main():
 
     if args.warmup < 1:
         ap.error("--warmup must be at least 1 (step 0 is timed on its own)")
+    if args.graph and args.no_overlap:
+        ap.error("--graph replays the whole-step call; --no-overlap needs the stage calls")
     w = W.get(args.config)
     n_steps = max(w.steps, args.warmup + 2 * args.steps)
     t0 = time.time()
@@ -175,8 +179,9 @@ def main():
         for b in range(w.B):
             spin.set_budget(b, budget)
     q = torch.from_numpy(draws.q_bits.view(np.int16)).to("cuda")
-    S = torch.cuda.current_stream()
+    S = torch.cuda.Stream()  # a created stream: HIP graphs cannot capture the null stream
     Cs = S if args.single_stream else torch.cuda.Stream()
+    torch.cuda.synchronize()
 
     overlap = not args.single_stream and not args.no_overlap
 
@@ -227,13 +232,24 @@ def main():
     K = args.steps
     # timed pass: the steps alone (a timing event costs the GPU several
     # microseconds, so the per-stage events go in a second pass)
+    graph = None
+    if args.graph:
+        # one step captured with the device-side step index, replayed K times
+        t_dev = torch.full((1,), args.warmup, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=S):
+            spin.step_at(q, t_dev, stream=S, copy_stream=Cs)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(S)
     for i in range(K):
-        if overlap or args.single_stream:
+        if graph is not None:
+            with torch.cuda.stream(S):
+                graph.replay()
+        elif overlap or args.single_stream:
             # the library's whole-step call (one entry into the library)
             spin.step(q[args.warmup + i], args.warmup + i, stream=S, copy_stream=Cs)
         else:
@@ -300,6 +316,7 @@ def main():
     # nothing between, is reported beside it)
     scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()  # (filled on the default stream)
     bd.read_stream(scratch, sink, S)  # written back once; later reads leave it clean
 
     def cold(fn):
@@ -391,6 +408,7 @@ def main():
         "median_step_ms_instrumented": float(np.median(step_ms)),
         "attended_head_tokens_per_s": attended_tokens / (iso_attend_ms * 1e-3),
         "overlap_retrieve_attend": overlap,
+        "timed_as_graph_replays": graph is not None,
         "rooflines": rl,
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,
                       "evictions_per_step": evictions / K},

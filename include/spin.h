@@ -282,6 +282,21 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream);
 
+/* spin_step with the step index on the device, for HIP graph capture: the
+ * kernels read t from *d_t (device int32) and the step's queries at
+ * d_q_steps + t * q_step_elems (bf16 elements; q_step_elems * 2 a multiple
+ * of 16), and a last kernel on `stream` increments *d_t, so one captured call
+ * replays as consecutive steps.  t is the caller's to keep non-decreasing.
+ * Captured (stream capture active on `stream`), the call waits for no
+ * transfer enqueued before the capture: the context must be idle when the
+ * capture begins (synchronise the streams it used).  The captured graph holds
+ * kernel launches and event record / wait dependencies only (no memset or
+ * copy nodes). */
+SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_elems,
+                          int32_t* d_t, int32_t* d_sel, int32_t* d_block_table,
+                          int32_t* d_block_ntok, int32_t* d_block_count, float* d_out,
+                          void* stream, void* copy_stream);
+
 /* Totals since create.  per_request may be NULL, else [max_batch][4] int64:
  * hits, misses, evictions, cutoff bucket of the last step (-1 = none).
  * Synchronises the device. */

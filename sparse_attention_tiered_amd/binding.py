@@ -66,6 +66,7 @@ SIGNATURES = {
     "spin_attend_begin": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend_finish": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spin_step": (c_int, [_P, _P, c_int32, _P, _P, _P, _P, _P, _P, _P]),
+    "spin_step_at": (c_int, [_P, _P, c_int64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "spin_get_stats": (c_int, [_P, POINTER(SpinStats), POINTER(c_int64)]),
     "spin_snapshot": (c_int, [_P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P, _I32P]),
     "spin_read_summaries": (c_int, [_P, c_int32, POINTER(ctypes.c_float)]),
@@ -262,6 +263,17 @@ class Spin:
         self._chk("spin_step", self.lib.spin_step(
             self.ctx, _ptr(q), int(t), _ptr(self.sel), _ptr(self.block_table), _ptr(self.block_ntok),
             _ptr(self.block_count), _ptr(self.out), s, cs))
+        return self.out
+
+    def step_at(self, q_steps, t_dev, stream=None, copy_stream=None):
+        """One step at the device-side index t_dev (int32 device tensor of one
+        element, incremented on the device): q_steps[t] are its queries."""
+        s = _stream(stream)
+        cs = _stream(copy_stream) if copy_stream is not None else s
+        step_elems = q_steps[0].numel() if q_steps.dim() > 1 else 0
+        self._chk("spin_step_at", self.lib.spin_step_at(
+            self.ctx, _ptr(q_steps), step_elems, _ptr(t_dev), _ptr(self.sel), _ptr(self.block_table),
+            _ptr(self.block_ntok), _ptr(self.block_count), _ptr(self.out), s, cs))
         return self.out
 
     # ---------------------------------------------------------------- inspection

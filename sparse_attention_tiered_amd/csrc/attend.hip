@@ -63,6 +63,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
                                                    const int* __restrict__ bntok,
                                                    const int* __restrict__ bcount,
                                                    float* __restrict__ out, int mode) {
+  q = step_queries(d, q);
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][132];

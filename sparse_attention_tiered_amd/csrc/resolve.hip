@@ -42,6 +42,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   __shared__ int tmp[17];
   __shared__ int sh_cut, sh_below;
 
+  if (d.step_t) t = *d.step_t;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int C = d.C, Hkv = d.Hkv, k = d.k, MB = d.max_blocks;
   const int n_parts = d.req_parts[b];
@@ -382,6 +383,15 @@ __global__ __launch_bounds__(1024) void k_segments(Dev d) {
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s) {
   hipLaunchKernelGGL(k_resolve, dim3(d.B), dim3(1024), 0, s, d, sel, t, bt, bntok, bcount);
+  return hipGetLastError();
+}
+
+__global__ void k_step_advance(int* t) {
+  if (threadIdx.x == 0) *t += 1;
+}
+
+hipError_t launch_step_advance(int* t, hipStream_t s) {
+  hipLaunchKernelGGL(k_step_advance, dim3(1), dim3(64), 0, s, t);
   return hipGetLastError();
 }
 

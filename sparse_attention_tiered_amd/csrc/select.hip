@@ -21,6 +21,7 @@ constexpr int kScorePerWG = 4 * kScorePerWave;
 
 __global__ __launch_bounds__(kScoreWG) void k_score(Dev d, const uint16_t* __restrict__ q,
                                                     float* __restrict__ scores) {
+  q = step_queries(d, q);
   __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];  // the group's bf16 queries
   __shared__ float sqbar[kHeadDim];               // their sum, times 1 / (G sqrt(128))
   const int bh = blockIdx.y;
@@ -315,6 +316,7 @@ constexpr int kFusedRows = 4;  // rows in flight per 8-lane group
 __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __restrict__ q,
                                                        float* __restrict__ scores,
                                                        int* __restrict__ sel) {
+  q = step_queries(d, q);
   __shared__ TopkLds<1024> L;
   __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];
   __shared__ float sqbar[kHeadDim];

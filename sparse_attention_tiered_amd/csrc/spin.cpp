@@ -298,6 +298,8 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.stats = reinterpret_cast<long long*>(w + L.stats);
   v.err = reinterpret_cast<int*>(w + L.err);
   v.pool = static_cast<uint16_t*>(d_pool);
+  v.step_t = nullptr;
+  v.q_step = 0;
   hipError_t e = hipEventCreateWithFlags(&ctx->ev_resolved, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&ctx->ev_fetched, hipEventDisableTiming);
   if (e == hipSuccess) e = spin::launch_init(v, S(stream));
@@ -497,8 +499,10 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
                                 int32_t* d_block_table, int32_t* d_block_ntok,
                                 int32_t* d_block_count, void* stream) {
   if (!ctx || !d_sel || !d_block_table || !d_block_ntok || !d_block_count || t < 0) return SPIN_EINVAL;
-  if (t < ctx->last_t) return SPIN_EINVAL;
-  ctx->last_t = t;
+  if (!ctx->dev.step_t) {  // a device-side step index is checked by nobody but its owner
+    if (t < ctx->last_t) return SPIN_EINVAL;
+    ctx->last_t = t;
+  }
   // the previous step's transfer reads the insert lists this call rewrites
   HIPCHK(ctx, wait_fetched(ctx, S(stream)));
   HIPCHK(ctx, spin::launch_resolve(ctx->dev, d_sel, t, d_block_table, d_block_ntok, d_block_count,
@@ -569,6 +573,33 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
     if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   }
   return rc;
+}
+
+SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_elems,
+                          int32_t* d_t, int32_t* d_sel, int32_t* d_block_table,
+                          int32_t* d_block_ntok, int32_t* d_block_count, float* d_out,
+                          void* stream, void* copy_stream) {
+  if (!ctx || !d_q_steps || !d_t || q_step_elems < 0 || (q_step_elems * 2) % 16 != 0)
+    return SPIN_EINVAL;
+  if (!aligned(d_t, 4)) return SPIN_EINVAL;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  HIPCHK(ctx, hipStreamIsCapturing(S(stream), &cap));
+  // a capture starts from an idle context: no transfer recorded before it is
+  // waited for inside the graph (stream order between replays covers it), so
+  // `stream` counts as having waited for the latest one
+  if (cap == hipStreamCaptureStatusActive) {
+    ctx->waited_on = S(stream);
+    ctx->waited_gen = ctx->fetched_gen;
+  }
+  ctx->dev.step_t = d_t;
+  ctx->dev.q_step = q_step_elems;
+  int rc = spin_step(ctx, d_q_steps, 0, d_sel, d_block_table, d_block_ntok, d_block_count, d_out,
+                     stream, copy_stream);
+  ctx->dev.step_t = nullptr;
+  ctx->dev.q_step = 0;
+  if (rc) return rc;
+  HIPCHK(ctx, spin::launch_step_advance(d_t, S(stream)));
+  return SPIN_OK;
 }
 
 SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* st, int64_t* per_request) {

@@ -63,9 +63,19 @@ struct Dev {
   long long* stats;            // [B][4] hits, misses, evictions, last cutoff
   int* err;                    // [1] error bits
   uint16_t* pool;              // [B * C][kPageElems]
+  // Device-side step index (spin_step_at): when set, kernels take the step t
+  // from *step_t and the step's queries at q + t * q_step instead of their
+  // host arguments, so one captured step replays for consecutive steps.
+  const int* step_t;
+  long long q_step;            // elements between consecutive steps' queries
 };
 
 // launchers (each returns the hipError_t of its launch)
+// The queries of this step: q itself, or q + t * q_step with a device-side step index.
+__device__ __forceinline__ const uint16_t* step_queries(const Dev& d, const uint16_t* q) {
+  return d.step_t ? q + (long long)(*d.step_t) * d.q_step : q;
+}
+
 hipError_t launch_init(const Dev& d, hipStream_t s);
 hipError_t launch_release(const Dev& d, int req, hipStream_t s);
 hipError_t launch_set_budget(const Dev& d, int req, int slots, hipStream_t s);
@@ -82,6 +92,7 @@ constexpr int kFusedSelectMinLists = 128;
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s);
 hipError_t launch_segments(const Dev& d, hipStream_t s);
+hipError_t launch_step_advance(int* t, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 // mode 0: every block, finished output; 1: resident blocks only, partials;

@@ -348,3 +348,53 @@ def test_streams_change_between_steps(spin_lib):
     assert st.error_word == 0 and st.evictions > 0
     a.close()
     b.close()
+
+
+def test_graph_replayed_steps(spin_lib):
+    """One spin_step_at call (device-side step index) captured in a HIP graph
+    and replayed for consecutive steps, with eager work and synchronisations
+    between the replays, equals the eager whole-step calls bit for bit
+    (outputs, selections, the whole residency state) and the oracle."""
+    import torch
+
+    w = W.variant(W.C1, name="graph", steps=10, ar_coef=0.2)
+    a = _pair(w, slots=2 * 8 + 4)                # eager, checked against the oracle
+    b = _pair(w, slots=2 * 8 + 4, oracle=False)  # the graph
+    Sa, Ca = torch.cuda.Stream(), torch.cuda.Stream()
+    Sb, Cb = torch.cuda.Stream(), torch.cuda.Stream()
+    t_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    def compare(t):
+        sel_o, _, out_o = a.oracle.step(a.draws.q_bits[t], t)
+        out = a.spin.out.cpu().numpy()
+        assert np.array_equal(a.spin.sel.cpu().numpy(), sel_o.astype(np.int32)), t
+        assert np.max(np.abs(out - out_o)) <= 2e-3, t
+        assert np.array_equal(out.view(np.uint32), b.spin.out.cpu().numpy().view(np.uint32)), t
+        assert torch.equal(a.spin.sel, b.spin.sel), t
+        sa, sb = a.spin.snapshot(), b.spin.snapshot()
+        for key in sa:
+            assert np.array_equal(sa[key], sb[key]), (t, key)
+        assert int(t_dev.item()) == t + 1
+
+    # step 0 eagerly through the device-index call, then capture one step
+    a.spin.step(a.q_dev[0], 0, stream=Sa, copy_stream=Ca)
+    b.spin.step_at(b.q_dev, t_dev, stream=Sb, copy_stream=Cb)
+    torch.cuda.synchronize()
+    compare(0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=Sb):
+        b.spin.step_at(b.q_dev, t_dev, stream=Sb, copy_stream=Cb)
+    torch.cuda.synchronize()
+    assert int(t_dev.item()) == 1  # capturing ran nothing
+    for t in range(1, w.steps):
+        with torch.cuda.stream(Sb):
+            g.replay()
+        a.spin.step(a.q_dev[t], t, stream=Sa, copy_stream=Ca)
+        torch.cuda.synchronize()
+        compare(t)
+        b.spin.stats()  # eager library work between replays
+    st, _ = b.spin.stats()
+    assert st.error_word == 0 and st.evictions > 0
+    a.close()
+    b.close()
