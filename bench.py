@@ -186,6 +186,7 @@ def main():
     overlap = not args.single_stream and not args.no_overlap
 
     def step(t, ev=None):
+        # the stages of spin_step, one call each
         # events (instrumented pass only): 0 start, 1 select done, 2 resolve
         # done (S); 3 retrieve start, 4 retrieve done (copy stream); 5
         # resident-page attention done (overlapped with retrieve), 6 attention
@@ -201,7 +202,11 @@ def main():
             if Cs is not S:
                 Cs.wait_stream(S)
             ev[3].record(Cs)
-        spin.retrieve(copy_stream=Cs)
+        if overlap:
+            # as the whole-step call: the transfer attends its pages on arrival
+            spin.retrieve_attend(q[t], copy_stream=Cs)
+        else:
+            spin.retrieve(copy_stream=Cs)
         if ev is not None:
             ev[4].record(Cs)
         if overlap:
@@ -365,7 +370,7 @@ def main():
                      "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if retrieve_bytes else 0.0,
                      "launch_ms": stage_ms["retrieve"],
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
-                     "kernels": ["k_retrieve"]},
+                     "kernels": ["k_retrieve_attend" if overlap else "k_retrieve"]},
     }
     # the transfer over the steps that move at least 8 MB (small transfers are
     # dominated by a fixed latency), and step 0 on its own

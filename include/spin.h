@@ -251,6 +251,15 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
  * `copy_stream` (it waits for that resolve; spin_attend waits for this). */
 SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream);
 
+/* spin_retrieve that also attends each fetched page as it arrives ([XT]
+ * part 1 attention, done where the page already sits in the transfer's
+ * registers): for the G query heads of the page's KV head, d_q as for
+ * spin_attend, it keeps an unnormalised partial per fetched page, so
+ * spin_attend_finish after it only merges (no fetched page is read back from
+ * HBM).  The next spin_attend_finish must be given the same d_q.  spin_attend
+ * after it attends every page as usual. */
+SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_stream);
+
 /* Attention ([XT] part 1, Fig. 3) over the block-table pages:
  * out[b][g] = softmax(q[b][g] . K^T / sqrt(128)) V over the valid tokens of
  * the pages of KV head g / G, bf16 inputs, float32 accumulation.  A head with
@@ -264,7 +273,8 @@ SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_
  * attention over the pages of the last spin_resolve_evict that were already
  * resident, without waiting for spin_retrieve, and keeps per-head partials;
  * spin_attend_finish waits for spin_retrieve, attends the pages it fetched and
- * merges both passes (log-sum-exp) into d_out.  Both must be given the block
+ * merges both passes (log-sum-exp) into d_out (after spin_retrieve_attend it
+ * only merges).  Both must be given the block
  * tables written by the last spin_resolve_evict; the result equals spin_attend
  * up to float32 rounding of the merge. */
 SPIN_API int spin_attend_begin(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
@@ -275,9 +285,10 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
                                 float* d_out, void* stream);
 
 /* One whole decode step: select, resolve_evict, retrieve (on copy_stream),
- * attention.  When copy_stream differs from stream, attention over the
- * resident pages overlaps the retrieve (spin_attend_begin / _finish);
- * otherwise it is spin_attend after the retrieve. */
+ * attention.  When copy_stream differs from stream, the transfer attends its
+ * pages on arrival (spin_retrieve_attend) while attention over the resident
+ * pages runs on `stream` (spin_attend_begin), and spin_attend_finish merges;
+ * otherwise it is spin_retrieve, then spin_attend. */
 SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream);

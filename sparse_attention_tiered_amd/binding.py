@@ -62,6 +62,7 @@ SIGNATURES = {
     "spin_select": (c_int, [_P, _P, _P, _P, _P]),
     "spin_resolve_evict": (c_int, [_P, _P, c_int32, _P, _P, _P, _P]),
     "spin_retrieve": (c_int, [_P, _P]),
+    "spin_retrieve_attend": (c_int, [_P, _P, _P]),
     "spin_attend": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spin_attend_begin": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend_finish": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
@@ -233,6 +234,10 @@ class Spin:
 
     def retrieve(self, copy_stream=None):
         self._chk("spin_retrieve", self.lib.spin_retrieve(self.ctx, _stream(copy_stream)))
+
+    def retrieve_attend(self, q, copy_stream=None):
+        self._chk("spin_retrieve_attend",
+                  self.lib.spin_retrieve_attend(self.ctx, _ptr(q), _stream(copy_stream)))
 
     def attend(self, q, out=None, stream=None, block_table=None, block_ntok=None, block_count=None):
         out = self.out if out is None else out

@@ -26,37 +26,13 @@
 // combines the split partials (log-sum-exp).  (Merging in the last workgroup
 // to finish would need a device-scope fence per workgroup, which writes back
 // the whole L2 on this chip and cost more than the second launch.)
+#include "attend_tile.h"
 #include "device_util.h"
 #include "spin_internal.h"
 
 namespace spin {
 
 constexpr int kAttWG = 256;
-
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Key tile tt, row r holds token 32 (tt/2) + 8 (r/4) + 4 (tt%2) + r%4: with
-// that order the logits come out of the MFMA in the P^T operand layout.
-__device__ __forceinline__ void load_keys(const uint16_t* K, int r, int g, bf16x8 (&ka)[4][4]) {
-#pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tok = 32 * (tt >> 1) + 8 * (r >> 2) + 4 * (tt & 1) + (r & 3);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      ka[tt][kb] = *reinterpret_cast<const bf16x8*>(K + tok * kHeadDim + 32 * kb + 8 * g);
-  }
-}
-
-// Value tile dt, row r holds dim 16 dt + r; its k-slots are tokens 32 kt + 8 g + 0..7.
-__device__ __forceinline__ void load_values(const uint16_t* Vt, int r, int g, bf16x8 (&va)[8][2]) {
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-      va[dt][kt] = *reinterpret_cast<const bf16x8*>(Vt + (16 * dt + r) * kPageTokens + 32 * kt + 8 * g);
-}
 
 __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
                                                    const int* __restrict__ bt,
@@ -289,8 +265,122 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
   o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
+// One workgroup per (request, KV head): the resident-page partials of its
+// splits and the partials of its pages attended on arrival (a contiguous run
+// of the batch's insert lists: this request's offset plus the head's),
+// merged by log-sum-exp and normalised.
+__global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const int* __restrict__ bcount,
+                                                                 float* __restrict__ out) {
+  __shared__ int pm[1025];
+  __shared__ int tmp[5];
+  const int bh = blockIdx.x;
+  const int b = bh / d.Hkv, h = bh - b * d.Hkv;
+  const int G = d.G;
+  const int tid = threadIdx.x;
+  {
+    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
+    int loc[per], sum = 0;
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int rb = tid * per + u;
+      loc[u] = rb < d.B ? d.nmiss[rb] : 0;
+      sum += loc[u];
+    }
+    int tot;
+    int ex = block_excl_scan<kAttWG>(sum, tmp, &tot);
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int rb = tid * per + u;
+      if (rb < d.B) pm[rb] = ex;
+      ex += loc[u];
+    }
+    __syncthreads();
+  }
+  const int cnt = max(0, min(bcount[bh], d.max_blocks));
+  const int ns = (cnt + d.pps - 1) / d.pps;
+  // 16 groups of 16 threads: nsub = 16 / G subgroups per query head, each
+  // folding every nsub-th partial (8 dims per thread), combined through LDS
+  const int nsub = 16 / G;
+  const int grp = tid >> 4, dc = (tid & 15) * 8;
+  const int sg = grp / G, hh = grp - sg * G;
+  const bool active = sg < nsub;
+  const int nm = d.nmiss[b];
+  const int* mo = d.head_moff + (size_t)b * (d.Hkv + 1);
+  const int j0 = pm[b] + min(max(mo[h], 0), nm), j1 = pm[b] + min(max(mo[h + 1], 0), nm);
+  const int n_all = ns + (j1 - j0);
+  // online log-sum-exp over the resident partials, then the arrival ones
+  float M = -INFINITY, L = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  auto fold = [&](float ms, float ls, float4 a, float4 c) {
+    if (ms == -INFINITY) return;
+    const float Mn = fmaxf(M, ms);
+    const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn), fn = exp2f(ms - Mn);
+    M = Mn;
+    L = L * fo + ls * fn;
+    o[0] = o[0] * fo + a.x * fn; o[1] = o[1] * fo + a.y * fn;
+    o[2] = o[2] * fo + a.z * fn; o[3] = o[3] * fo + a.w * fn;
+    o[4] = o[4] * fo + c.x * fn; o[5] = o[5] * fo + c.y * fn;
+    o[6] = o[6] * fo + c.z * fn; o[7] = o[7] * fo + c.w * fn;
+  };
+  if (active) {
+    constexpr int U = 16;  // partials whose loads are in flight together
+    for (int base = sg; base < n_all; base += U * nsub) {
+      float ms[U], ls[U];
+      float4 a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int x = base + u * nsub;
+        ms[u] = -INFINITY;
+        ls[u] = 0.f;
+        if (x < n_all) {
+          const float* ml;
+          const float* po;
+          if (x < ns) {
+            const size_t pi = ((size_t)bh * 2 * d.splits + x) * G + hh;
+            ml = d.part_ml + 2 * pi;
+            po = d.part_o + pi * kHeadDim + dc;
+          } else {
+            const size_t pi = (size_t)(j0 + x - ns) * G + hh;
+            ml = d.arr_ml + 2 * pi;
+            po = d.arr_o + pi * kHeadDim + dc;
+          }
+          ms[u] = ml[0];
+          ls[u] = ml[1];
+          a[u] = reinterpret_cast<const float4*>(po)[0];
+          c[u] = reinterpret_cast<const float4*>(po)[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ms[u] != -INFINITY) fold(ms[u], ls[u], a[u], c[u]);
+    }
+  }
+  // combine the subgroups of each head
+  __shared__ float sm[16][16][10];
+  const int ln = tid & 15;
+  sm[grp][ln][0] = M;
+  sm[grp][ln][1] = L;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[grp][ln][2 + e] = o[e];
+  __syncthreads();
+  if (!active || sg != 0) return;
+  for (int t2 = 1; t2 < nsub; ++t2) {
+    const float* x = sm[t2 * G + hh][ln];
+    fold(x[0], x[1], make_float4(x[2], x[3], x[4], x[5]), make_float4(x[6], x[7], x[8], x[9]));
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4* o4 = reinterpret_cast<float4*>(out + ((size_t)b * d.Hq + (size_t)h * G + hh) * kHeadDim + dc);
+  o4[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+}
+
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
                          const int* bcount, float* out, int mode, hipStream_t s) {
+  if (mode == kAttendMergeArrival) {
+    hipLaunchKernelGGL(k_attend_merge_arrival, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q, bt, bntok,
                      bcount, out, mode);
   hipError_t e = hipGetLastError();

@@ -135,6 +135,8 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     }
     int tot;
     const int ex = block_excl_scan<1024>(nm, tmp, &tot);
+    // insert-list index of each head's first miss (items are head-major)
+    if (i < n_items && i % k == 0) d.head_moff[(size_t)b * (Hkv + 1) + i / k] = mcarry + ex;
     if (nm) {
       int rnk = mcarry + ex;
       for (int j = 0; j < np; ++j)
@@ -145,6 +147,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     mcarry += tot;
   }
   const int nmiss = mcarry;
+  if (tid == 0) d.head_moff[(size_t)b * (Hkv + 1) + Hkv] = nmiss;
   __syncthreads();
 
   // 3. bucketed LRU, only when the resident pages plus the misses exceed the

@@ -37,6 +37,7 @@ struct spin_ctx {
   int last_t = -1;
   size_t ws_bytes = 0;
   int32_t* h_segments = nullptr;  // host address of the segment tables, if in host memory
+  bool arrival = false;  // the last transfer attended its pages on arrival
 };
 
 namespace {
@@ -109,7 +110,8 @@ struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
       directory, segments,
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, miss_tmp, ins, nmiss,
-      freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, stats, err, total;
+      freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
+      total;
 };
 
 Layout layout(const spin_config* c, const Derived& d) {
@@ -150,6 +152,9 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.bmiss = take(B * Hkv * d.max_blocks);
   L.part_o = take(B * Hkv * 2 * d.splits * d.G * spin::kHeadDim * sizeof(float));
   L.part_ml = take(B * Hkv * 2 * d.splits * d.G * 2 * sizeof(float));
+  L.arr_o = take(B * d.max_mand * d.G * spin::kHeadDim * sizeof(float));
+  L.arr_ml = take(B * d.max_mand * d.G * 2 * sizeof(float));
+  L.head_moff = take(B * (Hkv + 1) * sizeof(int));
   L.stats = take(B * 4 * sizeof(long long));
   L.err = take(4 * sizeof(int));
   L.total = o;
@@ -295,6 +300,9 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.bmiss = reinterpret_cast<unsigned char*>(w + L.bmiss);
   v.part_o = reinterpret_cast<float*>(w + L.part_o);
   v.part_ml = reinterpret_cast<float*>(w + L.part_ml);
+  v.arr_o = reinterpret_cast<float*>(w + L.arr_o);
+  v.arr_ml = reinterpret_cast<float*>(w + L.arr_ml);
+  v.head_moff = reinterpret_cast<int*>(w + L.head_moff);
   v.stats = reinterpret_cast<long long*>(w + L.stats);
   v.err = reinterpret_cast<int*>(w + L.err);
   v.pool = static_cast<uint16_t*>(d_pool);
@@ -519,6 +527,19 @@ SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream) {
   if (!ctx) return SPIN_EINVAL;
   HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
   HIPCHK(ctx, spin::launch_retrieve(ctx->dev, S(copy_stream)));
+  ctx->arrival = false;
+  HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
+  ++ctx->fetched_gen;
+  ctx->fetched_on = S(copy_stream);
+  return SPIN_OK;
+}
+
+SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_stream) {
+  if (!ctx || !d_q || !aligned(d_q, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
+  HIPCHK(ctx, spin::launch_retrieve_attend(ctx->dev, static_cast<const uint16_t*>(d_q),
+                                           S(copy_stream)));
+  ctx->arrival = true;
   HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
   ++ctx->fetched_gen;
   ctx->fetched_on = S(copy_stream);
@@ -553,8 +574,10 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
   if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
   if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
   HIPCHK(ctx, wait_fetched(ctx, S(stream)));
+  // pages attended on arrival need only the merge; otherwise attend them now
   HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
-                                  d_block_ntok, d_block_count, d_out, spin::kAttendFetched,
+                                  d_block_ntok, d_block_count, d_out,
+                                  ctx->arrival ? spin::kAttendMergeArrival : spin::kAttendFetched,
                                   S(stream)));
   return SPIN_OK;
 }
@@ -564,11 +587,13 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
                        float* d_out, void* stream, void* copy_stream) {
   int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
   if (!rc) rc = spin_resolve_evict(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream);
-  if (!rc) rc = spin_retrieve(ctx, copy_stream);
   if (copy_stream == stream) {
+    if (!rc) rc = spin_retrieve(ctx, copy_stream);
     if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   } else {
-    // attention over the resident pages overlaps the transfer of the others
+    // the transfer attends each page as it arrives, while attention over the
+    // resident pages runs on the compute stream; then one merge
+    if (!rc) rc = spin_retrieve_attend(ctx, d_q, copy_stream);
     if (!rc) rc = spin_attend_begin(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
     if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   }

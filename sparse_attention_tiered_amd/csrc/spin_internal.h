@@ -60,6 +60,11 @@ struct Dev {
   unsigned char* bmiss;        // [B][Hkv][max_blocks] 1 = block fetched by this step's retrieve
   float* part_o;               // [B * Hkv][2 * splits][G][128]
   float* part_ml;              // [B * Hkv][2 * splits][G][2] (max in log2 units, sum)
+  // attention of each fetched page on arrival, indexed by its place in the
+  // batch's insert lists (requests ascending, canonical order)
+  float* arr_o;                // [B * max_mand][G][128] unnormalised
+  float* arr_ml;               // [B * max_mand][G][2]
+  int* head_moff;              // [B][Hkv + 1] first insert-list index of each head; [Hkv] = count
   long long* stats;            // [B][4] hits, misses, evictions, last cutoff
   int* err;                    // [1] error bits
   uint16_t* pool;              // [B * C][kPageElems]
@@ -94,10 +99,13 @@ hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bnt
 hipError_t launch_segments(const Dev& d, hipStream_t s);
 hipError_t launch_step_advance(int* t, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
+hipError_t launch_retrieve_attend(const Dev& d, const uint16_t* q, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 // mode 0: every block, finished output; 1: resident blocks only, partials;
-// 2: fetched blocks only, partials, then the merge of both passes
-enum AttendMode { kAttendAll = 0, kAttendResident = 1, kAttendFetched = 2 };
+// 2: fetched blocks only, partials, then the merge of both passes;
+// 3: no attention, only the merge of the resident-block partials with the
+// fetched pages attended on arrival (launch_retrieve_attend)
+enum AttendMode { kAttendAll = 0, kAttendResident = 1, kAttendFetched = 2, kAttendMergeArrival = 3 };
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
                          const int* bcount, float* out, int mode, hipStream_t s);
 

@@ -103,9 +103,11 @@ def test_whole_step_call_matches_stages(spin_lib, pps):
     b.close()
 
 
-def test_overlapped_attention_calls(spin_lib):
+@pytest.mark.parametrize("arrival", [False, True], ids=["fetched_pass", "on_arrival"])
+def test_overlapped_attention_calls(spin_lib, arrival):
     """attend_begin / attend_finish on one stream equal spin_attend (every
-    block a hit, every block a miss, and mixed steps)."""
+    block a hit, every block a miss, and mixed steps), with the fetched pages
+    attended after the transfer or by the transfer itself on arrival."""
     import torch
     w = W.variant(W.C2, B=2, ctx=(9000, 5000), k=8, steps=6, ar_coef=0.3)
     p = _pair(w, slots=8 * 8 + 8, oracle=False, attend_pps=8)
@@ -113,7 +115,10 @@ def test_overlapped_attention_calls(spin_lib):
     for t in range(w.steps):
         p.spin.select(p.q_dev[t])
         p.spin.resolve_evict(t)
-        p.spin.retrieve()
+        if arrival:
+            p.spin.retrieve_attend(p.q_dev[t])
+        else:
+            p.spin.retrieve()
         p.spin.attend(p.q_dev[t], out=ref)
         p.spin.attend_begin(p.q_dev[t])
         p.spin.attend_finish(p.q_dev[t])
