@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const ui
   };
   int j = blockIdx.x;
   Item cur;
-  u32x4 v[8];
+  u32x4 v[8], vn[8];
   if (j < M) {
     cur = item(j);
     load(cur, v);
@@ -137,6 +137,15 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const ui
   for (; j < M; j += gridDim.x) {
     float* po = d.arr_o + (size_t)j * G * kHeadDim;
     float* pml = d.arr_ml + (size_t)j * G * 2;
+    // the next page's loads go out first: two pages in flight per workgroup,
+    // and the next one keeps arriving while this one is stored and attended
+    const int jn = j + gridDim.x;
+    Item nxt;
+    nxt.ok = false;
+    if (jn < M) {
+      nxt = item(jn);
+      load(nxt, vn);
+    }
     if (cur.ok) {
       u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)cur.b * d.C + cur.m.x) * kPageElems);
 #pragma unroll
@@ -144,14 +153,6 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const ui
         dst[u * kRetrieveWG + tid] = v[u];
         page[u * kRetrieveWG + tid] = v[u];
       }
-    }
-    // the next page: its loads go out before this one is attended
-    const int jn = j + gridDim.x;
-    Item nxt;
-    nxt.ok = false;
-    if (jn < M) {
-      nxt = item(jn);
-      load(nxt, v);
     }
     __syncthreads();
     if (wave == 0 && !cur.ok) {
@@ -235,6 +236,8 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const ui
     }
     __syncthreads();  // the LDS page is free for the next one
     cur = nxt;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = vn[u];
   }
 }
 
