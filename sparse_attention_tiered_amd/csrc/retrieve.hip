@@ -72,9 +72,10 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
 // its KV head (the same MFMA tiles as the attention kernel, one page at a
 // time), writing an unnormalised partial (max, sum, output) under the page's
 // insert-list index.  The page is never read back from HBM for attention;
-// k_attend_merge folds these partials into the resident-page ones.  One page
-// costs the wave well under a microsecond, against tens of microseconds of
-// its workgroup's share of the link.
+// k_attend_merge_arrival folds these partials into the resident-page ones.
+// One page costs the wave about a microsecond, against tens of microseconds
+// of its workgroup's share of the link, and the next page's loads are
+// already in flight meanwhile.
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const uint16_t* __restrict__ q) {
   q = step_queries(d, q);
   __shared__ int pm[1025];
