@@ -34,6 +34,16 @@ namespace spin {
 
 constexpr int kAttWG = 256;
 
+// Pages per split of a head with cnt pages: its pages spread evenly over the
+// head's `splits` workgroups (whole pages per wave), so heads with fewer
+// pages than the largest possible count still use all their workgroups and
+// the slowest workgroup carries no more than it must.  Never above d.pps,
+// the split size the grid was sized with.
+__device__ __forceinline__ int head_pps(const Dev& d, int cnt) {
+  const int per = (cnt + d.splits - 1) / d.splits;
+  return max(4, (per + 3) & ~3);
+}
+
 __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
                                                    const int* __restrict__ bt,
                                                    const int* __restrict__ bntok,
@@ -49,7 +59,8 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + d.pps - 1) / d.pps;  // splits that hold pages
+  const int pps = head_pps(d, cnt);
+  const int ns = (cnt + pps - 1) / pps;  // splits that hold pages
   const int tid = threadIdx.x;
   const int hh = tid >> 4, dc = (tid & 15) * 8;  // merge layout: head, 8 dims
   float* orow = out + ((size_t)b * d.Hq + (size_t)h * G) * kHeadDim;
@@ -64,8 +75,8 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   if (split >= ns) return;
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int ppw = d.pps / 4;
-  const int p0 = split * d.pps + wave * ppw;
+  const int ppw = pps / 4;
+  const int p0 = split * pps + wave * ppw;
   const int np = max(0, min(cnt, p0 + ppw) - p0);  // this wave's pages: p0 .. p0+np-1
 
   // block-table entries of the wave's pages, one per lane; in the two
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + d.pps - 1) / d.pps;
+  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
   if (!both && ns <= 1) return;
   const int hh = threadIdx.x >> 4, dc = (threadIdx.x & 15) * 8;
   if (hh >= G) return;
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
     __syncthreads();
   }
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + d.pps - 1) / d.pps;
+  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
   // 16 groups of 16 threads: nsub = 16 / G subgroups per query head, each
   // folding every nsub-th partial (8 dims per thread), combined through LDS
   const int nsub = 16 / G;
