@@ -238,37 +238,70 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   }
 }
 
-// One workgroup per (request, KV head): merge its split partials (log-sum-exp)
-// and normalise.  `both` merges the resident-page and fetched-page passes;
-// otherwise only heads spanning several splits need it (the rest were
-// finished by k_attend).
-__global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __restrict__ bcount,
-                                                         float* __restrict__ out, int both) {
-  const int bh = blockIdx.x;
+// Log-sum-exp merge of the n_all partials of one (request, KV head), then
+// normalisation into out; part(x, hh, dc, ml, po) points ml at partial x's
+// (max, sum) for query head hh and po at its dims dc .. dc+7.  The 256
+// threads form 16 groups of 16: nsub = 16 / G subgroups per query head, each
+// folding every nsub-th partial (8 dims per thread) with sixteen partials'
+// loads in flight at a time, combined through LDS.  Every thread calls it.
+template <class Part>
+__device__ void merge_head(const Dev& d, int bh, int n_all, Part part, float* __restrict__ out) {
+  __shared__ float sm[16][16][10];
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
-  const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
-  if (!both && ns <= 1) return;
-  const int hh = threadIdx.x >> 4, dc = (threadIdx.x & 15) * 8;
-  if (hh >= G) return;
-  const int nslot = both ? 2 * ns : ns;
-  auto slot_of = [&](int k) { return k < ns ? k : d.splits + (k - ns); };
-  float M = -INFINITY;
-  for (int k = 0; k < nslot; ++k)
-    M = fmaxf(M, d.part_ml[2 * (((size_t)bh * 2 * d.splits + slot_of(k)) * G + hh)]);
-  float L = 0.f, o[8];
+  const int tid = threadIdx.x;
+  const int nsub = 16 / G;
+  const int grp = tid >> 4, ln = tid & 15, dc = ln * 8;
+  const int sg = grp / G, hh = grp - sg * G;
+  const bool active = sg < nsub;
+  float M = -INFINITY, L = 0.f, o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  for (int k = 0; k < nslot; ++k) {
-    const size_t pi = ((size_t)bh * 2 * d.splits + slot_of(k)) * G + hh;
-    const float ms = d.part_ml[2 * pi];
-    const float f = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    L += d.part_ml[2 * pi + 1] * f;
-    const float4* po = reinterpret_cast<const float4*>(d.part_o + pi * kHeadDim + dc);
-    const float4 a = po[0], c = po[1];
-    o[0] += a.x * f; o[1] += a.y * f; o[2] += a.z * f; o[3] += a.w * f;
-    o[4] += c.x * f; o[5] += c.y * f; o[6] += c.z * f; o[7] += c.w * f;
+  auto fold = [&](float ms, float ls, float4 a, float4 c) {
+    if (ms == -INFINITY) return;
+    const float Mn = fmaxf(M, ms);
+    const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn), fn = exp2f(ms - Mn);
+    M = Mn;
+    L = L * fo + ls * fn;
+    o[0] = o[0] * fo + a.x * fn; o[1] = o[1] * fo + a.y * fn;
+    o[2] = o[2] * fo + a.z * fn; o[3] = o[3] * fo + a.w * fn;
+    o[4] = o[4] * fo + c.x * fn; o[5] = o[5] * fo + c.y * fn;
+    o[6] = o[6] * fo + c.z * fn; o[7] = o[7] * fo + c.w * fn;
+  };
+  if (active) {
+    constexpr int U = 16;
+    for (int base = sg; base < n_all; base += U * nsub) {
+      float ms[U], ls[U];
+      float4 a[U], c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int x = base + u * nsub;
+        ms[u] = -INFINITY;
+        ls[u] = 0.f;
+        if (x < n_all) {
+          const float* ml;
+          const float* po;
+          part(x, hh, dc, ml, po);
+          ms[u] = ml[0];
+          ls[u] = ml[1];
+          a[u] = reinterpret_cast<const float4*>(po)[0];
+          c[u] = reinterpret_cast<const float4*>(po)[1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ms[u] != -INFINITY) fold(ms[u], ls[u], a[u], c[u]);
+    }
+  }
+  sm[grp][ln][0] = M;
+  sm[grp][ln][1] = L;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm[grp][ln][2 + e] = o[e];
+  __syncthreads();
+  if (!active || sg != 0) return;
+  for (int t2 = 1; t2 < nsub; ++t2) {
+    const float* x = sm[t2 * G + hh][ln];
+    fold(x[0], x[1], make_float4(x[2], x[3], x[4], x[5]), make_float4(x[6], x[7], x[8], x[9]));
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   float4* o4 = reinterpret_cast<float4*>(out + ((size_t)b * d.Hq + (size_t)h * G + hh) * kHeadDim + dc);
@@ -276,17 +309,36 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
   o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
+// One workgroup per (request, KV head): merge its split partials and
+// normalise.  `both` merges the resident-page and fetched-page passes;
+// otherwise only heads spanning several splits need it (the rest were
+// finished by k_attend).
+__global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __restrict__ bcount,
+                                                         float* __restrict__ out, int both) {
+  const int bh = blockIdx.x;
+  const int cnt = max(0, min(bcount[bh], d.max_blocks));
+  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
+  if (!both && ns <= 1) return;  // (the whole workgroup)
+  const int G = d.G;
+  merge_head(d, bh, both ? 2 * ns : ns,
+             [&](int x, int hh, int dc, const float*& ml, const float*& po) {
+               const int slot = x < ns ? x : d.splits + (x - ns);
+               const size_t pi = ((size_t)bh * 2 * d.splits + slot) * G + hh;
+               ml = d.part_ml + 2 * pi;
+               po = d.part_o + pi * kHeadDim + dc;
+             },
+             out);
+}
+
 // One workgroup per (request, KV head): the resident-page partials of its
 // splits and the partials of its pages attended on arrival (a contiguous run
-// of the batch's insert lists: this request's offset plus the head's),
-// merged by log-sum-exp and normalised.
+// of the batch's insert lists: this request's offset plus the head's).
 __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const int* __restrict__ bcount,
                                                                  float* __restrict__ out) {
   __shared__ int pm[1025];
   __shared__ int tmp[5];
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
-  const int G = d.G;
   const int tid = threadIdx.x;
   {
     constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
@@ -309,81 +361,23 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
   }
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
   const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
-  // 16 groups of 16 threads: nsub = 16 / G subgroups per query head, each
-  // folding every nsub-th partial (8 dims per thread), combined through LDS
-  const int nsub = 16 / G;
-  const int grp = tid >> 4, dc = (tid & 15) * 8;
-  const int sg = grp / G, hh = grp - sg * G;
-  const bool active = sg < nsub;
   const int nm = d.nmiss[b];
   const int* mo = d.head_moff + (size_t)b * (d.Hkv + 1);
   const int j0 = pm[b] + min(max(mo[h], 0), nm), j1 = pm[b] + min(max(mo[h + 1], 0), nm);
-  const int n_all = ns + (j1 - j0);
-  // online log-sum-exp over the resident partials, then the arrival ones
-  float M = -INFINITY, L = 0.f, o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.f;
-  auto fold = [&](float ms, float ls, float4 a, float4 c) {
-    if (ms == -INFINITY) return;
-    const float Mn = fmaxf(M, ms);
-    const float fo = M == -INFINITY ? 0.f : exp2f(M - Mn), fn = exp2f(ms - Mn);
-    M = Mn;
-    L = L * fo + ls * fn;
-    o[0] = o[0] * fo + a.x * fn; o[1] = o[1] * fo + a.y * fn;
-    o[2] = o[2] * fo + a.z * fn; o[3] = o[3] * fo + a.w * fn;
-    o[4] = o[4] * fo + c.x * fn; o[5] = o[5] * fo + c.y * fn;
-    o[6] = o[6] * fo + c.z * fn; o[7] = o[7] * fo + c.w * fn;
-  };
-  if (active) {
-    constexpr int U = 16;  // partials whose loads are in flight together
-    for (int base = sg; base < n_all; base += U * nsub) {
-      float ms[U], ls[U];
-      float4 a[U], c[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int x = base + u * nsub;
-        ms[u] = -INFINITY;
-        ls[u] = 0.f;
-        if (x < n_all) {
-          const float* ml;
-          const float* po;
-          if (x < ns) {
-            const size_t pi = ((size_t)bh * 2 * d.splits + x) * G + hh;
-            ml = d.part_ml + 2 * pi;
-            po = d.part_o + pi * kHeadDim + dc;
-          } else {
-            const size_t pi = (size_t)(j0 + x - ns) * G + hh;
-            ml = d.arr_ml + 2 * pi;
-            po = d.arr_o + pi * kHeadDim + dc;
-          }
-          ms[u] = ml[0];
-          ls[u] = ml[1];
-          a[u] = reinterpret_cast<const float4*>(po)[0];
-          c[u] = reinterpret_cast<const float4*>(po)[1];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (ms[u] != -INFINITY) fold(ms[u], ls[u], a[u], c[u]);
-    }
-  }
-  // combine the subgroups of each head
-  __shared__ float sm[16][16][10];
-  const int ln = tid & 15;
-  sm[grp][ln][0] = M;
-  sm[grp][ln][1] = L;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sm[grp][ln][2 + e] = o[e];
-  __syncthreads();
-  if (!active || sg != 0) return;
-  for (int t2 = 1; t2 < nsub; ++t2) {
-    const float* x = sm[t2 * G + hh][ln];
-    fold(x[0], x[1], make_float4(x[2], x[3], x[4], x[5]), make_float4(x[6], x[7], x[8], x[9]));
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  float4* o4 = reinterpret_cast<float4*>(out + ((size_t)b * d.Hq + (size_t)h * G + hh) * kHeadDim + dc);
-  o4[0] = make_float4(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
-  o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+  const int G = d.G;
+  merge_head(d, bh, ns + (j1 - j0),
+             [&](int x, int hh, int dc, const float*& ml, const float*& po) {
+               if (x < ns) {
+                 const size_t pi = ((size_t)bh * 2 * d.splits + x) * G + hh;
+                 ml = d.part_ml + 2 * pi;
+                 po = d.part_o + pi * kHeadDim + dc;
+               } else {
+                 const size_t pi = (size_t)(j0 + x - ns) * G + hh;
+                 ml = d.arr_ml + 2 * pi;
+                 po = d.arr_o + pi * kHeadDim + dc;
+               }
+             },
+             out);
 }
 
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
