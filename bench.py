@@ -67,11 +67,24 @@ def memcpy_h2d_gbs(nbytes=1 << 30):
     return gbs
 
 
+def kernel_sources_sha():
+    """sha256 (12 hex digits) over every kernel source and header of the
+    library, in name order: what a committed counter summary was taken with."""
+    import hashlib
+    csrc = os.path.join(ROOT, "sparse_attention_tiered_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
 def counter_traffic(cfg_key, stage, bytes_per_launch):
     """HBM-side bytes per launch of a stage from the committed rocprofv3 counter
-    summary (traffic per algorithmic byte over timed steps), or None when any
-    kernel source changed since the counters were taken."""
-    import hashlib
+    summary (traffic per algorithmic byte over the steps it counts), or None
+    when any kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{cfg_key}_hbm_counters.md")
     try:
         text = open(path).read()
@@ -81,10 +94,8 @@ def counter_traffic(cfg_key, stage, bytes_per_launch):
     if not lines:
         return None
     kv = dict(t.split("=", 1) for t in lines[-1].split()[1:])
-    for src in ("select", "resolve", "retrieve", "attend"):
-        with open(os.path.join(ROOT, "sparse_attention_tiered_amd", "csrc", f"{src}.hip"), "rb") as fh:
-            if hashlib.sha256(fh.read()).hexdigest()[:12] != kv.get(f"sha_{src}"):
-                return None
+    if kv.get("sha_kernels") != kernel_sources_sha():
+        return None
     ratio = kv.get(f"traffic_ratio_{stage}")
     return None if ratio is None else float(ratio) * bytes_per_launch
 
