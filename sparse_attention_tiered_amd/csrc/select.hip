@@ -139,7 +139,7 @@ struct TopkLds {
 // ids, ascending, to out.  Every thread of the workgroup calls it.
 template <int NT>
 __device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, int* out) {
-  static_assert(NT * 2 >= kTopkBins && NT >= kTopkCand, "one thread per bucket pair");
+  static_assert(kTopkBins % NT == 0 && NT >= kTopkCand && NT >= 256, "whole buckets per thread");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < kTopkBins; i += NT) L.hist[i] = 0;
   for (int i = tid; i < (n + 31) / 32; i += NT) L.chosen[i] = 0;
@@ -165,17 +165,29 @@ __device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, in
   if (!(scale < 3.0e38f)) scale = 0.f;
   for (int i = tid; i < n; i += NT) atomicAdd(&L.hist[topk_bucket(L.vals[i], mn, scale)], 1);
   __syncthreads();
-  // counts from the top: thread t holds buckets 2047-2t and 2046-2t
+  // counts from the top: thread t holds the PER buckets just below
+  // 2047 - PER t, highest first
   {
-    const int hi = kTopkBins - 1 - 2 * tid, lo = hi - 1;
-    const int a = tid < kTopkBins / 2 ? L.hist[hi] : 0;
-    const int c = tid < kTopkBins / 2 ? L.hist[lo] : 0;
+    constexpr int PER = kTopkBins / NT;
+    const int top = kTopkBins - 1 - PER * tid;
+    int cnts[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      cnts[i] = L.hist[top - i];
+      sum += cnts[i];
+    }
     int tot;
-    const int before = block_excl_scan<NT>(a + c, L.tmp, &tot);
-    if (tid < kTopkBins / 2 && before < k && before + a + c >= k) {
-      const bool in_hi = before + a >= k;
-      L.sh[0] = in_hi ? hi : lo;
-      L.sh[1] = in_hi ? before : before + a;
+    int before = block_excl_scan<NT>(sum, L.tmp, &tot);
+    if (before < k && before + sum >= k) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (before + cnts[i] >= k) {
+          L.sh[0] = top - i;
+          L.sh[1] = before;
+          break;
+        }
+        before += cnts[i];
+      }
     }
   }
   __syncthreads();
@@ -412,8 +424,8 @@ hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, i
 }
 
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s) {
-  // 1024 threads: measured fastest (per-key work dominates, not barriers;
-  // 512 and 256 threads were 1.1-1.9x slower on 2048 and 7.7K-key lists)
+  // 1024 threads: measured fastest (512 and 256 threads took 1.0-1.3x and
+  // 1.3-2.0x as long on 2048- and 7.7K-score lists)
   hipLaunchKernelGGL(k_topk<1024>, dim3(d.B * d.Hkv), dim3(1024), 0, s, d, scores, sel);
   return hipGetLastError();
 }
