@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = src[u * kRetrieveWG + tid];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dst[u * kRetrieveWG + tid] = v[u];
+    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(v[u], dst + u * kRetrieveWG + tid);
   }
 }
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const ui
       u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)cur.b * d.C + cur.m.x) * kPageElems);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        dst[u * kRetrieveWG + tid] = v[u];
+        __builtin_nontemporal_store(v[u], dst + u * kRetrieveWG + tid);
         page[u * kRetrieveWG + tid] = v[u];
       }
     }
