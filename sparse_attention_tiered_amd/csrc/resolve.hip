@@ -354,30 +354,82 @@ __global__ __launch_bounds__(1024) void k_segments(Dev d) {
     }
     __syncthreads();
   }
+  // each loop below issues the loads of U iterations before using any, so a
+  // thread waits for one round trip per U items rather than one per item
+  constexpr int U = 8;
   const int top0 = d.seg_ctl[0];
-  for (int j = tid; j < F; j += 1024) {
-    const int b = owner_of(pf, B, j);
-    const int at = top0 + j;
-    if (at < d.n_seg) d.seg_stack[at] = d.freed[(size_t)b * ne + (j - pf[b])];
-    else atomicOr(d.err, kErrState);
+  for (int j0 = tid; j0 < F; j0 += 1024 * U) {
+    int fs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 1024 * u;
+      fs[u] = -1;
+      if (j < F) {
+        const int b = owner_of(pf, B, j);
+        fs[u] = d.freed[(size_t)b * ne + (j - pf[b])];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 1024 * u;
+      if (j >= F) break;
+      const int at = top0 + j;
+      if (at < d.n_seg) d.seg_stack[at] = fs[u];
+      else atomicOr(d.err, kErrState);
+    }
   }
   const int top1 = min(top0 + F, d.n_seg);
   __syncthreads();
-  for (int j = tid; j < A; j += 1024) {
-    const int b = owner_of(pa, B, j);
-    const int e = d.alloc[(size_t)b * ne + (j - pa[b])];
-    const int idx = top1 - 1 - j;
-    if (idx >= 0) d.directory[(size_t)b * ne + e] = d.seg_stack[idx];
-    else atomicOr(d.err, kErrSegPool);
+  for (int j0 = tid; j0 < A; j0 += 1024 * U) {
+    int es[U], ss[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 1024 * u;
+      es[u] = -1;
+      ss[u] = -1;
+      if (j < A) {
+        const int b = owner_of(pa, B, j);
+        es[u] = b * ne + d.alloc[(size_t)b * ne + (j - pa[b])];
+        const int idx = top1 - 1 - j;
+        if (idx >= 0) ss[u] = d.seg_stack[idx];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 1024 * u;
+      if (j >= A) break;
+      if (top1 - 1 - j >= 0) d.directory[es[u]] = ss[u];
+      else atomicOr(d.err, kErrSegPool);
+    }
   }
   __syncthreads();
-  for (int j = tid; j < M; j += 1024) {
-    const int b = owner_of(pm, B, j);
-    const int4 m = d.ins[(size_t)b * d.max_mand + (j - pm[b])];  // (slot, h, page)
-    const int seg = d.directory[(size_t)b * ne + m.y * d.ndir + (m.z >> 6)];
-    if (seg >= 0 && seg < d.n_seg) {
-      d.segments[(size_t)seg * kSegEntries + (m.z & 63)] = m.x;
-      atomicAdd(&d.seg_live[seg], 1);
+  for (int j0 = tid; j0 < M; j0 += 1024 * U) {
+    int4 ms[U];
+    int bs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 1024 * u;
+      ms[u] = make_int4(-1, 0, 0, 0);
+      bs[u] = 0;
+      if (j < M) {
+        bs[u] = owner_of(pm, B, j);
+        ms[u] = d.ins[(size_t)bs[u] * d.max_mand + (j - pm[bs[u]])];  // (slot, h, page)
+      }
+    }
+    int segs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      segs[u] = -1;
+      if (j0 + 1024 * u < M)
+        segs[u] = d.directory[(size_t)bs[u] * ne + ms[u].y * d.ndir + (ms[u].z >> 6)];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int seg = segs[u];
+      if (j0 + 1024 * u < M && seg >= 0 && seg < d.n_seg) {
+        d.segments[(size_t)seg * kSegEntries + (ms[u].z & 63)] = ms[u].x;
+        atomicAdd(&d.seg_live[seg], 1);
+      }
     }
   }
   if (tid == 0) d.seg_ctl[0] = max(top1 - A, 0);
