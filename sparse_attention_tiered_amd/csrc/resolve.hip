@@ -198,11 +198,18 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   const int E = (C + 1023) / 1024;  // contiguous slots per thread
   const int lo = min(C, tid * E), hi = min(C, lo + E);
   if (need > 0) {
-    if (tid == 0) {
-      int below = 0, cv = 0;
-      while (cv < kBuckets - 1 && below + hist[cv] < need) below += hist[cv++];
-      sh_cut = cv;
-      sh_below = below;
+    // the cutoff: the first bucket whose inclusive count reaches `need`, or
+    // the newest one (one wave, one bucket per lane)
+    static_assert(kBuckets == 64, "one bucket per lane");
+    if (tid < 64) {
+      const int hv = hist[tid];
+      const int inc = wave_incl_scan(hv);
+      const unsigned long long hit = __ballot(inc >= need) | (1ull << (kBuckets - 1));
+      const int cv = __ffsll((long long)hit) - 1;
+      if (tid == cv) {
+        sh_cut = cv;
+        sh_below = inc - hv;
+      }
     }
     __syncthreads();
     cut = sh_cut;
@@ -218,20 +225,39 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       }
     }
     __syncthreads();
-    for (int c = tid; c < C; c += 1024) {
-      if (code[c] != kCodeVictim) continue;
-      const int own = owner[c];
-      const int h = own / d.max_pages, page = own - h * d.max_pages;
-      const int seg = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
-      if (seg >= 0 && seg < d.n_seg) {
-        d.segments[(size_t)seg * kSegEntries + (page & 63)] = -1;
-        atomicSub(&d.seg_live[seg], 1);
-      } else {
-        atomicOr(d.err, kErrState);
+    // the victims' owners, then their directory entries, eight slots' loads
+    // in flight at a time, then the table updates
+    constexpr int UV = 8;
+    for (int c0 = tid; c0 < C; c0 += 1024 * UV) {
+      int own[UV], seg[UV];
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const int c = c0 + 1024 * u;
+        own[u] = (c < C && code[c] == kCodeVictim) ? owner[c] : -1;
       }
-      owner[c] = -1;
-      last[c] = -1;
-      code[c] = kCodeFree;
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        seg[u] = -2;  // not a victim
+        if (own[u] >= 0) {
+          const int h = own[u] / d.max_pages, page = own[u] - h * d.max_pages;
+          seg[u] = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        if (seg[u] == -2) continue;
+        const int c = c0 + 1024 * u;
+        const int page = own[u] % d.max_pages;
+        if (seg[u] >= 0 && seg[u] < d.n_seg) {
+          d.segments[(size_t)seg[u] * kSegEntries + (page & 63)] = -1;
+          atomicSub(&d.seg_live[seg[u]], 1);
+        } else {
+          atomicOr(d.err, kErrState);
+        }
+        owner[c] = -1;
+        last[c] = -1;
+        code[c] = kCodeFree;
+      }
     }
     __syncthreads();
     // emptied segments leave the directory, in (head, directory index) order:
@@ -240,9 +266,23 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     const int ne = Hkv * d.ndir;
     for (int i = tid; i < (ne + 31) / 32; i += 1024) mand[i] = 0;
     __syncthreads();
-    for (int e = tid; e < ne; e += 1024) {
-      const int seg = dir[e];
-      if (seg >= 0 && load_device(&d.seg_live[seg]) == 0) atomicOr(&mand[e >> 5], 1u << (e & 31));
+    constexpr int UE = 4;  // entries whose loads are in flight together
+    for (int e0 = tid; e0 < ne; e0 += 1024 * UE) {
+      int seg[UE], live[UE];
+#pragma unroll
+      for (int u = 0; u < UE; ++u) {
+        const int e = e0 + 1024 * u;
+        seg[u] = e < ne ? dir[e] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < UE; ++u)
+        live[u] = (seg[u] >= 0 && seg[u] < d.n_seg) ? load_device(&d.seg_live[seg[u]]) : 1;
+#pragma unroll
+      for (int u = 0; u < UE; ++u)
+        if (live[u] == 0) {
+          const int e = e0 + 1024 * u;
+          atomicOr(&mand[e >> 5], 1u << (e & 31));
+        }
     }
     __syncthreads();
     const int Ed = (ne + 1023) / 1024;
