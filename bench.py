@@ -5,8 +5,10 @@ top-k), two-level resolve with bucketed-LRU eviction, retrieve of missed pages
 from pinned host memory (on a second stream), and paged sparse attention.
 Inputs (host KV, queries for every step) are resident before the timed
 region.  Runs step 0 (all misses) with stage events, W-1 more warm-up steps,
-K timed steps (the whole-step call, no events inside: `value`), K more steps
-with an event between stages (stage times, the transfer's rate), then
+K timed steps (`value`: replays of one captured HIP graph of the
+device-indexed whole-step call, as a serving loop would run them; --eager
+calls spin_step per step instead), K more steps with an event between stages
+(stage times, the transfer's rate), then
 isolated replays of select and attention on the last step's data, warm and
 after a 512 MB read that evicts the memory-side cache (cold).  Prints one
 JSON line.
@@ -143,8 +145,9 @@ def main():
     ap.add_argument("--budget-ratio", type=float, default=None,
                     help="buffer elasticity ablation: each request's budget = mandatory pages "
                          "x (1 + ratio), capped by its slots (0 = no buffer pages)")
-    ap.add_argument("--graph", action="store_true",
-                    help="time the steps as replays of one captured HIP graph (spin_step_at)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as eager whole-step calls (spin_step) instead of replays "
+                         "of one captured HIP graph (spin_step_at)")
     ap.add_argument("--host-segments", action="store_true",
                     help="keep the second-level segment tables in pinned host memory")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -164,8 +167,7 @@ def main():
 
     if args.warmup < 1:
         ap.error("--warmup must be at least 1 (step 0 is timed on its own)")
-    if args.graph and args.no_overlap:
-        ap.error("--graph replays the whole-step call; --no-overlap needs the stage calls")
+    use_graph = not args.eager and not args.no_overlap
     w = W.get(args.config)
     n_steps = max(w.steps, args.warmup + 2 * args.steps)
     t0 = time.time()
@@ -199,9 +201,8 @@ def main():
     def step(t, ev=None):
         # the stages of spin_step, one call each
         # events (instrumented pass only): 0 start, 1 select done, 2 resolve
-        # done (S); 3 retrieve start, 4 retrieve done (copy stream); 5
-        # resident-page attention done (overlapped with retrieve), 6 attention
-        # done (S)
+        # done; 3 / 4 around the transfer (with the resident-page attention
+        # in the same launch when overlapped); 6 attention done
         if ev is not None:
             ev[0].record(S)
         spin.select(q[t], stream=S)
@@ -210,23 +211,24 @@ def main():
         spin.resolve_evict(t, stream=S)
         if ev is not None:
             ev[2].record(S)
-            if Cs is not S:
-                Cs.wait_stream(S)
-            ev[3].record(Cs)
         if overlap:
-            # as the whole-step call: the transfer attends its pages on arrival
-            spin.retrieve_attend(q[t], copy_stream=Cs)
-        else:
-            spin.retrieve(copy_stream=Cs)
-        if ev is not None:
-            ev[4].record(Cs)
-        if overlap:
-            spin.attend_begin(q[t], stream=S)
+            # as the whole-step call: one launch pulls the missed pages
+            # (attending each on arrival) while it attends the resident ones
             if ev is not None:
+                ev[3].record(S)
+            spin.transfer_attend(q[t], stream=S)
+            if ev is not None:
+                ev[4].record(S)
                 ev[5].record(S)
             spin.attend_finish(q[t], stream=S)
         else:
             if ev is not None:
+                if Cs is not S:
+                    Cs.wait_stream(S)
+                ev[3].record(Cs)
+            spin.retrieve(copy_stream=Cs)
+            if ev is not None:
+                ev[4].record(Cs)
                 ev[5].record(S)
             spin.attend(q[t], stream=S)
         if ev is not None:
@@ -249,7 +251,7 @@ def main():
     # timed pass: the steps alone (a timing event costs the GPU several
     # microseconds, so the per-stage events go in a second pass)
     graph = None
-    if args.graph:
+    if use_graph:
         # one step captured with the device-side step index, replayed K times
         t_dev = torch.full((1,), args.warmup, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
@@ -290,8 +292,7 @@ def main():
         step_miss.append(st_i.misses - prev)
         prev = st_i.misses
     st2 = st_i
-    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend_resident": 0.0,
-             "attend": 0.0}
+    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend": 0.0}
     instr_ms = 0.0
     step_ms, ret_ms = [], []
     for e in evs:
@@ -300,10 +301,8 @@ def main():
         stage["select"] += e[0].elapsed_time(e[1])
         stage["resolve_evict"] += e[1].elapsed_time(e[2])
         stage["retrieve"] += e[3].elapsed_time(e[4])
-        stage["attend_resident"] += e[2].elapsed_time(e[5]) if overlap else 0.0
-        # after the transfer: fetched-page attention and the merge (or the
-        # whole attention without overlap)
-        stage["attend"] += max(e[4].elapsed_time(e[6]), 0.0) if overlap else e[4].elapsed_time(e[6])
+        # after the transfer: the merge (or the whole attention without overlap)
+        stage["attend"] += max(e[4].elapsed_time(e[6]), 0.0)
         instr_ms += e[0].elapsed_time(e[6])
     stage_ms = {k: v / K for k, v in stage.items()}
 
@@ -381,7 +380,7 @@ def main():
                      "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if retrieve_bytes else 0.0,
                      "launch_ms": stage_ms["retrieve"],
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
-                     "kernels": ["k_retrieve_attend" if overlap else "k_retrieve"]},
+                     "kernels": ["k_transfer_attend" if overlap else "k_retrieve"]},
     }
     # the transfer over the steps that move at least 8 MB (small transfers are
     # dominated by a fixed latency), and step 0 on its own

@@ -284,11 +284,23 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
                                 const int32_t* d_block_ntok, const int32_t* d_block_count,
                                 float* d_out, void* stream);
 
-/* One whole decode step: select, resolve_evict, retrieve (on copy_stream),
- * attention.  When copy_stream differs from stream, the transfer attends its
- * pages on arrival (spin_retrieve_attend) while attention over the resident
- * pages runs on `stream` (spin_attend_begin), and spin_attend_finish merges;
- * otherwise it is spin_retrieve, then spin_attend. */
+/* Retrieve and Attention overlapped in one launch on `stream`: some
+ * workgroups pull the pages the last spin_resolve_evict listed and attend
+ * each on arrival (as spin_retrieve_attend), the others attend the resident
+ * pages (as spin_attend_begin); spin_attend_finish then merges into d_out.
+ * No second stream and no event between the two.  The block tables are
+ * those of the last spin_resolve_evict; the same d_q goes to
+ * spin_attend_finish. */
+SPIN_API int spin_transfer_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                                  const int32_t* d_block_ntok, const int32_t* d_block_count,
+                                  void* stream);
+
+/* One whole decode step: select, resolve_evict, then Retrieve and
+ * Attention.  When copy_stream differs from stream the two overlap: the
+ * transfer attends its pages on arrival on copy_stream (spin_retrieve_attend)
+ * while `stream` attends the resident pages (spin_attend_begin), then
+ * spin_attend_finish merges; when they are equal it is spin_retrieve, then
+ * spin_attend. */
 SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream);
@@ -297,7 +309,10 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
  * kernels read t from *d_t (device int32) and the step's queries at
  * d_q_steps + t * q_step_elems (bf16 elements; q_step_elems * 2 a multiple
  * of 16), and a last kernel on `stream` increments *d_t, so one captured call
- * replays as consecutive steps.  t is the caller's to keep non-decreasing.
+ * replays as consecutive steps.  Overlapped (copy_stream != stream), the
+ * transfer and the resident-page attention share one launch on `stream`
+ * (spin_transfer_attend): nothing runs on copy_stream and the graph holds no
+ * event; the results equal spin_step's bit for bit.  t is the caller's to keep non-decreasing.
  * Captured (stream capture active on `stream`), the call waits for no
  * transfer enqueued before the capture: the context must be idle when the
  * capture begins (synchronise the streams it used).  The captured graph holds

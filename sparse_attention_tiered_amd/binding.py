@@ -63,6 +63,7 @@ SIGNATURES = {
     "spin_resolve_evict": (c_int, [_P, _P, c_int32, _P, _P, _P, _P]),
     "spin_retrieve": (c_int, [_P, _P]),
     "spin_retrieve_attend": (c_int, [_P, _P, _P]),
+    "spin_transfer_attend": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spin_attend_begin": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend_finish": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
@@ -234,6 +235,11 @@ class Spin:
 
     def retrieve(self, copy_stream=None):
         self._chk("spin_retrieve", self.lib.spin_retrieve(self.ctx, _stream(copy_stream)))
+
+    def transfer_attend(self, q, stream=None):
+        self._chk("spin_transfer_attend", self.lib.spin_transfer_attend(
+            self.ctx, _ptr(q), _ptr(self.block_table), _ptr(self.block_ntok), _ptr(self.block_count),
+            _stream(stream)))
 
     def retrieve_attend(self, q, copy_stream=None):
         self._chk("spin_retrieve_attend",

@@ -1,0 +1,190 @@
+// The transfer that attends each fetched page on arrival, as a workgroup
+// body shared by the transfer kernel and the one-launch transfer + attention
+// kernel.
+#pragma once
+
+#include "attend_tile.h"
+#include "device_util.h"
+#include "spin_internal.h"
+
+namespace spin {
+
+// The transfer with the fetched pages attended on arrival: each page also
+// goes into LDS, and wave 0 runs its attention there for the G query heads of
+// its KV head (the same MFMA tiles as the attention kernel, one page at a
+// time), writing an unnormalised partial (max, sum, output) under the page's
+// insert-list index.  The page is never read back from HBM for attention;
+// k_attend_merge_arrival folds these partials into the resident-page ones.
+// One page costs the wave about a microsecond, against tens of microseconds
+// of its workgroup's share of the link, and the next page's loads are
+// already in flight meanwhile.
+//
+// Workgroup wg of nwg: pages wg, wg + nwg, ... of the batch's insert lists;
+// q already points at this step's queries.
+__device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t* __restrict__ q,
+                                                   int wg, int nwg) {
+  __shared__ int pm[1025];
+  __shared__ int tmp[5];
+  __shared__ u32x4 page[kPageBytes / 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int G = d.G;
+  int M;
+  {
+    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
+    int loc[per], sum = 0;
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int b = tid * per + u;
+      loc[u] = b < d.B ? d.nmiss[b] : 0;
+      sum += loc[u];
+    }
+    int ex = block_excl_scan<kRetrieveWG>(sum, tmp, &M);
+#pragma unroll
+    for (int u = 0; u < per; ++u) {
+      const int b = tid * per + u;
+      if (b < d.B) pm[b] = ex;
+      ex += loc[u];
+    }
+    __syncthreads();
+  }
+  const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  // a page's host address and its checks; its loads are issued one page
+  // ahead, so they stay in flight while the wave attends the page before it
+  struct Item {
+    int b, ntok;
+    int4 m;  // (slot, KV head, page)
+    bool ok;
+  };
+  auto item = [&](int j) {
+    Item it;
+    it.b = owner_of(pm, d.B, j);
+    const size_t e = (size_t)it.b * d.max_mand + (j - pm[it.b]);
+    it.m = d.ins[e];
+    it.ntok = d.miss_tmp[e].w;
+    it.ok = (unsigned)it.m.x < (unsigned)d.C && (unsigned)it.m.y < (unsigned)d.Hkv &&
+            (unsigned)it.m.z < (unsigned)d.req_pages[it.b];
+    return it;
+  };
+  auto load = [&](const Item& it, u32x4 (&v)[8]) {
+    if (!it.ok) return;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        d.host_base[it.b] + ((size_t)it.m.y * d.req_stride[it.b] + it.m.z) * (size_t)kPageBytes);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[u * kRetrieveWG + tid];
+  };
+  int j = wg;
+  Item cur;
+  u32x4 v[8], vn[8];
+  if (j < M) {
+    cur = item(j);
+    load(cur, v);
+  }
+  for (; j < M; j += nwg) {
+    float* po = d.arr_o + (size_t)j * G * kHeadDim;
+    float* pml = d.arr_ml + (size_t)j * G * 2;
+    // the next page's loads go out first: two pages in flight per workgroup,
+    // and the next one keeps arriving while this one is stored and attended
+    const int jn = j + nwg;
+    Item nxt;
+    nxt.ok = false;
+    if (jn < M) {
+      nxt = item(jn);
+      load(nxt, vn);
+    }
+    if (cur.ok) {
+      u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)cur.b * d.C + cur.m.x) * kPageElems);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        __builtin_nontemporal_store(v[u], dst + u * kRetrieveWG + tid);
+        page[u * kRetrieveWG + tid] = v[u];
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && !cur.ok) {
+      // (the same decision in every thread) an empty partial
+      if (r < G && g == 0) {
+        pml[2 * r] = -INFINITY;
+        pml[2 * r + 1] = 0.f;
+      }
+    } else if (wave == 0) {
+      const int b = cur.b, ntok = cur.ntok;
+      bf16x8 qb[4];
+      if (r < G) {
+        const uint16_t* qp = q + ((size_t)b * d.Hq + (size_t)cur.m.y * G + r) * kHeadDim;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = *reinterpret_cast<const bf16x8*>(qp + 32 * kb + 8 * g);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qb[kb] = bf16x8{};
+      }
+      const uint16_t* P = reinterpret_cast<const uint16_t*>(page);
+      bf16x8 ka[4][4];
+      load_keys(P, r, g, ka);
+      f32x4 s[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) s[tt] = mfma16x16x32(ka[tt][kb], qb[kb], s[tt]);
+      }
+      // s[tt][i]: head r, token 32 (tt/2) + 8 g + 4 (tt%2) + i
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 32 * (tt >> 1) + 8 * g + 4 * (tt & 1) + i;
+          const float x = tok < ntok ? s[tt][i] * sl2 : -INFINITY;
+          s[tt][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool none = mx == -INFINITY;
+      float l = 0.f;
+      bf16x8 phi[2], plo[2];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = none ? 0.f : exp2f(s[tt][i] - mx);
+          l += pv;
+          const __bf16 hi = (__bf16)pv;
+          phi[tt >> 1][4 * (tt & 1) + i] = hi;
+          plo[tt >> 1][4 * (tt & 1) + i] = (__bf16)(pv - (float)hi);
+        }
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+      bf16x8 va[8][2];
+      load_values(P + kPageTokens * kHeadDim, r, g, va);
+      f32x4 acc[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          acc[dt] = mfma16x16x32(va[dt][kt], phi[kt], acc[dt]);
+          acc[dt] = mfma16x16x32(va[dt][kt], plo[kt], acc[dt]);
+        }
+      }
+      // acc[dt][i] = unnormalised out[head r][dim 16 dt + 4 g + i]
+      if (r < G) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          *reinterpret_cast<float4*>(po + (size_t)r * kHeadDim + 16 * dt + 4 * g) =
+              make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+        if (g == 0) {
+          pml[2 * r] = mx;
+          pml[2 * r + 1] = l;
+        }
+      }
+    }
+    __syncthreads();  // the LDS page is free for the next one
+    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = vn[u];
+  }
+}
+
+}  // namespace spin

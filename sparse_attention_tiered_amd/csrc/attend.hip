@@ -26,6 +26,7 @@
 // combines the split partials (log-sum-exp).  (Merging in the last workgroup
 // to finish would need a device-scope fence per workgroup, which writes back
 // the whole L2 on this chip and cost more than the second launch.)
+#include "arrival.h"
 #include "attend_tile.h"
 #include "device_util.h"
 #include "spin_internal.h"
@@ -44,18 +45,18 @@ __device__ __forceinline__ int head_pps(const Dev& d, int cnt) {
   return max(4, (per + 3) & ~3);
 }
 
-__global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
-                                                   const int* __restrict__ bt,
-                                                   const int* __restrict__ bntok,
-                                                   const int* __restrict__ bcount,
-                                                   float* __restrict__ out, int mode) {
-  q = step_queries(d, q);
+// Workgroup wg of the attention grid (B * Hkv * splits): split wg % splits
+// of (request, KV head) wg / splits; q already points at this step's queries.
+__device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restrict__ q,
+                                          const int* __restrict__ bt, const int* __restrict__ bntok,
+                                          const int* __restrict__ bcount, float* __restrict__ out,
+                                          int mode, int wg) {
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][132];
 
-  const int split = blockIdx.x % d.splits;
-  const int bh = blockIdx.x / d.splits;
+  const int split = wg % d.splits;
+  const int bh = wg / d.splits;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
@@ -238,6 +239,31 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
   }
 }
 
+__global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
+                                                   const int* __restrict__ bt,
+                                                   const int* __restrict__ bntok,
+                                                   const int* __restrict__ bcount,
+                                                   float* __restrict__ out, int mode) {
+  attend_wg(d, step_queries(d, q), bt, bntok, bcount, out, mode, blockIdx.x);
+}
+
+// Retrieve and the resident-page attention in one launch on one stream: the
+// first kRetrieveGrid workgroups pull the step's missed pages and attend each
+// on arrival, the rest attend the resident pages (partials), so the two
+// overlap without a second stream or any event between them; the merge
+// follows on the same stream.
+__global__ __launch_bounds__(kAttWG, 2) void k_transfer_attend(Dev d, const uint16_t* __restrict__ q,
+                                                            const int* __restrict__ bt,
+                                                            const int* __restrict__ bntok,
+                                                            const int* __restrict__ bcount) {
+  static_assert(kRetrieveWG == kAttWG, "one workgroup size for both roles");
+  q = step_queries(d, q);
+  if ((int)blockIdx.x < kRetrieveGrid)
+    retrieve_attend_wg(d, q, blockIdx.x, kRetrieveGrid);
+  else
+    attend_wg(d, q, bt, bntok, bcount, nullptr, kAttendResident, blockIdx.x - kRetrieveGrid);
+}
+
 // Log-sum-exp merge of the n_all partials of one (request, KV head), then
 // normalisation into out; part(x, hh, dc, ml, po) points ml at partial x's
 // (max, sum) for query head hh and po at its dims dc .. dc+7.  The 256
@@ -378,6 +404,13 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
                }
              },
              out);
+}
+
+hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
+                                  const int* bcount, hipStream_t s) {
+  hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s,
+                     d, q, bt, bntok, bcount);
+  return hipGetLastError();
 }
 
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,

@@ -25,14 +25,21 @@ struct spin_ctx {
   spin_config cfg;
   Dev dev;
   std::vector<ReqMirror> req;
-  hipEvent_t ev_resolved = nullptr;  // recorded after resolve/evict
-  hipEvent_t ev_fetched = nullptr;   // recorded after retrieve
-  // Which recording of ev_fetched is the latest (0: none yet), the stream it
-  // was recorded on, and the stream that last waited for that recording: a
-  // stream already ordered after the transfer needs no second wait (each wait
-  // costs the GPU several microseconds even when the event has completed).
+  // Cross-stream ordering, recorded lazily: an event record or wait costs the
+  // GPU several microseconds even when nothing is pending, so the events are
+  // recorded only when another stream has to wait.  ev_resolved marks the
+  // latest resolve (enqueued on resolved_on), ev_fetched the latest transfer
+  // (fetched_gen counts transfers, 0: none yet; enqueued on fetched_on); each
+  // is recorded, behind everything enqueued on its stream by then, the first
+  // time another stream needs it.  waited_on already waited for transfer
+  // waited_gen and needs no second wait.
+  hipEvent_t ev_resolved = nullptr;
+  hipEvent_t ev_fetched = nullptr;
   uint64_t fetched_gen = 0, waited_gen = 0;
   hipStream_t fetched_on = nullptr, waited_on = nullptr;
+  bool fetched_recorded = false;
+  hipStream_t resolved_on = nullptr;
+  bool resolved_any = false, resolved_recorded = false;
   int hip_err = 0;
   int last_t = -1;
   size_t ws_bytes = 0;
@@ -42,16 +49,41 @@ struct spin_ctx {
 
 namespace {
 
-// Orders stream s after the latest transfer (see spin_ctx::fetched_gen).
+// Orders stream s after the latest transfer (see spin_ctx).
 hipError_t wait_fetched(spin_ctx* ctx, hipStream_t s) {
   if (ctx->fetched_gen == 0 || s == ctx->fetched_on) return hipSuccess;
   if (s == ctx->waited_on && ctx->waited_gen == ctx->fetched_gen) return hipSuccess;
-  const hipError_t e = hipStreamWaitEvent(s, ctx->ev_fetched, 0);
+  hipError_t e = hipSuccess;
+  if (!ctx->fetched_recorded) {
+    e = hipEventRecord(ctx->ev_fetched, ctx->fetched_on);
+    if (e != hipSuccess) return e;
+    ctx->fetched_recorded = true;
+  }
+  e = hipStreamWaitEvent(s, ctx->ev_fetched, 0);
   if (e == hipSuccess) {
     ctx->waited_on = s;
     ctx->waited_gen = ctx->fetched_gen;
   }
   return e;
+}
+
+// Orders stream s after the latest resolve.
+hipError_t wait_resolved(spin_ctx* ctx, hipStream_t s) {
+  if (!ctx->resolved_any || s == ctx->resolved_on) return hipSuccess;
+  hipError_t e = hipSuccess;
+  if (!ctx->resolved_recorded) {
+    e = hipEventRecord(ctx->ev_resolved, ctx->resolved_on);
+    if (e != hipSuccess) return e;
+    ctx->resolved_recorded = true;
+  }
+  return hipStreamWaitEvent(s, ctx->ev_resolved, 0);
+}
+
+// A transfer was just enqueued on s.
+void transfer_enqueued(spin_ctx* ctx, hipStream_t s) {
+  ++ctx->fetched_gen;
+  ctx->fetched_on = s;
+  ctx->fetched_recorded = false;
 }
 
 struct Derived {
@@ -322,7 +354,10 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
 
 SPIN_API int spin_destroy(spin_ctx* ctx) {
   if (!ctx) return SPIN_EINVAL;
-  if (ctx->fetched_gen) (void)hipEventSynchronize(ctx->ev_fetched);
+  if (ctx->fetched_gen) {
+    if (!ctx->fetched_recorded) (void)hipStreamSynchronize(ctx->fetched_on);
+    else (void)hipEventSynchronize(ctx->ev_fetched);
+  }
   if (ctx->ev_resolved) (void)hipEventDestroy(ctx->ev_resolved);
   if (ctx->ev_fetched) (void)hipEventDestroy(ctx->ev_fetched);
   delete ctx;
@@ -519,30 +554,42 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
   // pass is latency-bound and runs several times slower next to the PCIe
   // pulls (measured), so it finishes before the transfer starts.
   HIPCHK(ctx, spin::launch_segments(ctx->dev, S(stream)));
-  HIPCHK(ctx, hipEventRecord(ctx->ev_resolved, S(stream)));
+  ctx->resolved_on = S(stream);
+  ctx->resolved_any = true;
+  ctx->resolved_recorded = false;
   return SPIN_OK;
 }
 
 SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream) {
   if (!ctx) return SPIN_EINVAL;
-  HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
+  HIPCHK(ctx, wait_resolved(ctx, S(copy_stream)));
   HIPCHK(ctx, spin::launch_retrieve(ctx->dev, S(copy_stream)));
   ctx->arrival = false;
-  HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
-  ++ctx->fetched_gen;
-  ctx->fetched_on = S(copy_stream);
+  transfer_enqueued(ctx, S(copy_stream));
   return SPIN_OK;
 }
 
 SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_stream) {
   if (!ctx || !d_q || !aligned(d_q, 16)) return SPIN_EINVAL;
-  HIPCHK(ctx, hipStreamWaitEvent(S(copy_stream), ctx->ev_resolved, 0));
+  HIPCHK(ctx, wait_resolved(ctx, S(copy_stream)));
   HIPCHK(ctx, spin::launch_retrieve_attend(ctx->dev, static_cast<const uint16_t*>(d_q),
                                            S(copy_stream)));
   ctx->arrival = true;
-  HIPCHK(ctx, hipEventRecord(ctx->ev_fetched, S(copy_stream)));
-  ++ctx->fetched_gen;
-  ctx->fetched_on = S(copy_stream);
+  transfer_enqueued(ctx, S(copy_stream));
+  return SPIN_OK;
+}
+
+SPIN_API int spin_transfer_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                                  const int32_t* d_block_ntok, const int32_t* d_block_count,
+                                  void* stream) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count) return SPIN_EINVAL;
+  if (!aligned(d_q, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, wait_resolved(ctx, S(stream)));
+  const uint16_t* q = static_cast<const uint16_t*>(d_q);
+  HIPCHK(ctx, spin::launch_transfer_attend(ctx->dev, q, d_block_table, d_block_ntok, d_block_count,
+                                           S(stream)));
+  ctx->arrival = true;
+  transfer_enqueued(ctx, S(stream));
   return SPIN_OK;
 }
 
@@ -582,22 +629,40 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
   return SPIN_OK;
 }
 
-SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
-                       int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
-                       float* d_out, void* stream, void* copy_stream) {
+namespace {
+
+// One decode step.  Overlapped (copy_stream != stream) it runs the transfer,
+// attending pages on arrival, either on copy_stream beside the resident-page
+// pass on `stream` (one_launch false: measured faster with eager launches),
+// or together with that pass in one launch on `stream` (one_launch true: no
+// second stream and no event inside the step, measured faster as replays of
+// a captured graph).  Both give the same results bit for bit.
+int step_impl(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel, int32_t* d_block_table,
+              int32_t* d_block_ntok, int32_t* d_block_count, float* d_out, void* stream,
+              void* copy_stream, bool one_launch) {
   int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
   if (!rc) rc = spin_resolve_evict(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream);
   if (copy_stream == stream) {
     if (!rc) rc = spin_retrieve(ctx, copy_stream);
     if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+  } else if (one_launch) {
+    if (!rc) rc = spin_transfer_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
+    if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   } else {
-    // the transfer attends each page as it arrives, while attention over the
-    // resident pages runs on the compute stream; then one merge
     if (!rc) rc = spin_retrieve_attend(ctx, d_q, copy_stream);
     if (!rc) rc = spin_attend_begin(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
     if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   }
   return rc;
+}
+
+}  // namespace
+
+SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
+                       int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
+                       float* d_out, void* stream, void* copy_stream) {
+  return step_impl(ctx, d_q, t, d_sel, d_block_table, d_block_ntok, d_block_count, d_out, stream,
+                   copy_stream, false);
 }
 
 SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_elems,
@@ -618,8 +683,8 @@ SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_e
   }
   ctx->dev.step_t = d_t;
   ctx->dev.q_step = q_step_elems;
-  int rc = spin_step(ctx, d_q_steps, 0, d_sel, d_block_table, d_block_ntok, d_block_count, d_out,
-                     stream, copy_stream);
+  int rc = step_impl(ctx, d_q_steps, 0, d_sel, d_block_table, d_block_ntok, d_block_count, d_out,
+                     stream, copy_stream, true);
   ctx->dev.step_t = nullptr;
   ctx->dev.q_step = 0;
   if (rc) return rc;

@@ -18,6 +18,8 @@ constexpr int kMaxItems = 4096;        // Hkv * topk, mandatory partitions of on
 constexpr int kMaxPPP = 4;             // pages per partition
 constexpr int kMaxGroup = 16;          // query heads per KV head
 constexpr int kMaxKvHeads = 16;
+constexpr int kRetrieveWG = 256;       // threads of a transfer workgroup
+constexpr int kRetrieveGrid = 64;      // transfer workgroups (see retrieve.hip)
 
 // device error-word bits (kept equal to the SPIN_DEVERR_* values of spin.h)
 constexpr int kErrPartition = 1;       // selected partition id out of range
@@ -100,6 +102,10 @@ hipError_t launch_segments(const Dev& d, hipStream_t s);
 hipError_t launch_step_advance(int* t, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
 hipError_t launch_retrieve_attend(const Dev& d, const uint16_t* q, hipStream_t s);
+// the transfer with attention on arrival and the resident-page attention pass
+// in one launch (kRetrieveGrid transfer workgroups, then the attention grid)
+hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
+                                  const int* bcount, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 // mode 0: every block, finished output; 1: resident blocks only, partials;
 // 2: fetched blocks only, partials, then the merge of both passes;

@@ -20,7 +20,7 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert "one GPU only" in r.stderr
 
 
-@pytest.mark.parametrize("args", [["--warmup", "0"], ["--graph", "--no-overlap"]])
+@pytest.mark.parametrize("args", [["--warmup", "0"], ["--warmup", "-1"]])
 def test_inconsistent_options_are_refused(args):
     r = _run(*args)
     assert r.returncode == 2 and "error" in r.stderr
