@@ -308,11 +308,13 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
 /* spin_step with the step index on the device, for HIP graph capture: the
  * kernels read t from *d_t (device int32) and the step's queries at
  * d_q_steps + t * q_step_elems (bf16 elements; q_step_elems * 2 a multiple
- * of 16), and a last kernel on `stream` increments *d_t, so one captured call
- * replays as consecutive steps.  Overlapped (copy_stream != stream), the
- * transfer and the resident-page attention share one launch on `stream`
- * (spin_transfer_attend): nothing runs on copy_stream and the graph holds no
- * event; the results equal spin_step's bit for bit.  t is the caller's to keep non-decreasing.
+ * of 16), and the step's last kernel on `stream` increments *d_t, so one
+ * captured call replays as consecutive steps.  Overlapped (copy_stream !=
+ * stream), the transfer and the resident-page attention share one launch on
+ * `stream` (spin_transfer_attend), which also runs the segment-pool pass of
+ * resolve_evict in a workgroup of its own; nothing runs on copy_stream and
+ * the graph holds no event; the results (outputs, selections, the whole
+ * residency state) equal spin_step's bit for bit.  t is the caller's to keep non-decreasing.
  * Captured (stream capture active on `stream`), the call waits for no
  * transfer enqueued before the capture: the context must be idle when the
  * capture begins (synchronise the streams it used).  The captured graph holds

@@ -20,34 +20,17 @@ namespace spin {
 // already in flight meanwhile.
 //
 // Workgroup wg of nwg: pages wg, wg + nwg, ... of the batch's insert lists;
-// q already points at this step's queries.
+// q already points at this step's queries.  LDS from the caller: pm holds
+// 1025 ints, tmp kRetrieveWG / 64 + 1, page one 32 KiB page.
 __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t* __restrict__ q,
-                                                   int wg, int nwg) {
-  __shared__ int pm[1025];
-  __shared__ int tmp[5];
-  __shared__ u32x4 page[kPageBytes / 16];
+                                                   int wg, int nwg, int* pm, int* tmp,
+                                                   u32x4* page) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int G = d.G;
-  int M;
-  {
-    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
-    int loc[per], sum = 0;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      loc[u] = b < d.B ? d.nmiss[b] : 0;
-      sum += loc[u];
-    }
-    int ex = block_excl_scan<kRetrieveWG>(sum, tmp, &M);
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      if (b < d.B) pm[b] = ex;
-      ex += loc[u];
-    }
-    __syncthreads();
-  }
+  // where each request's misses start in the batch-wide concatenation of the
+  // insert lists k_resolve wrote
+  const int M = request_offsets<kRetrieveWG>(d.nmiss, d.B, pm, tmp);
   const float sl2 = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
   // a page's host address and its checks; its loads are issued one page
   // ahead, so they stay in flight while the wave attends the page before it

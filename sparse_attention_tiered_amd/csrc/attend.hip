@@ -27,6 +27,7 @@
 // to finish would need a device-scope fence per workgroup, which writes back
 // the whole L2 on this chip and cost more than the second launch.)
 #include "arrival.h"
+#include "segments.h"
 #include "attend_tile.h"
 #include "device_util.h"
 #include "spin_internal.h"
@@ -251,17 +252,29 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
 // first kRetrieveGrid workgroups pull the step's missed pages and attend each
 // on arrival, the rest attend the resident pages (partials), so the two
 // overlap without a second stream or any event between them; the merge
-// follows on the same stream.
+// follows on the same stream.  With segments set, workgroup kRetrieveGrid
+// runs the segment-pool pass (inserts too unless with_inserts is 0), which
+// nothing else in the launch reads, behind the transfer instead of before it.
 __global__ __launch_bounds__(kAttWG, 2) void k_transfer_attend(Dev d, const uint16_t* __restrict__ q,
                                                             const int* __restrict__ bt,
                                                             const int* __restrict__ bntok,
-                                                            const int* __restrict__ bcount) {
+                                                            const int* __restrict__ bcount,
+                                                            int segments, int with_inserts) {
   static_assert(kRetrieveWG == kAttWG, "one workgroup size for both roles");
+  static_assert(3 * 1025 <= kPageBytes / 4, "the segment pass borrows the page buffer");
+  __shared__ int pm[1025];
+  __shared__ int tmp[kAttWG / 64 + 1];
+  __shared__ u32x4 page[kPageBytes / 16];
   q = step_queries(d, q);
-  if ((int)blockIdx.x < kRetrieveGrid)
-    retrieve_attend_wg(d, q, blockIdx.x, kRetrieveGrid);
-  else
-    attend_wg(d, q, bt, bntok, bcount, nullptr, kAttendResident, blockIdx.x - kRetrieveGrid);
+  const int wg = blockIdx.x;
+  if (wg < kRetrieveGrid) {
+    retrieve_attend_wg(d, q, wg, kRetrieveGrid, pm, tmp, page);
+  } else if (segments && wg == kRetrieveGrid) {
+    int* lds = reinterpret_cast<int*>(page);
+    segments_wg<kAttWG>(d, with_inserts, lds, tmp);
+  } else {
+    attend_wg(d, q, bt, bntok, bcount, nullptr, kAttendResident, wg - kRetrieveGrid - segments);
+  }
 }
 
 // Log-sum-exp merge of the n_all partials of one (request, KV head), then
@@ -360,31 +373,14 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
 // splits and the partials of its pages attended on arrival (a contiguous run
 // of the batch's insert lists: this request's offset plus the head's).
 __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const int* __restrict__ bcount,
-                                                                 float* __restrict__ out) {
+                                                                 float* __restrict__ out,
+                                                                 int* __restrict__ advance) {
   __shared__ int pm[1025];
-  __shared__ int tmp[5];
+  __shared__ int tmp[kAttWG / 64 + 1];
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
-  const int tid = threadIdx.x;
-  {
-    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
-    int loc[per], sum = 0;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int rb = tid * per + u;
-      loc[u] = rb < d.B ? d.nmiss[rb] : 0;
-      sum += loc[u];
-    }
-    int tot;
-    int ex = block_excl_scan<kAttWG>(sum, tmp, &tot);
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int rb = tid * per + u;
-      if (rb < d.B) pm[rb] = ex;
-      ex += loc[u];
-    }
-    __syncthreads();
-  }
+  if (advance && bh == 0 && threadIdx.x == 0) *advance += 1;  // the next step's index
+  request_offsets<kAttWG>(d.nmiss, d.B, pm, tmp);
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
   const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
   const int nm = d.nmiss[b];
@@ -407,16 +403,19 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
 }
 
 hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                                  const int* bcount, hipStream_t s) {
-  hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s,
-                     d, q, bt, bntok, bcount);
+                                  const int* bcount, bool segments, hipStream_t s) {
+  const int seg = segments ? 1 : 0;
+  hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + seg + d.B * d.Hkv * d.splits),
+                     dim3(kAttWG), 0, s, d, q, bt, bntok, bcount, seg,
+                     segments && !segment_inserts_split(d) ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                         const int* bcount, float* out, int mode, hipStream_t s) {
+                         const int* bcount, float* out, int mode, hipStream_t s, int* advance) {
   if (mode == kAttendMergeArrival) {
-    hipLaunchKernelGGL(k_attend_merge_arrival, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out);
+    hipLaunchKernelGGL(k_attend_merge_arrival, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out,
+                       advance);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q, bt, bntok,

@@ -47,6 +47,34 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return res;
 }
 
+// Exclusive prefix sums of counts[0 .. B) into pre (LDS, B <= 1024), in
+// request order, by an NT-thread workgroup; returns the total.  tmp is LDS of
+// NT / 64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int request_offsets(const int* __restrict__ counts, int B, int* pre,
+                                               int* tmp) {
+  constexpr int per = 1024 / NT;  // max_batch <= 1024
+  static_assert(per * NT == 1024, "");
+  const int tid = threadIdx.x;
+  int loc[per], sum = 0;
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int b = tid * per + u;
+    loc[u] = b < B ? counts[b] : 0;
+    sum += loc[u];
+  }
+  int total;
+  int ex = block_excl_scan<NT>(sum, tmp, &total);
+#pragma unroll
+  for (int u = 0; u < per; ++u) {
+    const int b = tid * per + u;
+    if (b < B) pre[b] = ex;
+    ex += loc[u];
+  }
+  __syncthreads();
+  return total;
+}
+
 // Largest b in [0, nb) with prefix[b] <= j (prefix ascending, prefix[0] = 0):
 // the request that owns flat index j of a per-request concatenation.
 __device__ __forceinline__ int owner_of(const int* prefix, int nb, int j) {

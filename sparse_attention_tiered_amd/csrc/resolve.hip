@@ -22,6 +22,7 @@
 // deterministic and match a sequential walk.  k_segments is one workgroup for
 // the whole batch because the segment pool is shared.
 #include "device_util.h"
+#include "segments.h"
 #include "spin_internal.h"
 
 namespace spin {
@@ -365,126 +366,10 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   }
 }
 
-// The inserts of the step into their segments (slot entries and live
-// counts), once every segment they need is linked: items start, start +
-// stride, ... of the batch's insert lists (pm: each request's offset in it,
-// M: its length), four items' loads in flight per thread.
-__device__ void insert_segments(const Dev& d, const int* pm, int M, int start, int stride) {
-  const int ne = d.Hkv * d.ndir;
-  constexpr int U = 4;
-  for (int j0 = start; j0 < M; j0 += stride * U) {
-    int4 ms[U];
-    int bs[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + stride * u;
-      ms[u] = make_int4(-1, 0, 0, 0);
-      bs[u] = 0;
-      if (j < M) {
-        bs[u] = owner_of(pm, d.B, j);
-        ms[u] = d.ins[(size_t)bs[u] * d.max_mand + (j - pm[bs[u]])];  // (slot, h, page)
-      }
-    }
-    int segs[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      segs[u] = -1;
-      if (j0 + stride * u < M && (unsigned)ms[u].y < (unsigned)d.Hkv && ms[u].z >= 0)
-        segs[u] = d.directory[(size_t)bs[u] * ne + ms[u].y * d.ndir + (ms[u].z >> 6)];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int seg = segs[u];
-      if (j0 + stride * u < M && seg >= 0 && seg < d.n_seg) {
-        d.segments[(size_t)seg * kSegEntries + (ms[u].z & 63)] = ms[u].x;
-        atomicAdd(&d.seg_live[seg], 1);
-      }
-    }
-  }
-}
-
-// Shared segment pool, one workgroup for the batch: push every request's
-// emptied segments (requests ascending), then hand segments to the directory
-// ranges that k_resolve listed (requests ascending, canonical order);
-// k_segment_inserts then writes the inserts into their segments.  Each phase is a flat loop over the
-// batch; a request is found from a flat index by binary search over the
-// per-request prefix sums kept in LDS.  The retrieve does not wait for this
-// pass: it reads the insert lists k_resolve wrote.
-
 __global__ __launch_bounds__(1024) void k_segments(Dev d, int with_inserts) {
-  __shared__ int pf[1025], pa[1025], pm[1025];
-  __shared__ int tmp[17];
-  const int tid = threadIdx.x;
-  const int ne = d.Hkv * d.ndir;
-  const int B = d.B;
-  int F, A, M;
-  {
-    const int nf = tid < B ? d.nfreed[tid] : 0;
-    const int na = tid < B ? d.nalloc[tid] : 0;
-    const int nm = tid < B ? d.nmiss[tid] : 0;
-    const int xf = block_excl_scan<1024>(nf, tmp, &F);
-    const int xa = block_excl_scan<1024>(na, tmp, &A);
-    const int xm = block_excl_scan<1024>(nm, tmp, &M);
-    if (tid < B) {
-      pf[tid] = xf;
-      pa[tid] = xa;
-      pm[tid] = xm;
-    }
-    __syncthreads();
-  }
-  // each loop below issues the loads of U iterations before using any, so a
-  // thread waits for one round trip per U items rather than one per item
-  constexpr int U = 8;
-  const int top0 = d.seg_ctl[0];
-  for (int j0 = tid; j0 < F; j0 += 1024 * U) {
-    int fs[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 1024 * u;
-      fs[u] = -1;
-      if (j < F) {
-        const int b = owner_of(pf, B, j);
-        fs[u] = d.freed[(size_t)b * ne + (j - pf[b])];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 1024 * u;
-      if (j >= F) break;
-      const int at = top0 + j;
-      if (at < d.n_seg) d.seg_stack[at] = fs[u];
-      else atomicOr(d.err, kErrState);
-    }
-  }
-  const int top1 = min(top0 + F, d.n_seg);
-  __syncthreads();
-  for (int j0 = tid; j0 < A; j0 += 1024 * U) {
-    int es[U], ss[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 1024 * u;
-      es[u] = -1;
-      ss[u] = -1;
-      if (j < A) {
-        const int b = owner_of(pa, B, j);
-        es[u] = b * ne + d.alloc[(size_t)b * ne + (j - pa[b])];
-        const int idx = top1 - 1 - j;
-        if (idx >= 0) ss[u] = d.seg_stack[idx];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + 1024 * u;
-      if (j >= A) break;
-      if (top1 - 1 - j >= 0) d.directory[es[u]] = ss[u];
-      else atomicOr(d.err, kErrSegPool);
-    }
-  }
-  if (tid == 0) d.seg_ctl[0] = max(top1 - A, 0);
-  if (with_inserts) {
-    __syncthreads();
-    insert_segments(d, pm, M, tid, 1024);
-  }
+  __shared__ int lds[3 * 1025];
+  __shared__ int tmp[1024 / 64 + 1];
+  segments_wg<1024>(d, with_inserts, lds, tmp);
 }
 
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
@@ -504,43 +389,28 @@ hipError_t launch_step_advance(int* t, hipStream_t s) {
 
 // Large batches write the inserts with many workgroups (one workgroup would
 // be bound by its own CU's scattered accesses: 23 -> 12 us for 4.7K inserts),
-// small ones inside k_segments (a second launch would cost more).
+// small ones inside the segment-pool pass (a second launch would cost more);
+// segment_inserts_split() decides.
 constexpr int kInsertWG = 256, kInsertGrid = 64;
-constexpr long long kInsertSplitMin = 8192;  // B * max pages per step above which
 
 __global__ __launch_bounds__(kInsertWG) void k_segment_inserts(Dev d) {
   __shared__ int pm[1025];
   __shared__ int tmp[kInsertWG / 64 + 1];
-  const int tid = threadIdx.x;
-  int M;
-  {
-    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
-    int loc[per], sum = 0;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      loc[u] = b < d.B ? d.nmiss[b] : 0;
-      sum += loc[u];
-    }
-    int ex = block_excl_scan<kInsertWG>(sum, tmp, &M);
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      if (b < d.B) pm[b] = ex;
-      ex += loc[u];
-    }
-    __syncthreads();
-  }
-  insert_segments(d, pm, M, blockIdx.x * kInsertWG + tid, kInsertGrid * kInsertWG);
+  const int M = request_offsets<kInsertWG>(d.nmiss, d.B, pm, tmp);
+  insert_segments(d, pm, M, blockIdx.x * kInsertWG + threadIdx.x, kInsertGrid * kInsertWG);
+}
+
+hipError_t launch_segment_inserts(const Dev& d, hipStream_t s) {
+  hipLaunchKernelGGL(k_segment_inserts, dim3(kInsertGrid), dim3(kInsertWG), 0, s, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_segments(const Dev& d, hipStream_t s) {
-  const bool split = (long long)d.B * d.max_mand > kInsertSplitMin;
+  const bool split = segment_inserts_split(d);
   hipLaunchKernelGGL(k_segments, dim3(1), dim3(1024), 0, s, d, split ? 0 : 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  hipLaunchKernelGGL(k_segment_inserts, dim3(kInsertGrid), dim3(kInsertWG), 0, s, d);
-  return hipGetLastError();
+  return launch_segment_inserts(d, s);
 }
 
 }  // namespace spin

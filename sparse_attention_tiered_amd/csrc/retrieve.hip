@@ -67,7 +67,10 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
 }
 
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const uint16_t* __restrict__ q) {
-  retrieve_attend_wg(d, step_queries(d, q), blockIdx.x, gridDim.x);
+  __shared__ int pm[1025];
+  __shared__ int tmp[kRetrieveWG / 64 + 1];
+  __shared__ u32x4 page[kPageBytes / 16];
+  retrieve_attend_wg(d, step_queries(d, q), blockIdx.x, gridDim.x, pm, tmp, page);
 }
 
 hipError_t launch_retrieve_attend(const Dev& d, const uint16_t* q, hipStream_t s) {

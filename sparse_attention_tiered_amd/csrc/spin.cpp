@@ -538,9 +538,12 @@ SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* 
   return SPIN_OK;
 }
 
-SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
-                                int32_t* d_block_table, int32_t* d_block_ntok,
-                                int32_t* d_block_count, void* stream) {
+namespace {
+
+// Resolve/evict; segments false leaves the segment-pool pass to the
+// transfer launch that follows on the same stream (the one-launch step).
+int resolve_impl(spin_ctx* ctx, const int32_t* d_sel, int32_t t, int32_t* d_block_table,
+                 int32_t* d_block_ntok, int32_t* d_block_count, void* stream, bool segments) {
   if (!ctx || !d_sel || !d_block_table || !d_block_ntok || !d_block_count || t < 0) return SPIN_EINVAL;
   if (!ctx->dev.step_t) {  // a device-side step index is checked by nobody but its owner
     if (t < ctx->last_t) return SPIN_EINVAL;
@@ -552,12 +555,52 @@ SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
                                    S(stream)));
   // The transfer needs only k_resolve's insert lists, but the segment-pool
   // pass is latency-bound and runs several times slower next to the PCIe
-  // pulls (measured), so it finishes before the transfer starts.
-  HIPCHK(ctx, spin::launch_segments(ctx->dev, S(stream)));
+  // pulls (measured), so on its own stream it finishes before the transfer
+  // starts; inside the one-launch transfer it runs in a workgroup of its own,
+  // where its time is hidden.
+  if (segments) HIPCHK(ctx, spin::launch_segments(ctx->dev, S(stream)));
   ctx->resolved_on = S(stream);
   ctx->resolved_any = true;
   ctx->resolved_recorded = false;
   return SPIN_OK;
+}
+
+int transfer_attend_impl(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                         const int32_t* d_block_ntok, const int32_t* d_block_count, void* stream,
+                         bool segments) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count) return SPIN_EINVAL;
+  if (!aligned(d_q, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, wait_resolved(ctx, S(stream)));
+  const uint16_t* q = static_cast<const uint16_t*>(d_q);
+  HIPCHK(ctx, spin::launch_transfer_attend(ctx->dev, q, d_block_table, d_block_ntok, d_block_count,
+                                           segments, S(stream)));
+  if (segments && spin::segment_inserts_split(ctx->dev))
+    HIPCHK(ctx, spin::launch_segment_inserts(ctx->dev, S(stream)));
+  ctx->arrival = true;
+  transfer_enqueued(ctx, S(stream));
+  return SPIN_OK;
+}
+
+int attend_finish_impl(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
+                       const int32_t* d_block_ntok, const int32_t* d_block_count, float* d_out,
+                       void* stream, int32_t* advance) {
+  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
+  if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
+  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
+  // pages attended on arrival need only the merge; otherwise attend them now
+  HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
+                                  d_block_ntok, d_block_count, d_out,
+                                  ctx->arrival ? spin::kAttendMergeArrival : spin::kAttendFetched,
+                                  S(stream), ctx->arrival ? advance : nullptr));
+  return SPIN_OK;
+}
+
+}  // namespace
+
+SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
+                                int32_t* d_block_table, int32_t* d_block_ntok,
+                                int32_t* d_block_count, void* stream) {
+  return resolve_impl(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream, true);
 }
 
 SPIN_API int spin_retrieve(spin_ctx* ctx, void* copy_stream) {
@@ -582,15 +625,7 @@ SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_str
 SPIN_API int spin_transfer_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
                                   const int32_t* d_block_ntok, const int32_t* d_block_count,
                                   void* stream) {
-  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count) return SPIN_EINVAL;
-  if (!aligned(d_q, 16)) return SPIN_EINVAL;
-  HIPCHK(ctx, wait_resolved(ctx, S(stream)));
-  const uint16_t* q = static_cast<const uint16_t*>(d_q);
-  HIPCHK(ctx, spin::launch_transfer_attend(ctx->dev, q, d_block_table, d_block_ntok, d_block_count,
-                                           S(stream)));
-  ctx->arrival = true;
-  transfer_enqueued(ctx, S(stream));
-  return SPIN_OK;
+  return transfer_attend_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream, false);
 }
 
 SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
@@ -618,15 +653,8 @@ SPIN_API int spin_attend_begin(spin_ctx* ctx, const void* d_q, const int32_t* d_
 SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
                                 const int32_t* d_block_ntok, const int32_t* d_block_count,
                                 float* d_out, void* stream) {
-  if (!ctx || !d_q || !d_block_table || !d_block_ntok || !d_block_count || !d_out) return SPIN_EINVAL;
-  if (!aligned(d_q, 16) || !aligned(d_out, 16)) return SPIN_EINVAL;
-  HIPCHK(ctx, wait_fetched(ctx, S(stream)));
-  // pages attended on arrival need only the merge; otherwise attend them now
-  HIPCHK(ctx, spin::launch_attend(ctx->dev, static_cast<const uint16_t*>(d_q), d_block_table,
-                                  d_block_ntok, d_block_count, d_out,
-                                  ctx->arrival ? spin::kAttendMergeArrival : spin::kAttendFetched,
-                                  S(stream)));
-  return SPIN_OK;
+  return attend_finish_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream,
+                            nullptr);
 }
 
 namespace {
@@ -636,18 +664,31 @@ namespace {
 // pass on `stream` (one_launch false: measured faster with eager launches),
 // or together with that pass in one launch on `stream` (one_launch true: no
 // second stream and no event inside the step, measured faster as replays of
-// a captured graph).  Both give the same results bit for bit.
+// a captured graph; the segment-pool pass then runs inside the transfer
+// launch, and a non-null advance (the device-side step index) is incremented
+// by the merge, *advanced telling the caller so).  Both give the same results
+// bit for bit.
 int step_impl(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel, int32_t* d_block_table,
               int32_t* d_block_ntok, int32_t* d_block_count, float* d_out, void* stream,
-              void* copy_stream, bool one_launch) {
+              void* copy_stream, bool one_launch, int32_t* advance = nullptr,
+              bool* advanced = nullptr) {
+  const bool fused = copy_stream != stream && one_launch;
   int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
-  if (!rc) rc = spin_resolve_evict(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream);
+  if (!rc)
+    rc = resolve_impl(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream, !fused);
   if (copy_stream == stream) {
     if (!rc) rc = spin_retrieve(ctx, copy_stream);
     if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
   } else if (one_launch) {
-    if (!rc) rc = spin_transfer_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
-    if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+    // the arguments were all checked by the calls above, so the deferred
+    // segment pass cannot be skipped by an argument error here
+    if (!rc)
+      rc = transfer_attend_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream, true);
+    if (!rc) {
+      rc = attend_finish_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream,
+                              advance);
+      if (!rc && advanced) *advanced = advance != nullptr;
+    }
   } else {
     if (!rc) rc = spin_retrieve_attend(ctx, d_q, copy_stream);
     if (!rc) rc = spin_attend_begin(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
@@ -683,12 +724,13 @@ SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_e
   }
   ctx->dev.step_t = d_t;
   ctx->dev.q_step = q_step_elems;
+  bool advanced = false;
   int rc = step_impl(ctx, d_q_steps, 0, d_sel, d_block_table, d_block_ntok, d_block_count, d_out,
-                     stream, copy_stream, true);
+                     stream, copy_stream, true, d_t, &advanced);
   ctx->dev.step_t = nullptr;
   ctx->dev.q_step = 0;
   if (rc) return rc;
-  HIPCHK(ctx, spin::launch_step_advance(d_t, S(stream)));
+  if (!advanced) HIPCHK(ctx, spin::launch_step_advance(d_t, S(stream)));
   return SPIN_OK;
 }
 

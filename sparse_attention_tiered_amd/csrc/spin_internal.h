@@ -98,21 +98,30 @@ hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, i
 constexpr int kFusedSelectMinLists = 128;
 hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bntok, int* bcount,
                           hipStream_t s);
+// the segment-pool pass; large batches write the inserts in a second launch
 hipError_t launch_segments(const Dev& d, hipStream_t s);
+hipError_t launch_segment_inserts(const Dev& d, hipStream_t s);
+// more pages a step than one workgroup inserts quickly: k_segment_inserts
+inline bool segment_inserts_split(const Dev& d) { return (long long)d.B * d.max_mand > 8192; }
 hipError_t launch_step_advance(int* t, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
 hipError_t launch_retrieve_attend(const Dev& d, const uint16_t* q, hipStream_t s);
 // the transfer with attention on arrival and the resident-page attention pass
-// in one launch (kRetrieveGrid transfer workgroups, then the attention grid)
+// in one launch (kRetrieveGrid transfer workgroups, then the attention grid);
+// with segments, one more workgroup runs the segment-pool pass (and the
+// inserts unless segment_inserts_split)
 hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                                  const int* bcount, hipStream_t s);
+                                  const int* bcount, bool segments, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);
 // mode 0: every block, finished output; 1: resident blocks only, partials;
 // 2: fetched blocks only, partials, then the merge of both passes;
 // 3: no attention, only the merge of the resident-block partials with the
-// fetched pages attended on arrival (launch_retrieve_attend)
+// fetched pages attended on arrival (launch_retrieve_attend); in that mode a
+// non-null advance is incremented once the kernel is done with the step
+// (nothing in it reads the device-side step index)
 enum AttendMode { kAttendAll = 0, kAttendResident = 1, kAttendFetched = 2, kAttendMergeArrival = 3 };
 hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
-                         const int* bcount, float* out, int mode, hipStream_t s);
+                         const int* bcount, float* out, int mode, hipStream_t s,
+                         int* advance = nullptr);
 
 }  // namespace spin

@@ -214,5 +214,75 @@ class Pair:
             f"evictions={st.evictions} tie-flips={total_flips} max|out-oracle|={worst:.2e}")
         return st, worst
 
+    def valid_selection(self, t, sel_gpu):
+        """The GPU's selection, checked against the oracle's: the same sets
+        except partitions whose scores tie the k-th within TIE_WINDOW, ascending,
+        -1 padded.  Returns the number of (request, head) lists that differ."""
+        sel_o, sc_o = self.oracle.select(self.draws.q_bits[t])
+        k = self.w.k
+        flips = 0
+        for b in range(self.w.B):
+            n = self.n_parts(b)
+            for h in range(self.w.Hkv):
+                g, o = sel_gpu[b, h], sel_o[b, h]
+                m = min(k, n)
+                assert np.all(g[m:] == -1) and np.all(o[m:] == -1)
+                assert np.all(np.diff(g[:m]) > 0), ("GPU selection not ascending", b, h)
+                if set(g[:m]) != set(o[:m]):
+                    kth = np.sort(sc_o[b][h])[::-1][k - 1]
+                    for p in set(g[:m]) ^ set(o[:m]):
+                        assert 0 <= p < n and abs(sc_o[b][h][p] - kth) <= TIE_WINDOW, (
+                            f"step {t} b{b} h{h}: partition {p} vs k-th {kth}")
+                    flips += 1
+        return flips
+
+    def run_graph(self, steps, out_sample, seed=0):
+        """The benchmark's timed configuration: one spin_step_at call (the
+        transfer and the resident-page attention in one launch, the step index
+        on the device) captured in a HIP graph and replayed once per step.
+        Each step the oracle takes the GPU's selection once it is shown valid,
+        then the whole residency state, the block tables and sampled outputs
+        are compared."""
+        rng = np.random.default_rng(seed)
+        S, C = torch.cuda.Stream(), torch.cuda.Stream()
+        t_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        graph = None
+        flips_total, worst = 0, 0.0
+        for t in range(steps):
+            if t == 0:  # eagerly, then capture the step once
+                self.spin.step_at(self.q_dev, t_dev, stream=S, copy_stream=C)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=S):
+                    self.spin.step_at(self.q_dev, t_dev, stream=S, copy_stream=C)
+                torch.cuda.synchronize()
+                assert int(t_dev.item()) == 1
+            else:
+                with torch.cuda.stream(S):
+                    graph.replay()
+                torch.cuda.synchronize()
+                assert int(t_dev.item()) == t + 1
+            sel_gpu = self.spin.sel.cpu().numpy()
+            flips_total += self.valid_selection(t, sel_gpu)
+            blocks = self.oracle.resolve_evict(sel_gpu.astype(np.int64), t)
+            self.check_state(t)
+            self.check_blocks(t, blocks)
+            self.oracle.retrieve()
+            out = self.spin.out.cpu().numpy()
+            qb = self.draws.q_bits[t]
+            err = 0.0
+            for _ in range(out_sample):
+                b = int(rng.integers(self.w.B))
+                g = int(rng.integers(self.w.Hq))
+                want = self.oracle.attend_one(qb, b, g, blocks)
+                err = max(err, float(np.max(np.abs(out[b, g] - want))))
+            worst = max(worst, err)
+            assert err <= OUT_TOL, (t, err)
+        st = self.check_stats()
+        log(f"[parity] {self.w.name} graph: {steps} steps, hits={st.hits} misses={st.misses} "
+            f"evictions={st.evictions} tie-flips={flips_total} max|out-oracle|={worst:.2e}")
+        return st, worst
+
     def close(self):
         self.spin.close()

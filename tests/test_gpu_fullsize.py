@@ -22,3 +22,19 @@ def test_full_size(spin_lib, name):
     st, worst = p.run(steps=steps, out_sample=24)
     assert st.misses > 0
     p.close()
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_full_size_graph_replays(spin_lib, name):
+    """The timed configuration of the benchmark (graph replays of the
+    device-indexed step, transfer and attention in one launch, the segment
+    pass inside it; c4 also writes its inserts in a separate launch) against
+    the oracle at full size."""
+    from tests.gpu_harness import Pair, log
+    w = W.get(name)
+    steps = 6
+    log(f"[case] full-size graph replays {w.name}: {steps} steps")
+    p = Pair(w, n_steps=steps)
+    st, worst = p.run_graph(steps=steps, out_sample=24)
+    assert st.misses > 0
+    p.close()
