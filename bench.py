@@ -324,6 +324,17 @@ def main():
     torch.cuda.synchronize()
     iso_select_ms = iso[0].elapsed_time(iso[1]) / reps
     iso_attend_ms = iso[2].elapsed_time(iso[3]) / reps
+    # the last step's transfer again, alone on the compute stream: the same
+    # pages to the same slots (idempotent), no attention beside it, so the
+    # rate is the transfer's own for this many pages
+    iso_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    spin.retrieve(copy_stream=S)  # untimed: the kernel's first launch in the process loads it
+    iso_r[0].record(S)
+    for _ in range(reps):
+        spin.retrieve(copy_stream=S)
+    iso_r[1].record(S)
+    torch.cuda.synchronize()
+    iso_retrieve_ms = iso_r[0].elapsed_time(iso_r[1]) / reps
     # cold replays: a 512 MB read before each one fills the 256 MB memory-side
     # cache with clean lines of another buffer, so the kernel reads HBM (a write
     # would leave dirty lines whose write-back the kernel would pay for); an
@@ -362,6 +373,7 @@ def main():
     score_bytes = w.Hkv * n_parts * 128 * 4 + w.B * w.Hq * 128 * 2 + w.Hkv * n_parts * 4
     # the transfer's bytes per launch in the instrumented pass it is timed in
     retrieve_bytes = (st2.misses - st1.misses) * PAGE_BYTES / K
+    last_step_bytes = step_miss[-1] * PAGE_BYTES
     # everything the transfer launch itself reads and writes: each missed page
     # read over the link and written to its slot; with the overlap, also the
     # resident pages it attends (read once) and the queries
@@ -398,6 +410,10 @@ def main():
         sum(step_miss[i] for i in big) * PAGE_BYTES / (sum(ret_ms[i] for i in big) * 1e-3) / 1e9
         if big else None)
     rl["retrieve"]["step0"] = step0
+    rl["retrieve"]["isolated_last_step"] = {
+        "kernel": "k_retrieve", "bytes": last_step_bytes, "launch_ms": iso_retrieve_ms,
+        "achieved": last_step_bytes / (iso_retrieve_ms * 1e-3) / 1e9 if last_step_bytes else 0.0,
+        "frac": last_step_bytes / (iso_retrieve_ms * 1e-3) / 1e9 / PCIE_GEN5_X16_GBS if last_step_bytes else 0.0}
     rl["attend"]["cold"] = {"launch_ms": cold_attend_ms,
                             "achieved": iso_attend_bytes / (cold_attend_ms * 1e-3) / 1e9}
     rl["select"]["cold"] = {"launch_ms": cold_select_ms,

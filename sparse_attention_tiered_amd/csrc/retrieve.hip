@@ -5,8 +5,7 @@
 //
 // The GPU pulls the pages itself: each workgroup reads whole 32 KiB pages
 // through the host buffer's device-mapped address with 16-byte loads per lane
-// (eight loads in flight per lane, the full page per workgroup) and writes
-// them to HBM.  The host never reads the miss count: the grid is fixed and
+// (two pages, sixteen loads, in flight per lane) and writes them to HBM.  The host never reads the miss count: the grid is fixed and
 // every workgroup strides over the batch's insert lists, which k_resolve
 // writes, so the transfer does not wait for the segment-pool pass.
 #include "arrival.h"
@@ -16,7 +15,7 @@
 namespace spin {
 
 // A few dozen workgroups keep far more than the link's bandwidth-delay product
-// in flight (eight 16 B loads per lane, 32 KiB per workgroup); measured on
+// in flight (sixteen 16 B loads per lane, 64 KiB per workgroup); measured on
 // MI355X, 16-128 workgroups pull 56.5-57.4 GB/s of scattered pages, as fast as
 // a bulk DMA copy, while 256+ workgroups drop to 55 GB/s.  A small grid also
 // leaves the other CUs to the attention pass that overlaps the transfer.
@@ -26,43 +25,45 @@ namespace spin {
 
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
   __shared__ int pm[1025];
-  __shared__ int tmp[5];
+  __shared__ int tmp[kRetrieveWG / 64 + 1];
   const int tid = threadIdx.x;
   // where each request's misses start in the batch-wide concatenation of the
   // insert lists k_resolve wrote (requests ascending, canonical order)
-  int M;
-  {
-    constexpr int per = 4;  // max_batch <= 1024 = 256 threads x 4
-    int loc[per], sum = 0;
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      loc[u] = b < d.B ? d.nmiss[b] : 0;
-      sum += loc[u];
-    }
-    int ex = block_excl_scan<kRetrieveWG>(sum, tmp, &M);
-#pragma unroll
-    for (int u = 0; u < per; ++u) {
-      const int b = tid * per + u;
-      if (b < d.B) pm[b] = ex;
-      ex += loc[u];
-    }
-    __syncthreads();
-  }
-  for (int j = blockIdx.x; j < M; j += gridDim.x) {
+  const int M = request_offsets<kRetrieveWG>(d.nmiss, d.B, pm, tmp);
+  // a page's source and destination, or null when its entry is out of range
+  auto page = [&](int j, const u32x4*& src, u32x4*& dst) {
+    src = nullptr;
+    dst = nullptr;
+    if (j >= M) return;
     const int b = owner_of(pm, d.B, j);
     const int4 m = d.ins[(size_t)b * d.max_mand + (j - pm[b])];  // (slot, KV head, page)
     if ((unsigned)m.x >= (unsigned)d.C || (unsigned)m.y >= (unsigned)d.Hkv ||
         (unsigned)m.z >= (unsigned)d.req_pages[b])
-      continue;
-    const u32x4* src = reinterpret_cast<const u32x4*>(
-        d.host_base[b] + ((size_t)m.y * d.req_stride[b] + m.z) * (size_t)kPageBytes);
-    u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)b * d.C + m.x) * kPageElems);
-    u32x4 v[8];
+      return;
+    src = reinterpret_cast<const u32x4*>(d.host_base[b] +
+                                         ((size_t)m.y * d.req_stride[b] + m.z) * (size_t)kPageBytes);
+    dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)b * d.C + m.x) * kPageElems);
+  };
+  // two pages in flight per workgroup (pages j and j + grid), 64 KiB
+  const int nwg = gridDim.x;
+  for (int j = blockIdx.x; j < M; j += 2 * nwg) {
+    const u32x4 *s0, *s1;
+    u32x4 *d0, *d1;
+    page(j, s0, d0);
+    page(j + nwg, s1, d1);
+    u32x4 v[8], w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[u * kRetrieveWG + tid];
+    for (int u = 0; u < 8; ++u)
+      if (s0) v[u] = s0[u * kRetrieveWG + tid];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) __builtin_nontemporal_store(v[u], dst + u * kRetrieveWG + tid);
+    for (int u = 0; u < 8; ++u)
+      if (s1) w[u] = s1[u * kRetrieveWG + tid];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (d0) __builtin_nontemporal_store(v[u], d0 + u * kRetrieveWG + tid);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (d1) __builtin_nontemporal_store(w[u], d1 + u * kRetrieveWG + tid);
   }
 }
 

@@ -322,6 +322,35 @@ def test_max_batch(spin_lib):
     p.close()
 
 
+@pytest.mark.parametrize("name,host", [("c4_pressure", False), ("c4_pressure", True),
+                                       ("churn", False), ("c5_variable", True)],
+                         ids=["c4_pressure", "c4_pressure-host_segments", "churn",
+                              "c5_variable-host_segments"])
+def test_graph_replays_match_oracle(spin_lib, name, host):
+    """Graph replays of the device-indexed step (transfer, resident-page
+    attention and the segment-pool pass in one launch; the merge advances
+    the step index) against the oracle every step: selection, the whole
+    residency state, block tables, every output; with the segment tables in
+    GPU or in host memory."""
+    w, kw = SMALL[name]
+    p = _pair(w, host_segments=host, **kw)
+    st, _ = p.run_graph()
+    assert st.evictions > 0
+    p.close()
+
+
+def test_max_batch_graph_replays(spin_lib):
+    """The batch limit through the one-launch step: the segment-pool pass in a
+    256-thread workgroup takes the per-request prefix sums of 1024 requests."""
+    ctx = tuple(64 * 3 - (b % 7) * 20 for b in range(1024))
+    w = W.variant(W.C1, name="max_batch_graph", B=1024, Hq=4, Hkv=2, ctx=ctx, k=2, steps=4,
+                  ar_coef=0.2)
+    p = _pair(w, slots=2 * 2 + 1)
+    st, _ = p.run_graph()
+    assert st.misses > 0 and st.evictions > 0
+    p.close()
+
+
 def test_streams_change_between_steps(spin_lib):
     """The whole-step call with the stream roles moving every step (this
     step's copy stream computes the next one) matches the oracle, and is
