@@ -253,13 +253,15 @@ __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __r
 // on arrival, the rest attend the resident pages (partials), so the two
 // overlap without a second stream or any event between them; the merge
 // follows on the same stream.  With segments set, workgroup kRetrieveGrid
-// runs the segment-pool pass (inserts too unless with_inserts is 0), which
-// nothing else in the launch reads, behind the transfer instead of before it.
+// runs the segment-pool pass and the inserts, which nothing else in the
+// launch reads, behind the transfer instead of before it: every insert is a
+// page this launch pulls (about 0.6 us of the link each), against a few
+// hundredths of a microsecond per insert for the one workgroup.
 __global__ __launch_bounds__(kAttWG, 2) void k_transfer_attend(Dev d, const uint16_t* __restrict__ q,
                                                             const int* __restrict__ bt,
                                                             const int* __restrict__ bntok,
                                                             const int* __restrict__ bcount,
-                                                            int segments, int with_inserts) {
+                                                            int segments) {
   static_assert(kRetrieveWG == kAttWG, "one workgroup size for both roles");
   static_assert(3 * 1025 <= kPageBytes / 4, "the segment pass borrows the page buffer");
   __shared__ int pm[1025];
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kAttWG, 2) void k_transfer_attend(Dev d, const uint
     retrieve_attend_wg(d, q, wg, kRetrieveGrid, pm, tmp, page);
   } else if (segments && wg == kRetrieveGrid) {
     int* lds = reinterpret_cast<int*>(page);
-    segments_wg<kAttWG>(d, with_inserts, lds, tmp);
+    segments_wg<kAttWG>(d, 1, lds, tmp);
   } else {
     attend_wg(d, q, bt, bntok, bcount, nullptr, kAttendResident, wg - kRetrieveGrid - segments);
   }
@@ -406,8 +408,7 @@ hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt
                                   const int* bcount, bool segments, hipStream_t s) {
   const int seg = segments ? 1 : 0;
   hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + seg + d.B * d.Hkv * d.splits),
-                     dim3(kAttWG), 0, s, d, q, bt, bntok, bcount, seg,
-                     segments && !segment_inserts_split(d) ? 1 : 0);
+                     dim3(kAttWG), 0, s, d, q, bt, bntok, bcount, seg);
   return hipGetLastError();
 }
 

@@ -389,9 +389,9 @@ hipError_t launch_step_advance(int* t, hipStream_t s) {
 
 // Large batches write the inserts with many workgroups (one workgroup would
 // be bound by its own CU's scattered accesses: 23 -> 12 us for 4.7K inserts),
-// small ones inside the segment-pool pass (a second launch would cost more);
-// segment_inserts_split() decides.
+// small ones inside the segment-pool pass (a second launch would cost more).
 constexpr int kInsertWG = 256, kInsertGrid = 64;
+constexpr long long kInsertSplitMin = 8192;  // B * max pages per step above which
 
 __global__ __launch_bounds__(kInsertWG) void k_segment_inserts(Dev d) {
   __shared__ int pm[1025];
@@ -400,17 +400,13 @@ __global__ __launch_bounds__(kInsertWG) void k_segment_inserts(Dev d) {
   insert_segments(d, pm, M, blockIdx.x * kInsertWG + threadIdx.x, kInsertGrid * kInsertWG);
 }
 
-hipError_t launch_segment_inserts(const Dev& d, hipStream_t s) {
-  hipLaunchKernelGGL(k_segment_inserts, dim3(kInsertGrid), dim3(kInsertWG), 0, s, d);
-  return hipGetLastError();
-}
-
 hipError_t launch_segments(const Dev& d, hipStream_t s) {
-  const bool split = segment_inserts_split(d);
+  const bool split = (long long)d.B * d.max_mand > kInsertSplitMin;
   hipLaunchKernelGGL(k_segments, dim3(1), dim3(1024), 0, s, d, split ? 0 : 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !split) return e;
-  return launch_segment_inserts(d, s);
+  hipLaunchKernelGGL(k_segment_inserts, dim3(kInsertGrid), dim3(kInsertWG), 0, s, d);
+  return hipGetLastError();
 }
 
 }  // namespace spin

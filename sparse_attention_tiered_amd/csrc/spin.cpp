@@ -574,8 +574,6 @@ int transfer_attend_impl(spin_ctx* ctx, const void* d_q, const int32_t* d_block_
   const uint16_t* q = static_cast<const uint16_t*>(d_q);
   HIPCHK(ctx, spin::launch_transfer_attend(ctx->dev, q, d_block_table, d_block_ntok, d_block_count,
                                            segments, S(stream)));
-  if (segments && spin::segment_inserts_split(ctx->dev))
-    HIPCHK(ctx, spin::launch_segment_inserts(ctx->dev, S(stream)));
   ctx->arrival = true;
   transfer_enqueued(ctx, S(stream));
   return SPIN_OK;

@@ -100,16 +100,13 @@ hipError_t launch_resolve(const Dev& d, const int* sel, int t, int* bt, int* bnt
                           hipStream_t s);
 // the segment-pool pass; large batches write the inserts in a second launch
 hipError_t launch_segments(const Dev& d, hipStream_t s);
-hipError_t launch_segment_inserts(const Dev& d, hipStream_t s);
-// more pages a step than one workgroup inserts quickly: k_segment_inserts
-inline bool segment_inserts_split(const Dev& d) { return (long long)d.B * d.max_mand > 8192; }
 hipError_t launch_step_advance(int* t, hipStream_t s);
 hipError_t launch_retrieve(const Dev& d, hipStream_t s);
 hipError_t launch_retrieve_attend(const Dev& d, const uint16_t* q, hipStream_t s);
 // the transfer with attention on arrival and the resident-page attention pass
 // in one launch (kRetrieveGrid transfer workgroups, then the attention grid);
-// with segments, one more workgroup runs the segment-pool pass (and the
-// inserts unless segment_inserts_split)
+// with segments, one more workgroup runs the segment-pool pass and the
+// inserts
 hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
                                   const int* bcount, bool segments, hipStream_t s);
 hipError_t launch_read_stream(const void* buf, size_t bytes, unsigned* sink, hipStream_t s);

@@ -28,8 +28,8 @@ def test_full_size(spin_lib, name):
 def test_full_size_graph_replays(spin_lib, name):
     """The timed configuration of the benchmark (graph replays of the
     device-indexed step, transfer and attention in one launch, the segment
-    pass inside it; c4 also writes its inserts in a separate launch) against
-    the oracle at full size."""
+    pass and the inserts inside it in one workgroup: 4.7K inserts a step on
+    c4) against the oracle at full size."""
     from tests.gpu_harness import Pair, log
     w = W.get(name)
     steps = 6
