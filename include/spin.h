@@ -54,9 +54,11 @@
  * (compute stream, copy stream) pair.  Streams are hipStream_t values passed
  * as void* (NULL = the null stream).  resolve_evict, attention and every call
  * that changes a request (index, offload, append, release) wait for the
- * latest spin_retrieve; the context remembers which stream already waited for
- * it and does not wait there twice, so a stream given to a context must not
- * be destroyed (and its handle reused) before the context is.
+ * latest transfer (spin_retrieve, spin_retrieve_attend or
+ * spin_transfer_attend); the context records an event only when another
+ * stream has to wait, remembers which stream already waited for that
+ * transfer and does not wait there twice, so a stream given to a context
+ * must not be destroyed (and its handle reused) before the context is.
  */
 #ifndef SPIN_H
 #define SPIN_H
@@ -169,8 +171,8 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_workspace, size_t ws
                             void* d_pool, size_t pool_bytes, void* h_segments,
                             size_t h_segment_bytes, void* stream, spin_ctx** out);
 
-/* Waits for the latest spin_retrieve, then frees the context (not the
- * caller's memory). */
+/* Waits for the latest transfer, then frees the context (not the caller's
+ * memory). */
 SPIN_API int spin_destroy(spin_ctx* ctx);
 
 /* Index + Offload registration of request `req` ([XT] part 1, Fig. 3; [GP] A).
@@ -263,7 +265,7 @@ SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_str
 /* Attention ([XT] part 1, Fig. 3) over the block-table pages:
  * out[b][g] = softmax(q[b][g] . K^T / sqrt(128)) V over the valid tokens of
  * the pages of KV head g / G, bf16 inputs, float32 accumulation.  A head with
- * no pages yields zeros.  Waits for the last spin_retrieve. */
+ * no pages yields zeros.  Waits for the latest transfer. */
 SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
                          const int32_t* d_block_ntok, const int32_t* d_block_count,
                          float* d_out, void* stream);
