@@ -298,11 +298,13 @@ SPIN_API int spin_transfer_attend(spin_ctx* ctx, const void* d_q, const int32_t*
                                   void* stream);
 
 /* One whole decode step: select, resolve_evict, then Retrieve and
- * Attention.  When copy_stream differs from stream the two overlap: the
- * transfer attends its pages on arrival on copy_stream (spin_retrieve_attend)
- * while `stream` attends the resident pages (spin_attend_begin), then
- * spin_attend_finish merges; when they are equal it is spin_retrieve, then
- * spin_attend. */
+ * Attention.  When copy_stream differs from stream the two overlap in one
+ * launch on `stream` (spin_transfer_attend, which here also runs the
+ * segment-pool pass of resolve_evict in a workgroup of its own), then
+ * spin_attend_finish merges; nothing is enqueued on copy_stream (the staged
+ * calls spin_retrieve_attend + spin_attend_begin / _finish put the transfer
+ * on a stream of its own, with the same results bit for bit).  When the two
+ * streams are equal it is spin_retrieve, then spin_attend. */
 SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel,
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream);
@@ -312,11 +314,9 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
  * d_q_steps + t * q_step_elems (bf16 elements; q_step_elems * 2 a multiple
  * of 16), and the step's last kernel on `stream` increments *d_t, so one
  * captured call replays as consecutive steps.  Overlapped (copy_stream !=
- * stream), the transfer and the resident-page attention share one launch on
- * `stream` (spin_transfer_attend), which also runs the segment-pool pass of
- * resolve_evict in a workgroup of its own; nothing runs on copy_stream and
- * the graph holds no event; the results (outputs, selections, the whole
- * residency state) equal spin_step's bit for bit.  t is the caller's to keep non-decreasing.
+ * stream) nothing runs on copy_stream and the graph holds no event; the
+ * results (outputs, selections, the whole residency state) equal
+ * spin_step's bit for bit.  t is the caller's to keep non-decreasing.
  * Captured (stream capture active on `stream`), the call waits for no
  * transfer enqueued before the capture: the context must be idle when the
  * capture begins (synchronise the streams it used).  The captured graph holds

@@ -657,40 +657,34 @@ SPIN_API int spin_attend_finish(spin_ctx* ctx, const void* d_q, const int32_t* d
 
 namespace {
 
-// One decode step.  Overlapped (copy_stream != stream) it runs the transfer,
-// attending pages on arrival, either on copy_stream beside the resident-page
-// pass on `stream` (one_launch false: measured faster with eager launches),
-// or together with that pass in one launch on `stream` (one_launch true: no
-// second stream and no event inside the step, measured faster as replays of
-// a captured graph; the segment-pool pass then runs inside the transfer
-// launch, and a non-null advance (the device-side step index) is incremented
-// by the merge, *advanced telling the caller so).  Both give the same results
-// bit for bit.
+// One decode step.  Overlapped (copy_stream != stream), the transfer, with
+// each fetched page attended on arrival, and the resident-page attention run
+// in one launch on `stream`, which also takes the segment-pool pass; then the
+// merge, which increments a non-null advance (the device-side step index),
+// *advanced telling the caller so.  No second stream and no event inside the
+// step: measured faster than the transfer on copy_stream beside the
+// resident-page pass on `stream`, both with eager launches and as replays of
+// a captured graph.  Otherwise retrieve, then attention, on `stream`.
 int step_impl(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel, int32_t* d_block_table,
               int32_t* d_block_ntok, int32_t* d_block_count, float* d_out, void* stream,
-              void* copy_stream, bool one_launch, int32_t* advance = nullptr,
-              bool* advanced = nullptr) {
-  const bool fused = copy_stream != stream && one_launch;
+              void* copy_stream, int32_t* advance = nullptr, bool* advanced = nullptr) {
+  const bool overlap = copy_stream != stream;
   int rc = spin_select(ctx, d_q, d_sel, nullptr, stream);
   if (!rc)
-    rc = resolve_impl(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream, !fused);
-  if (copy_stream == stream) {
-    if (!rc) rc = spin_retrieve(ctx, copy_stream);
+    rc = resolve_impl(ctx, d_sel, t, d_block_table, d_block_ntok, d_block_count, stream, !overlap);
+  if (!overlap) {
+    if (!rc) rc = spin_retrieve(ctx, stream);
     if (!rc) rc = spin_attend(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
-  } else if (one_launch) {
-    // the arguments were all checked by the calls above, so the deferred
-    // segment pass cannot be skipped by an argument error here
-    if (!rc)
-      rc = transfer_attend_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream, true);
-    if (!rc) {
-      rc = attend_finish_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream,
-                              advance);
-      if (!rc && advanced) *advanced = advance != nullptr;
-    }
-  } else {
-    if (!rc) rc = spin_retrieve_attend(ctx, d_q, copy_stream);
-    if (!rc) rc = spin_attend_begin(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream);
-    if (!rc) rc = spin_attend_finish(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream);
+    return rc;
+  }
+  // the arguments were all checked by the calls above, so the deferred
+  // segment pass cannot be skipped by an argument error here
+  if (!rc)
+    rc = transfer_attend_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, stream, true);
+  if (!rc) {
+    rc = attend_finish_impl(ctx, d_q, d_block_table, d_block_ntok, d_block_count, d_out, stream,
+                            advance);
+    if (!rc && advanced) *advanced = advance != nullptr;
   }
   return rc;
 }
@@ -701,7 +695,7 @@ SPIN_API int spin_step(spin_ctx* ctx, const void* d_q, int32_t t, int32_t* d_sel
                        int32_t* d_block_table, int32_t* d_block_ntok, int32_t* d_block_count,
                        float* d_out, void* stream, void* copy_stream) {
   return step_impl(ctx, d_q, t, d_sel, d_block_table, d_block_ntok, d_block_count, d_out, stream,
-                   copy_stream, false);
+                   copy_stream);
 }
 
 SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_elems,
@@ -724,7 +718,7 @@ SPIN_API int spin_step_at(spin_ctx* ctx, const void* d_q_steps, int64_t q_step_e
   ctx->dev.q_step = q_step_elems;
   bool advanced = false;
   int rc = step_impl(ctx, d_q_steps, 0, d_sel, d_block_table, d_block_ntok, d_block_count, d_out,
-                     stream, copy_stream, true, d_t, &advanced);
+                     stream, copy_stream, d_t, &advanced);
   ctx->dev.step_t = nullptr;
   ctx->dev.q_step = 0;
   if (rc) return rc;

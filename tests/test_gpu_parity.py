@@ -352,10 +352,13 @@ def test_max_batch_graph_replays(spin_lib):
 
 
 def test_streams_change_between_steps(spin_lib):
-    """The whole-step call with the stream roles moving every step (this
-    step's copy stream computes the next one) matches the oracle, and is
-    bit-identical to the same steps on one fixed stream pair: every wait for
-    a transfer lands where it must."""
+    """The staged calls with the transfer on a second stream
+    (spin_retrieve_attend on the copy stream beside spin_attend_begin, then
+    spin_attend_finish) and the stream roles moving every step (this step's
+    copy stream computes the next one) match the oracle, and are
+    bit-identical to the whole-step call (transfer and attention in one
+    launch) on one fixed stream pair: every cross-stream wait for a transfer
+    or a resolve lands where it must."""
     import torch
 
     w = W.variant(W.C1, name="rotating", steps=12, ar_coef=0.2)
@@ -366,7 +369,12 @@ def test_streams_change_between_steps(spin_lib):
     torch.cuda.synchronize()
     for t in range(w.steps):
         s, c = streams[t % 3], streams[(t + 1) % 3]
-        a.spin.step(a.q_dev[t], t, stream=s, copy_stream=c)
+        q = a.q_dev[t]
+        a.spin.select(q, stream=s)
+        a.spin.resolve_evict(t, stream=s)
+        a.spin.retrieve_attend(q, copy_stream=c)
+        a.spin.attend_begin(q, stream=s)
+        a.spin.attend_finish(q, stream=s)
         b.spin.step(b.q_dev[t], t, stream=fixed[0], copy_stream=fixed[1])
         torch.cuda.synchronize()
         sel_o, blocks, out_o = a.oracle.step(a.draws.q_bits[t], t)
