@@ -103,27 +103,40 @@ def test_whole_step_call_matches_stages(spin_lib, pps):
     b.close()
 
 
-@pytest.mark.parametrize("arrival", [False, True], ids=["fetched_pass", "on_arrival"])
-def test_overlapped_attention_calls(spin_lib, arrival):
+@pytest.mark.parametrize("mode", ["fetched_pass", "on_arrival", "one_launch"])
+def test_overlapped_attention_calls(spin_lib, mode):
     """attend_begin / attend_finish on one stream equal spin_attend (every
     block a hit, every block a miss, and mixed steps), with the fetched pages
-    attended after the transfer or by the transfer itself on arrival."""
+    attended after the transfer, by the transfer itself on arrival, or by
+    spin_transfer_attend (the transfer and the resident-page attention in one
+    launch, then attend_finish); the last two give the same bits."""
     import torch
     w = W.variant(W.C2, B=2, ctx=(9000, 5000), k=8, steps=6, ar_coef=0.3)
     p = _pair(w, slots=8 * 8 + 8, oracle=False, attend_pps=8)
     ref = torch.empty_like(p.spin.out)
+    arr = torch.empty_like(p.spin.out)
     for t in range(w.steps):
-        p.spin.select(p.q_dev[t])
+        q = p.q_dev[t]
+        p.spin.select(q)
         p.spin.resolve_evict(t)
-        if arrival:
-            p.spin.retrieve_attend(p.q_dev[t])
-        else:
+        if mode == "fetched_pass":
             p.spin.retrieve()
-        p.spin.attend(p.q_dev[t], out=ref)
-        p.spin.attend_begin(p.q_dev[t])
-        p.spin.attend_finish(p.q_dev[t])
+        else:
+            p.spin.retrieve_attend(q)
+        p.spin.attend(q, out=ref)
+        if mode == "one_launch":
+            # the staged two-stream form's bits, then the one launch over
+            # the same state (re-pulling the same pages is idempotent)
+            p.spin.attend_begin(q)
+            p.spin.attend_finish(q, out=arr)
+            p.spin.transfer_attend(q)
+        else:
+            p.spin.attend_begin(q)
+        p.spin.attend_finish(q)
         torch.cuda.synchronize()
         assert torch.max(torch.abs(ref - p.spin.out)).item() < 1e-5, t
+        if mode == "one_launch":
+            assert torch.equal(arr, p.spin.out), t
     p.close()
 
 
