@@ -215,6 +215,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     __syncthreads();
     cut = sh_cut;
     const int rem = need - sh_below;  // taken from the cutoff bucket, lowest slots first
+    int nv = 0;  // victims in this thread's slot range
     {
       int at = 0;
       for (int c = lo; c < hi; ++c) at += code[c] == cut;
@@ -222,19 +223,43 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       int rank = block_excl_scan<1024>(at, tmp, &tot);
       for (int c = lo; c < hi; ++c) {
         const int v = code[c];
-        if (v < cut || (v == cut && rank++ < rem)) code[c] = kCodeVictim;
+        if (v < cut || (v == cut && rank++ < rem)) {
+          code[c] = kCodeVictim;
+          ++nv;
+        }
       }
     }
+    // the victims listed in LDS (the item offsets are no longer read), so the
+    // loop below runs over the victims rather than over every slot; a list
+    // longer than that buffer falls back to the sweep over all slots
+    int nvict;
+    const int voff = block_excl_scan<1024>(nv, tmp, &nvict);
+    int* vlist = item_off;
+    const bool listed = nvict <= kMaxItems + 1;
+    if (listed && nv) {
+      int o = voff;
+      for (int c = lo; c < hi; ++c)
+        if (code[c] == kCodeVictim) vlist[o++] = c;
+    }
     __syncthreads();
-    // the victims' owners, then their directory entries, eight slots' loads
-    // in flight at a time, then the table updates
+    // the victims' owners, then their directory entries, eight victims'
+    // loads in flight at a time, then the table updates
     constexpr int UV = 8;
-    for (int c0 = tid; c0 < C; c0 += 1024 * UV) {
-      int own[UV], seg[UV];
+    const int nloop = listed ? nvict : C;
+    for (int j0 = tid; j0 < nloop; j0 += 1024 * UV) {
+      int own[UV], seg[UV], cs[UV];
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
-        const int c = c0 + 1024 * u;
-        own[u] = (c < C && code[c] == kCodeVictim) ? owner[c] : -1;
+        const int j = j0 + 1024 * u;
+        cs[u] = -1;
+        own[u] = -1;
+        if (j < nloop) {
+          const int c = listed ? vlist[j] : j;
+          if (code[c] == kCodeVictim) {
+            cs[u] = c;
+            own[u] = owner[c];
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
@@ -247,7 +272,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
         if (seg[u] == -2) continue;
-        const int c = c0 + 1024 * u;
+        const int c = cs[u];
         const int page = own[u] % d.max_pages;
         if (seg[u] >= 0 && seg[u] < d.n_seg) {
           d.segments[(size_t)seg[u] * kSegEntries + (page & 63)] = -1;
