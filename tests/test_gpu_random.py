@@ -1,0 +1,81 @@
+"""GPU parity on seeded random shapes (needs MI355X).
+
+Each case draws its own shape from a fixed seed: batch, KV heads, group size,
+ragged context lengths (an empty request now and then), fixed or variable
+partition lengths, top-k, a budget anywhere between the mandatory pages alone
+and six times them, the key structure and how fast the queries drift.  The
+shapes are small enough for the oracle to compute every output of every step,
+and together they reach corners the named cases do not combine: a tight
+budget with variable partitions, G = 1 or 16 with eviction, k above the
+partition count of some requests but not others.  The first half of the
+cases run stage by stage (the oracle's selection fed to the GPU's resolve,
+every state compared bit for bit), the second half run the benchmark's
+launch form: one captured spin_step_at graph, replayed once per step.
+"""
+import numpy as np
+import pytest
+
+from sparse_attention_tiered_amd import workload as W
+from tests.conftest import gpu_available
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+N_CASES = 32
+
+
+def random_case(i: int):
+    """Workload and slot count of random case i (a pure function of i)."""
+    rng = np.random.default_rng([4242, i])
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 5, 8, 16]))
+    while Hkv * G > 64:
+        G //= 2
+    B = int(rng.integers(1, 5))
+    var = bool(rng.random() < 0.4)
+    var_len = None
+    if var:
+        lo = int(rng.integers(8, 96))
+        var_len = (lo, int(rng.integers(lo, 257)))
+    ctx = []
+    for _ in range(B):
+        ctx.append(0 if rng.random() < 0.08 else int(rng.integers(1, 14000)))
+    k = int(rng.integers(1, 33))
+    kind = str(rng.choice(["hot", "plain", "cluster"]))
+    ppp = 1 if var_len is None else -(-var_len[1] // W.PAGE_TOKENS)
+    mand = Hkv * k * ppp
+    # most budgets tight (eviction fires within a few steps), some ample
+    slots = mand + int(mand * (rng.uniform(0.0, 0.5) if rng.random() < 0.7 else rng.uniform(0.5, 5.0)))
+    w = W.variant(W.C1, name=f"rand{i}", cfg_id=100 + i, seed=i, B=B, Hq=Hkv * G, Hkv=Hkv,
+                  ctx=tuple(ctx), k=k, slots_per_request=slots, steps=int(rng.integers(4, 11)),
+                  kv_kind=kind, hot_count=int(rng.integers(0, 5)), n_centroids=64,
+                  var_len=var_len, ar_coef=float(rng.uniform(0.2, 0.95)))
+    return w, slots
+
+
+CASES = [random_case(i) for i in range(N_CASES)]
+
+
+def _ids():
+    out = []
+    for w, slots in CASES:
+        parts = "var" if w.var_len is not None else "fixed"
+        out.append(f"{w.name}-B{w.B}-{w.Hq}x{w.Hkv}-k{w.k}-{parts}-C{slots}")
+    return out
+
+
+@pytest.mark.parametrize("i", range(N_CASES), ids=_ids())
+def test_random_shape_parity(spin_lib, i):
+    from tests.gpu_harness import Pair, log
+    w, slots = CASES[i]
+    log(f"[case] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx={w.ctx} k={w.k} var_len={w.var_len} "
+        f"kind={w.kv_kind} C={slots} steps={w.steps} ar={w.ar_coef:.2f}")
+    p = Pair(w, slots=slots)
+    p.check_summaries()
+    if i < N_CASES // 2:
+        st, worst = p.run()
+    else:
+        st, worst = p.run_graph()
+    assert st.error_word == 0
+    assert st.hits + st.misses > 0 or max(w.ctx) == 0
+    p.close()
