@@ -102,6 +102,18 @@ def counter_traffic(cfg_key, stage, bytes_per_launch):
     return None if ratio is None else float(ratio) * bytes_per_launch
 
 
+def select_kernels(B, Hkv, max_parts):
+    """The select kernels the library launches for this shape: one workgroup
+    per list for 128 or more (request, KV head) lists, several workgroups per
+    list for lists of up to 4096 partitions, otherwise scoring and top-k as
+    two launches."""
+    if B * Hkv >= 128:
+        return ["k_select_fused"]
+    if max_parts <= 4096:
+        return ["k_select_split"]
+    return ["k_score", "k_topk"]
+
+
 def cpu_baseline(w, geo, draws, host_np, budget_s=20.0):
     """The CPU oracle as it stands, on the same workload from step 0, for as
     many whole decode steps as fit in about budget_s seconds (at least one)."""
@@ -394,7 +406,7 @@ def main():
         "select": {"bound": "hbm", "achieved": score_bytes / (iso_select_ms * 1e-3) / 1e9,
                    "launch_ms": iso_select_ms,
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
-                   "kernels": ["k_score", "k_topk"]},
+                   "kernels": select_kernels(w.B, w.Hkv, geo.max_parts)},
         "retrieve": {"bound": "pcie",
                      "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if retrieve_bytes else 0.0,
                      "launch_ms": stage_ms["retrieve"],

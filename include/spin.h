@@ -228,7 +228,9 @@ SPIN_API int spin_release(spin_ctx* ctx, int32_t req, void* stream);
  * head), score = (mean of the group's G queries) . summary / sqrt(128), in
  * float32, and keep the topk highest per KV head (ties: lower partition id).
  * d_scores may be NULL ([max_batch][Hkv][max_partitions] float32, -inf past a
- * request's partitions). */
+ * request's partitions).  Two selects of one context must not overlap in time
+ * (on different streams): they share the workspace's scores and the per-list
+ * counters that hand each list to its top-k. */
 SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* d_scores,
                          void* stream);
 

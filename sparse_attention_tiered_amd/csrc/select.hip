@@ -121,10 +121,10 @@ __device__ __forceinline__ int topk_bucket(float v, float mn, float scale) {
   return (int)f;
 }
 
-// LDS of one top-k workgroup.
+// LDS of one top-k workgroup, besides the scores themselves (an array of
+// the list's length, reused for radix keys, that each caller provides).
 template <int NT>
 struct TopkLds {
-  float vals[kMaxPartitions];  // the scores; reused for radix keys
   int hist[kTopkBins];
   int cand[kTopkCand];
   float candv[kTopkCand];
@@ -134,11 +134,11 @@ struct TopkLds {
   int sh[4];  // boundary bucket, count above it, fill counter / radix state
 };
 
-// The selection itself, once the n > k scores of the list sit in L.vals and
-// each thread holds the min / max of the scores it wrote: writes the k chosen
-// ids, ascending, to out.  Every thread of the workgroup calls it.
+// The selection itself, once the n > k scores of the list sit in vals (LDS)
+// and each thread holds the min / max of the scores it wrote: writes the k
+// chosen ids, ascending, to out.  Every thread of the workgroup calls it.
 template <int NT>
-__device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, int* out) {
+__device__ void topk_select(TopkLds<NT>& L, float* vals, int n, int k, float mn, float mx, int* out) {
   static_assert(kTopkBins % NT == 0 && NT >= kTopkCand && NT >= 256, "whole buckets per thread");
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < kTopkBins; i += NT) L.hist[i] = 0;
@@ -163,7 +163,7 @@ __device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, in
   // a range too narrow for a finite scale puts everything in bucket 0
   float scale = (float)kTopkBins / (mx - mn);
   if (!(scale < 3.0e38f)) scale = 0.f;
-  for (int i = tid; i < n; i += NT) atomicAdd(&L.hist[topk_bucket(L.vals[i], mn, scale)], 1);
+  for (int i = tid; i < n; i += NT) atomicAdd(&L.hist[topk_bucket(vals[i], mn, scale)], 1);
   __syncthreads();
   // counts from the top: thread t holds the PER buckets just below
   // 2047 - PER t, highest first
@@ -196,7 +196,7 @@ __device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, in
   const int m = L.hist[cut];     // its members
   if (m <= kTopkCand) {
     for (int i = tid; i < n; i += NT) {
-      const float v = L.vals[i];
+      const float v = vals[i];
       const int bk = topk_bucket(v, mn, scale);
       if (bk > cut) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
       if (bk == cut) {
@@ -222,9 +222,9 @@ __device__ void topk_select(TopkLds<NT>& L, int n, int k, float mn, float mx, in
   } else {
     // radix select among the boundary bucket's members; key 0 marks the rest
     // (no finite score maps to 0)
-    uint32_t* keys = reinterpret_cast<uint32_t*>(L.vals);
+    uint32_t* keys = reinterpret_cast<uint32_t*>(vals);
     for (int i = tid; i < n; i += NT) {
-      const float v = L.vals[i];
+      const float v = vals[i];
       const int bk = topk_bucket(v, mn, scale);
       if (bk > cut) atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
       keys[i] = bk == cut ? float_key(v + 0.f) : 0u;  // -0 ranks as +0
@@ -298,6 +298,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ scores,
                                              int* __restrict__ sel) {
   __shared__ TopkLds<NT> L;
+  __shared__ float vals[kMaxPartitions];
   const int bh = blockIdx.x;
   const int n = d.req_parts[bh / d.Hkv];
   const int k = d.k;
@@ -311,11 +312,11 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
   float mn = INFINITY, mx = -INFINITY;
   for (int i = tid; i < n; i += NT) {
     const float v = srow[i];
-    L.vals[i] = v;
+    vals[i] = v;
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
   }
-  topk_select<NT>(L, n, k, mn, mx, out);
+  topk_select<NT>(L, vals, n, k, mn, mx, out);
 }
 
 // Scoring and top-k of one (request, KV head) in one 1024-thread workgroup,
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
                                                        int* __restrict__ sel) {
   q = step_queries(d, q);
   __shared__ TopkLds<1024> L;
+  __shared__ float vals[kMaxPartitions];
   __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];
   __shared__ float sqbar[kHeadDim];
   const int bh = blockIdx.x;
@@ -343,8 +345,28 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
   int* out = sel + (size_t)bh * k;
   for (int p = n + tid; p < d.Nmax; p += 1024) srow[p] = -INFINITY;
 
+  // wave `wave` of a pass covers rows base + 32 wave + 4 grp + it, it < 4; a
+  // row past the list re-reads row 0 and is not used
+  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
+  constexpr int kRowsPerPass = 16 * 8 * kFusedRows;
+  float4 v[kFusedRows][4];
+  auto load_pass = [&](int base) {
+    const int p0 = base + wave * 8 * kFusedRows + kFusedRows * grp;
+#pragma unroll
+    for (int it = 0; it < kFusedRows; ++it) {
+      const int p = p0 + it;
+      const float* row = S + (size_t)(p < n ? p : 0) * kHeadDim + 4 * r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[it][j] = *reinterpret_cast<const float4*>(row + 32 * j);
+    }
+  };
+  // the group's queries, then the first pass's summaries in flight while
+  // their mean is formed
   const int nq = d.G * kHeadDim / 8;
-  if (tid < nq) sq[tid] = reinterpret_cast<const uint4*>(q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim)[tid];
+  uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < nq) qc = reinterpret_cast<const uint4*>(q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim)[tid];
+  load_pass(0);
+  if (tid < nq) sq[tid] = qc;
   __syncthreads();
   if (tid < kHeadDim) {
     const uint16_t* sq16 = reinterpret_cast<const uint16_t*>(sq);
@@ -359,20 +381,10 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
 #pragma unroll
     for (int e = 0; e < 4; ++e) qv[4 * j + e] = sqbar[32 * j + 4 * r + e];
 
-  // wave `wave` of a pass covers rows base + 32 wave + 4 grp + it, it < 4
-  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
   float mn = INFINITY, mx = -INFINITY;
-  constexpr int kRowsPerPass = 16 * 8 * kFusedRows;
   for (int base = 0; base < n; base += kRowsPerPass) {
+    if (base > 0) load_pass(base);
     const int p0 = base + wave * 8 * kFusedRows + kFusedRows * grp;
-    float4 v[kFusedRows][4];
-#pragma unroll
-    for (int it = 0; it < kFusedRows; ++it) {
-      const int p = p0 + it;
-      const float* row = S + (size_t)(p < n ? p : 0) * kHeadDim + 4 * r;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[it][j] = *reinterpret_cast<const float4*>(row + 32 * j);
-    }
     float acc[kFusedRows];
 #pragma unroll
     for (int it = 0; it < kFusedRows; ++it) {
@@ -396,7 +408,7 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
       for (int it = 1; it < kFusedRows; ++it) mine = (r == it) ? acc[it] : mine;
       const int p = p0 + r;
       if (p < n) {
-        L.vals[p] = mine;
+        vals[p] = mine;
         srow[p] = mine;
         mn = fminf(mn, mine);
         mx = fmaxf(mx, mine);
@@ -408,8 +420,137 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
     return;
   }
   __syncthreads();
-  topk_select<1024>(L, n, k, mn, mx, out);
+  topk_select<1024>(L, vals, n, k, mn, mx, out);
 }
+
+// Scoring and top-k in one launch for batches with fewer lists than CUs.
+//
+// Each (request, KV head) list is spread over several 1024-thread
+// workgroups of kSplitRows partitions, as many as k_score would use, so the
+// summaries stream from HBM at the same rate; each row's dot product is the
+// same arithmetic as in k_score.  The last workgroup of a list to finish its
+// rows runs the top-k over the whole list, which a second launch did before.
+//
+// The hand-over between workgroups costs no cache write-back: the scores are
+// written as agent-scope atomic stores, which write through the XCD's L2, and
+// each wave waits for its stores to complete before the workgroup barrier;
+// only then does one thread count the workgroup in (relaxed agent-scope
+// atomic add on the list's counter).  The workgroup that brings the count to
+// the list's number of chunks reads the scores back with agent-scope atomic
+// loads, which do not hit stale lines of its own L2, and resets the counter
+// for the next launch.  A release fence would instead write back the whole L2
+// of every workgroup's XCD, which costs more than the second launch.
+template <int ROWS>
+struct SplitSelect {
+  static constexpr int kRows = 16 * 8 * ROWS;  // partitions per workgroup
+};
+
+template <int ROWS>
+__global__ __launch_bounds__(1024) void k_select_split(Dev d, const uint16_t* __restrict__ q,
+                                                       float* __restrict__ scores,
+                                                       int* __restrict__ sel, int* __restrict__ arrive) {
+  constexpr int kRows = SplitSelect<ROWS>::kRows;
+  extern __shared__ float vals[];  // [Nmax]: the list's scores, last workgroup only
+  __shared__ TopkLds<1024> L;
+  __shared__ uint4 sq[kMaxGroup * kHeadDim / 8];
+  __shared__ float sqbar[kHeadDim];
+  __shared__ int s_last;
+  q = step_queries(d, q);
+  const int bh = blockIdx.y;
+  const int b = bh / d.Hkv, h = bh - b * d.Hkv;
+  const int n = d.req_parts[b];
+  const int k = d.k;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = lane >> 3, r = lane & 7;
+  const int p0 = blockIdx.x * kRows;
+  float* srow = scores + (size_t)bh * d.Nmax;
+  int* out = sel + (size_t)bh * k;
+  // a list of at most k partitions keeps all of them, whatever the scores
+  if (blockIdx.x == 0 && n <= k)
+    for (int i = tid; i < k; i += 1024) out[i] = i < n ? i : -1;
+  if (p0 >= n) {
+    for (int p = p0 + tid; p < min(p0 + kRows, d.Nmax); p += 1024) srow[p] = -INFINITY;
+    return;
+  }
+
+  // the group's queries, then this workgroup's summary rows in flight while
+  // their mean is formed; group `grp` of wave `wave` takes rows
+  // p0 + wave 8 ROWS + ROWS grp + it (a row past the list re-reads row p0)
+  const int nq = d.G * kHeadDim / 8;
+  uint4 qc = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < nq) qc = reinterpret_cast<const uint4*>(q + ((size_t)b * d.Hq + (size_t)h * d.G) * kHeadDim)[tid];
+  const float* S = d.summaries + (size_t)bh * d.Nmax * kHeadDim;
+  const int pw = p0 + wave * 8 * ROWS + ROWS * grp;
+  float4 v[ROWS][4];
+#pragma unroll
+  for (int it = 0; it < ROWS; ++it) {
+    const int p = pw + it;
+    const float* row = S + (size_t)(p < n ? p : p0) * kHeadDim + 4 * r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[it][j] = *reinterpret_cast<const float4*>(row + 32 * j);
+  }
+  if (tid < nq) sq[tid] = qc;
+  __syncthreads();
+  if (tid < kHeadDim) {
+    const uint16_t* sq16 = reinterpret_cast<const uint16_t*>(sq);
+    float sum = 0.f;
+    for (int g = 0; g < d.G; ++g) sum += __uint_as_float((uint32_t)sq16[g * kHeadDim + tid] << 16);
+    sqbar[tid] = sum * (1.0f / ((float)d.G * sqrtf((float)kHeadDim)));
+  }
+  __syncthreads();
+  float qv[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[4 * j + e] = sqbar[32 * j + 4 * r + e];
+  float acc[ROWS];
+#pragma unroll
+  for (int it = 0; it < ROWS; ++it) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a = fmaf(v[it][j].x, qv[4 * j + 0], a);
+      a = fmaf(v[it][j].y, qv[4 * j + 1], a);
+      a = fmaf(v[it][j].z, qv[4 * j + 2], a);
+      a = fmaf(v[it][j].w, qv[4 * j + 3], a);
+    }
+    a += __shfl_xor(a, 1, 64);
+    a += __shfl_xor(a, 2, 64);
+    a += __shfl_xor(a, 4, 64);
+    acc[it] = a;
+  }
+  // lane r < ROWS of the group writes row pw + r
+  if (r < ROWS) {
+    float mine = acc[0];
+#pragma unroll
+    for (int it = 1; it < ROWS; ++it) mine = (r == it) ? acc[it] : mine;
+    const int p = pw + r;
+    if (p < n) __hip_atomic_store(&srow[p], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (p < d.Nmax) srow[p] = -INFINITY;
+  }
+  if (n <= k) return;
+
+  // count this workgroup in once every wave's score stores have completed
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int chunks = (n + kRows - 1) / kRows;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&arrive[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == chunks - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) __hip_atomic_store(&arrive[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = tid; i < n; i += 1024) {
+    const float x = __hip_atomic_load(&srow[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    vals[i] = x;
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  topk_select<1024>(L, vals, n, k, mn, mx, out);
+}
+
+constexpr int kSplitSelectRows = 2;  // rows in flight per 8-lane group
 
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s) {
   dim3 grid((d.Nmax + kScorePerWG - 1) / kScorePerWG, d.B * d.Hkv);
@@ -420,6 +561,15 @@ hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStrea
 hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, int* sel,
                                hipStream_t s) {
   hipLaunchKernelGGL(k_select_fused, dim3(d.B * d.Hkv), dim3(1024), 0, s, d, q, scores, sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_split(const Dev& d, const uint16_t* q, float* scores, int* sel,
+                               hipStream_t s) {
+  constexpr int rows = SplitSelect<kSplitSelectRows>::kRows;
+  dim3 grid((d.Nmax + rows - 1) / rows, d.B * d.Hkv);
+  hipLaunchKernelGGL(k_select_split<kSplitSelectRows>, grid, dim3(1024), d.Nmax * sizeof(float), s, d, q,
+                     scores, sel, d.arrive);
   return hipGetLastError();
 }
 

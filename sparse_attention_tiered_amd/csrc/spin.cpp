@@ -141,7 +141,8 @@ Derived derive(const spin_config* c) {
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
       directory, segments,
-      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, miss_tmp, ins, nmiss,
+      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, arrive, miss_tmp, ins,
+      nmiss,
       freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
       total;
 };
@@ -174,6 +175,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.free_count = take(B * sizeof(int));
   L.budget = take(B * sizeof(int));
   L.scores = take(B * Hkv * N * sizeof(float));
+  L.arrive = take(B * Hkv * sizeof(int));
   L.miss_tmp = take(B * d.max_mand * sizeof(int4));
   L.ins = take(B * d.max_mand * sizeof(int4));
   L.nmiss = take(B * sizeof(int));
@@ -322,6 +324,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.free_count = reinterpret_cast<int*>(w + L.free_count);
   v.budget = reinterpret_cast<int*>(w + L.budget);
   v.scores = reinterpret_cast<float*>(w + L.scores);
+  v.arrive = reinterpret_cast<int*>(w + L.arrive);
   v.miss_tmp = reinterpret_cast<int4*>(w + L.miss_tmp);
   v.ins = reinterpret_cast<int4*>(w + L.ins);
   v.nmiss = reinterpret_cast<int*>(w + L.nmiss);
@@ -531,6 +534,8 @@ SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* 
   const uint16_t* q = static_cast<const uint16_t*>(d_q);
   if (ctx->dev.B * ctx->dev.Hkv >= spin::kFusedSelectMinLists) {
     HIPCHK(ctx, spin::launch_select_fused(ctx->dev, q, sc, d_sel, S(stream)));
+  } else if (ctx->dev.Nmax <= spin::kSplitSelectMaxParts) {
+    HIPCHK(ctx, spin::launch_select_split(ctx->dev, q, sc, d_sel, S(stream)));
   } else {
     HIPCHK(ctx, spin::launch_score(ctx->dev, q, sc, S(stream)));
     HIPCHK(ctx, spin::launch_topk(ctx->dev, sc, d_sel, S(stream)));

@@ -52,6 +52,7 @@ struct Dev {
   int* budget;                 // [B] cap on resident pages (<= C)
   // per-step scratch
   float* scores;               // [B][Hkv][Nmax]
+  int* arrive;                 // [B][Hkv] workgroups of the list done scoring (0 between launches)
   int4* miss_tmp;              // [B][max_mand] (h, page, block position, valid tokens)
   int4* ins;                   // [B][max_mand] (slot, h, page, 0)
   int* nmiss;                  // [B]
@@ -91,6 +92,13 @@ hipError_t launch_index(const Dev& d, int req, int n_parts, const void* src, int
 hipError_t launch_append(const Dev& d, const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s);
 hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t s);
+// smaller batches with lists of at most this many partitions score and
+// select in one launch, several workgroups per list (measured: faster up to
+// 2048-partition lists, slower at 7.7K, where the last workgroup's top-k
+// tail outweighs the launch it saves)
+constexpr int kSplitSelectMaxParts = 4096;
+hipError_t launch_select_split(const Dev& d, const uint16_t* q, float* scores, int* sel,
+                               hipStream_t s);
 hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, int* sel,
                                hipStream_t s);
 // batches of at least this many (request, KV head) lists score and select in
