@@ -58,18 +58,45 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   int* btb = bt + (size_t)b * Hkv * MB;
   int* bnb = bntok + (size_t)b * Hkv * MB;
 
+  // loads that depend on nothing before them are issued first, so their
+  // round trips overlap the translation instead of following it: the free
+  // count and budget, and the first batch of the slot sweep of step 3 (the
+  // sweep reads owner, which nothing changes before it, and last_use, which
+  // step 2 changes only for mandatory slots, whose value the sweep ignores)
+  constexpr int U = 8;  // slots per thread whose loads are in flight together
+  const int freec = d.free_count[b];
+  const int budget = d.budget[b];
+  int ow0[U], lu0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = tid + 1024 * u;
+    ow0[u] = c < C ? owner[c] : -1;
+    lu0[u] = c < C ? last[c] : 0;
+  }
   for (int i = tid; i < (C + 31) / 32; i += 1024) mand[i] = 0;
 
-  // 1. position of every selected partition in the canonical page list
+  // 1. position of every selected partition in the canonical page list (the
+  //    first 1024 items' ids, lengths and first pages stay in registers for 2)
   int carry = 0;
+  int p_keep = -1, len_keep = 0, first_keep = 0;
   for (int base = 0; base < n_items; base += 1024) {
     const int i = base + tid;
     int np = 0;
     if (i < n_items) {
       const int p = selb[i];
+      if (base == 0) p_keep = p;
       if (p >= 0) {
-        if (p < n_parts) np = (plen[p] + kPageTokens - 1) / kPageTokens;
-        else atomicOr(d.err, kErrPartition);
+        if (p < n_parts) {
+          const int pl = plen[p];
+          const int pf = pfirst[p];
+          np = (pl + kPageTokens - 1) / kPageTokens;
+          if (base == 0) {
+            len_keep = pl;
+            first_keep = pf;
+          }
+        } else {
+          atomicOr(d.err, kErrPartition);
+        }
       }
     }
     int tot;
@@ -96,15 +123,16 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   int mcarry = 0;
   for (int base = 0; base < n_items; base += 1024) {
     const int i = base + tid;
-    int nm = 0, p = -1, h = 0, np = 0, pos0 = 0;
+    int nm = 0, p = -1, h = 0, np = 0, pos0 = 0, pf0 = 0, pl = 0;
     unsigned missmask = 0;
     if (i < n_items) {
-      p = selb[i];
+      p = base == 0 ? p_keep : selb[i];
       h = i / k;
       if (p >= 0 && p < n_parts) {
-        np = (plen[p] + kPageTokens - 1) / kPageTokens;
+        pf0 = base == 0 ? first_keep : pfirst[p];
+        pl = base == 0 ? len_keep : plen[p];
+        np = (pl + kPageTokens - 1) / kPageTokens;
         pos0 = item_off[i] - item_off[h * k];
-        const int pf0 = pfirst[p], pl = plen[p];
         int slots[kMaxPPP];
 #pragma unroll
         for (int j = 0; j < kMaxPPP; ++j) {
@@ -142,14 +170,23 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       int rnk = mcarry + ex;
       for (int j = 0; j < np; ++j)
         if (missmask & (1u << j))
-          misses[rnk++] = make_int4(h, pfirst[p] + j, pos0 + j,
-                                    min(kPageTokens, plen[p] - kPageTokens * j));
+          misses[rnk++] = make_int4(h, pf0 + j, pos0 + j, min(kPageTokens, pl - kPageTokens * j));
     }
     mcarry += tot;
   }
   const int nmiss = mcarry;
   if (tid == 0) d.head_moff[(size_t)b * (Hkv + 1) + Hkv] = nmiss;
   __syncthreads();
+  // the first 1024 misses, the one before each, and each one's directory
+  // entry as it stands before step 3, loaded now for steps 4 and 5 (step 3
+  // can only clear directory entries, and it flags each one it clears)
+  int4 m_pre = make_int4(0, 0, 0, 0), m_prev = make_int4(-1, 0, 0, 0);
+  int dir_pre = -1;
+  if (tid < nmiss) {
+    m_pre = misses[tid];
+    if (tid > 0) m_prev = misses[tid - 1];
+    dir_pre = dir[m_pre.x * d.ndir + (m_pre.y >> 6)];
+  }
 
   // 3. bucketed LRU, only when the resident pages plus the misses exceed the
   //    request's budget (with the budget at the whole area: when the misses
@@ -161,20 +198,23 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   //    the cutoff bucket, the free slots the misses take) is one workgroup
   //    scan over contiguous per-thread slot ranges of those codes, and the
   //    global updates run afterwards, one slot or one miss per thread.
-  const int freec = d.free_count[b];
-  const int need = (C - freec) + nmiss - d.budget[b];
+  const int need = (C - freec) + nmiss - budget;
   int nfreed = 0, cut = -1;
   if (tid < kBuckets) hist[tid] = 0;
   __syncthreads();
   if (need > 0 || nmiss > 0) {
-    constexpr int U = 8;  // slots per thread whose loads are in flight together
     for (int c0 = tid; c0 < C; c0 += 1024 * U) {
       int ow[U], lu[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = c0 + 1024 * u;
-        ow[u] = c < C ? owner[c] : -1;
-        lu[u] = (c < C && need > 0) ? last[c] : 0;
+        if (c0 == tid) {
+          ow[u] = ow0[u];
+          lu[u] = lu0[u];
+        } else {
+          ow[u] = c < C ? owner[c] : -1;
+          lu[u] = (c < C && need > 0) ? last[c] : 0;
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -324,21 +364,29 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   }
 
   // 4. misses take the free slots in ascending slot order: the rank of each
-  //    free slot goes to the insert list, then one thread per miss fills it
+  //    free slot goes to an LDS list (the item offsets' space, free again
+  //    since step 2; the insert list itself when there are more misses), then
+  //    one thread per miss fills it
   int assigned = 0;
   int4* insb = d.ins + (size_t)b * d.max_mand;
   if (nmiss > 0) {
+    const bool lds_slots = nmiss <= kMaxItems + 1;
+    int* slot_of = item_off;
     int fr = 0;
     for (int c = lo; c < hi; ++c) fr += code[c] == kCodeFree;
     int tot;
     int r = block_excl_scan<1024>(fr, tmp, &tot);
     for (int c = lo; c < hi && r < nmiss; ++c)
-      if (code[c] == kCodeFree) insb[r++].x = c;
+      if (code[c] == kCodeFree) {
+        if (lds_slots) slot_of[r] = c;
+        else insb[r].x = c;
+        ++r;
+      }
     assigned = min(tot, nmiss);
     __syncthreads();
     for (int j = tid; j < assigned; j += 1024) {
-      const int c = insb[j].x;
-      const int4 m = misses[j];  // (h, page, block position, valid tokens)
+      const int c = lds_slots ? slot_of[j] : insb[j].x;
+      const int4 m = j == tid ? m_pre : misses[j];  // (h, page, block position, valid tokens)
       owner[c] = m.x * d.max_pages + m.y;
       last[c] = t;
       btb[m.x * MB + m.z] = b * C + c;
@@ -360,14 +408,18 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       const int r = base + tid;
       int fl = 0, e = 0;
       if (r < assigned) {
-        const int4 m = misses[r];
+        const int4 m = base == 0 ? m_pre : misses[r];
         e = m.x * d.ndir + (m.y >> 6);
         bool first = true;
         if (r > 0) {
-          const int4 pm = misses[r - 1];
+          const int4 pm = base == 0 ? m_prev : misses[r - 1];
           first = (pm.x * d.ndir + (pm.y >> 6)) != e;
         }
-        fl = (first && dir[e] < 0) ? 1 : 0;
+        // the entry now: step 3 emptied it (and flagged it) or left it as it was
+        int dv;
+        if (base == 0) dv = (need > 0 && ((mand[e >> 5] >> (e & 31)) & 1u)) ? -1 : dir_pre;
+        else dv = dir[e];
+        fl = (first && dv < 0) ? 1 : 0;
       }
       int tot;
       const int ex = block_excl_scan<1024>(fl, tmp, &tot);
