@@ -79,3 +79,44 @@ def test_random_shape_parity(spin_lib, i):
     assert st.error_word == 0
     assert st.hits + st.misses > 0 or max(w.ctx) == 0
     p.close()
+
+
+N_VARIANTS = 16
+
+
+def variant_case(i: int):
+    """Random case i, with the segment tables in host memory or not, and the
+    KV offloaded from the device with a token appended per request per step
+    or not (each drawn from its own fixed seed)."""
+    w, slots = random_case(1000 + i)
+    rng = np.random.default_rng([4343, i])
+    host_segments = bool(rng.random() < 0.5)
+    append = bool(rng.random() < 0.5)
+    return w, slots, host_segments, append
+
+
+VARIANTS = [variant_case(i) for i in range(N_VARIANTS)]
+
+
+@pytest.mark.parametrize("i", range(N_VARIANTS),
+                         ids=[f"{w.name}-{'hostseg' if hs else 'gpuseg'}-{'append' if ap else 'fixed'}"
+                              for w, _, hs, ap in VARIANTS])
+def test_random_shape_variants(spin_lib, i):
+    """Stage parity on random shapes with the second-level tables in pinned
+    host memory and/or the prefill-side offload followed by decode-time
+    appends (host bytes and summaries compared too)."""
+    from tests.gpu_harness import Pair, log
+    w, slots, host_segments, append = VARIANTS[i]
+    log(f"[case] {w.name} B={w.B} Hq={w.Hq} Hkv={w.Hkv} ctx={w.ctx} k={w.k} var_len={w.var_len} "
+        f"C={slots} steps={w.steps} host_segments={host_segments} append={append}")
+    extra = (w.steps + W.PAGE_TOKENS - 1) // W.PAGE_TOKENS + 2 if append else None
+    p = Pair(w, slots=slots, host_segments=host_segments, offload_extra_pages=extra)
+    if append:
+        p.check_host()
+    p.check_summaries()
+    st, _ = p.run(append=append)
+    if append:
+        p.check_host()
+        p.check_summaries()
+    assert st.error_word == 0
+    p.close()
