@@ -24,17 +24,24 @@ def test_full_size(spin_lib, name):
     p.close()
 
 
-@pytest.mark.parametrize("name", ["c3", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_full_size_graph_replays(spin_lib, name):
     """The timed configuration of the benchmark (graph replays of the
     device-indexed step, transfer and attention in one launch, the segment
     pass and the inserts inside it in one workgroup: 4.7K inserts a step on
-    c4) against the oracle at full size."""
+    c4) against the oracle at full size, for every workload: each of the
+    three select forms (one launch with several workgroups per list on c1
+    and c3, one workgroup per list on c2 and c4, two kernels on c5's
+    7.7K-partition lists) and c5's variable partitions."""
     from tests.gpu_harness import Pair, log
     w = W.get(name)
-    steps = 6
+    # c4's pool (25% of demand) fills over its first steps; 12 take it well
+    # into eviction every step
+    steps = 12 if name == "c4" else 6
     log(f"[case] full-size graph replays {w.name}: {steps} steps")
     p = Pair(w, n_steps=steps)
     st, worst = p.run_graph(steps=steps, out_sample=24)
     assert st.misses > 0
+    if name == "c4":
+        assert st.evictions > 0
     p.close()
