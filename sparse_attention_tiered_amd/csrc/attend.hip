@@ -37,17 +37,25 @@ namespace spin {
 constexpr int kAttWG = 256;
 
 // Pages per split of a head with cnt pages: its pages spread evenly over the
-// head's `splits` workgroups (whole pages per wave), so heads with fewer
-// pages than the largest possible count still use all their workgroups and
-// the slowest workgroup carries no more than it must.  Never above d.pps,
-// the split size the grid was sized with.
-__device__ __forceinline__ int head_pps(const Dev& d, int cnt) {
-  const int per = (cnt + d.splits - 1) / d.splits;
+// head's `nsp` workgroups (whole pages per wave), so heads with fewer pages
+// than the largest possible count still use all their workgroups and the
+// slowest workgroup carries no more than it must.  Never above the split
+// size the grid was sized with (d.pps for nsp = d.splits, d.pps_res for the
+// resident-page pass's d.splits_res).
+__device__ __forceinline__ int head_pps(int cnt, int nsp) {
+  const int per = (cnt + nsp - 1) / nsp;
   return max(4, (per + 3) & ~3);
 }
 
-// Workgroup wg of the attention grid (B * Hkv * splits): split wg % splits
-// of (request, KV head) wg / splits; q already points at this step's queries.
+// Splits per head of an attention pass: the resident-page pass that runs
+// beside the transfer uses fewer, longer ones.
+__device__ __forceinline__ int pass_splits(const Dev& d, int mode) {
+  return mode == kAttendResident ? d.splits_res : d.splits;
+}
+
+// Workgroup wg of the attention grid (B * Hkv * nsp, nsp = pass_splits):
+// split wg % nsp of (request, KV head) wg / nsp; q already points at this
+// step's queries.
 __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restrict__ q,
                                           const int* __restrict__ bt, const int* __restrict__ bntok,
                                           const int* __restrict__ bcount, float* __restrict__ out,
@@ -56,12 +64,13 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
   __shared__ float sm_l[4][16];
   __shared__ float sm_o[4][16][132];
 
-  const int split = wg % d.splits;
-  const int bh = wg / d.splits;
+  const int nsp = pass_splits(d, mode);
+  const int split = wg % nsp;
+  const int bh = wg / nsp;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int pps = head_pps(d, cnt);
+  const int pps = head_pps(cnt, nsp);
   const int ns = (cnt + pps - 1) / pps;  // splits that hold pages
   const int tid = threadIdx.x;
   const int hh = tid >> 4, dc = (tid & 15) * 8;  // merge layout: head, 8 dims
@@ -358,12 +367,15 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __res
                                                          float* __restrict__ out, int both) {
   const int bh = blockIdx.x;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
+  // splits holding pages: of the whole-table pass, or of the resident-page
+  // pass followed by the fetched-page pass
+  const int ns = (cnt + head_pps(cnt, d.splits) - 1) / head_pps(cnt, d.splits);
   if (!both && ns <= 1) return;  // (the whole workgroup)
+  const int ns_res = both ? (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res) : ns;
   const int G = d.G;
-  merge_head(d, bh, both ? 2 * ns : ns,
+  merge_head(d, bh, both ? ns_res + ns : ns,
              [&](int x, int hh, int dc, const float*& ml, const float*& po) {
-               const int slot = x < ns ? x : d.splits + (x - ns);
+               const int slot = x < ns_res ? x : d.splits + (x - ns_res);
                const size_t pi = ((size_t)bh * 2 * d.splits + slot) * G + hh;
                ml = d.part_ml + 2 * pi;
                po = d.part_o + pi * kHeadDim + dc;
@@ -384,7 +396,7 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
   if (advance && bh == 0 && threadIdx.x == 0) *advance += 1;  // the next step's index
   request_offsets<kAttWG>(d.nmiss, d.B, pm, tmp);
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + head_pps(d, cnt) - 1) / head_pps(d, cnt);
+  const int ns = (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res);  // resident-page splits
   const int nm = d.nmiss[b];
   const int* mo = d.head_moff + (size_t)b * (d.Hkv + 1);
   const int j0 = pm[b] + min(max(mo[h], 0), nm), j1 = pm[b] + min(max(mo[h + 1], 0), nm);
@@ -407,7 +419,7 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
 hipError_t launch_transfer_attend(const Dev& d, const uint16_t* q, const int* bt, const int* bntok,
                                   const int* bcount, bool segments, hipStream_t s) {
   const int seg = segments ? 1 : 0;
-  hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + seg + d.B * d.Hkv * d.splits),
+  hipLaunchKernelGGL(k_transfer_attend, dim3(kRetrieveGrid + seg + d.B * d.Hkv * d.splits_res),
                      dim3(kAttWG), 0, s, d, q, bt, bntok, bcount, seg);
   return hipGetLastError();
 }
@@ -419,7 +431,8 @@ hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const i
                        advance);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * d.splits), dim3(kAttWG), 0, s, d, q, bt, bntok,
+  const int nsp = mode == kAttendResident ? d.splits_res : d.splits;
+  hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * nsp), dim3(kAttWG), 0, s, d, q, bt, bntok,
                      bcount, out, mode);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mode == kAttendResident) return e;

@@ -87,7 +87,7 @@ void transfer_enqueued(spin_ctx* ctx, hipStream_t s) {
 }
 
 struct Derived {
-  int G, ndir, max_blocks, max_mand, pps, splits;
+  int G, ndir, max_blocks, max_mand, pps, splits, pps_res, splits_res;
 };
 
 constexpr size_t kAlign = 256;
@@ -125,15 +125,25 @@ Derived derive(const spin_config* c) {
   d.max_blocks = c->topk * c->max_pages_per_partition;
   d.max_mand = c->num_kv_heads * d.max_blocks;
   int pps = (c->attend_pages_per_split + 3) / 4 * 4;  // whole pages per wave
+  int pps_res = pps;
   if (pps == 0) {
     // about one workgroup per CU over the worst-case page count: long-lived
     // waves keep their page pipeline full (measured best on MI355X)
     const long long work = (long long)c->max_batch * c->num_kv_heads * d.max_blocks;
     pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 255) / 256));
     pps = (pps + 3) / 4 * 4;
+    // the resident-page pass runs beside the transfer, which it must only
+    // keep up with: about half a workgroup per CU, each streaming pages
+    // while the PCIe pulls are in flight, contends less with them (128K
+    // workload, ~90 misses a step: 0.1115 -> 0.1070 ms per step; 64
+    // workgroups were too few, 0.117)
+    pps_res = (int)std::min<long long>(64, std::max<long long>(pps, (work + 127) / 128));
+    pps_res = (pps_res + 3) / 4 * 4;
   }
   d.pps = pps;
   d.splits = (d.max_blocks + pps - 1) / pps;
+  d.pps_res = pps_res;
+  d.splits_res = (d.max_blocks + pps_res - 1) / pps_res;
   return d;
 }
 
@@ -305,6 +315,8 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.max_mand = d.max_mand;
   v.splits = d.splits;
   v.pps = d.pps;
+  v.splits_res = d.splits_res;
+  v.pps_res = d.pps_res;
   v.summaries = reinterpret_cast<float*>(w + L.summaries);
   v.part_first = reinterpret_cast<int*>(w + L.part_first);
   v.part_len = reinterpret_cast<int*>(w + L.part_len);

@@ -30,7 +30,8 @@ constexpr int kErrState = 4;           // residency state inconsistent
 struct Dev {
   // geometry
   int B, Hq, Hkv, G, k, Nmax, max_pages, max_ppp, C, n_seg, ndir, max_blocks, max_mand;
-  int splits, pps;
+  int splits, pps;             // attention over the whole block table: splits per head, pages per split
+  int splits_res, pps_res;     // the resident-page pass beside the transfer (fewer, longer splits)
   // index tables (written by spin_index)
   float* summaries;            // [B][Hkv][Nmax][128]
   int* part_first;             // [B][Nmax] first page of partition

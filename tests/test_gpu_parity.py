@@ -78,7 +78,9 @@ def test_whole_step_call_matches_stages(spin_lib, pps):
     the same outputs up to the rounding of the two-pass merge; both match the
     oracle."""
     import torch
-    w = W.variant(W.C4, B=3, ctx=12000, k=16, steps=8, ar_coef=0.5)
+    # with the split size left to the library, 8 x 8 lists of 16 pages get
+    # 4-page splits for the whole table and 8-page ones for the resident pass
+    w = W.variant(W.C4, B=3 if pps else 8, ctx=12000, k=16, steps=8, ar_coef=0.5)
     a = _pair(w, slots=8 * 16 + 16, attend_pps=pps)
     b = _pair(w, slots=8 * 16 + 16, attend_pps=pps, oracle=False)
     side = torch.cuda.Stream()
@@ -103,16 +105,26 @@ def test_whole_step_call_matches_stages(spin_lib, pps):
     b.close()
 
 
+@pytest.mark.parametrize("pps", [8, 0])
 @pytest.mark.parametrize("mode", ["fetched_pass", "on_arrival", "one_launch"])
-def test_overlapped_attention_calls(spin_lib, mode):
+def test_overlapped_attention_calls(spin_lib, mode, pps):
     """attend_begin / attend_finish on one stream equal spin_attend (every
     block a hit, every block a miss, and mixed steps), with the fetched pages
     attended after the transfer, by the transfer itself on arrival, or by
     spin_transfer_attend (the transfer and the resident-page attention in one
-    launch, then attend_finish); the last two give the same bits."""
+    launch, then attend_finish); the last two give the same bits.  With the
+    split size left to the library (pps 0) the resident-page pass takes
+    longer splits than the whole-table and fetched-page passes (8 x 8 lists
+    of 16 pages: 8 pages against 4), so the merges combine differently
+    split passes."""
     import torch
-    w = W.variant(W.C2, B=2, ctx=(9000, 5000), k=8, steps=6, ar_coef=0.3)
-    p = _pair(w, slots=8 * 8 + 8, oracle=False, attend_pps=8)
+    if pps:
+        w = W.variant(W.C2, B=2, ctx=(9000, 5000), k=8, steps=6, ar_coef=0.3)
+        slots = 8 * 8 + 8
+    else:
+        w = W.variant(W.C2, B=8, ctx=tuple(5000 + 700 * b for b in range(8)), k=16, steps=6, ar_coef=0.3)
+        slots = 8 * 16 + 8
+    p = _pair(w, slots=slots, oracle=False, attend_pps=pps)
     ref = torch.empty_like(p.spin.out)
     arr = torch.empty_like(p.spin.out)
     for t in range(w.steps):
