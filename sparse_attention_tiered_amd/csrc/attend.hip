@@ -24,8 +24,12 @@
 // its pages loaded once up front.  The waves merge through LDS.  A head whose
 // pages fit in one workgroup is finished there; otherwise k_attend_merge
 // combines the split partials (log-sum-exp).  (Merging in the last workgroup
-// to finish would need a device-scope fence per workgroup, which writes back
-// the whole L2 on this chip and cost more than the second launch.)
+// to finish, with the partials handed over as agent-scope atomic stores and
+// loads, measured no faster than the second launch; with a device-scope
+// fence per workgroup, which writes back the whole L2, it was far slower.)
+// The resident-page pass that runs beside the transfer uses its own, longer
+// splits (d.pps_res): it only has to keep pace with the transfer, and fewer
+// attention workgroups contend less with the PCIe pulls.
 #include "arrival.h"
 #include "segments.h"
 #include "attend_tile.h"

@@ -426,9 +426,9 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
 // Scoring and top-k in one launch for batches with fewer lists than CUs.
 //
 // Each (request, KV head) list is spread over several 1024-thread
-// workgroups of kSplitRows partitions, as many as k_score would use, so the
-// summaries stream from HBM at the same rate; each row's dot product is the
-// same arithmetic as in k_score.  The last workgroup of a list to finish its
+// workgroups of 256 partitions (two rows in flight per 8-lane group), as many
+// workgroups as k_score would use, so the summaries stream from HBM at the
+// same rate; each row's dot product is the same arithmetic as in k_score.  The last workgroup of a list to finish its
 // rows runs the top-k over the whole list, which a second launch did before.
 //
 // The hand-over between workgroups costs no cache write-back: the scores are

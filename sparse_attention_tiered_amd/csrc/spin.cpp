@@ -135,9 +135,13 @@ Derived derive(const spin_config* c) {
     // the resident-page pass runs beside the transfer, which it must only
     // keep up with: about half a workgroup per CU, each streaming pages
     // while the PCIe pulls are in flight, contends less with them (128K
-    // workload, ~90 misses a step: 0.1115 -> 0.1070 ms per step; 64
-    // workgroups were too few, 0.117)
+    // workload, ~90 misses a step: 0.1115 -> 0.1070 ms per step), but at
+    // least two splits per head (one split per head there, 64 workgroups:
+    // 0.117 ms; on the 32K workload one split per head was 0.1-0.4% slower
+    // than two)
+    const int half = (d.max_blocks + 1) / 2;
     pps_res = (int)std::min<long long>(64, std::max<long long>(pps, (work + 127) / 128));
+    pps_res = std::min(pps_res, std::max(pps, half));
     pps_res = (pps_res + 3) / 4 * 4;
   }
   d.pps = pps;
