@@ -465,3 +465,42 @@ def test_graph_replayed_steps(spin_lib):
     assert st.error_word == 0 and st.evictions > 0
     a.close()
     b.close()
+
+
+@pytest.mark.parametrize("name", ["split_select", "fused_select", "long_lists"])
+def test_runs_are_deterministic(spin_lib, name):
+    """Two contexts driven through the same whole-step calls give the same
+    bits every step: selections, block tables, outputs, and the whole
+    residency state at the end.  Covers the hand-overs between workgroups of
+    one launch (the select's scores to the last workgroup of each list, the
+    transfer's arrival partials, the resident-page partials) on all three
+    select forms."""
+    import torch
+    if name == "split_select":      # few lists, 2 048 partitions each: several workgroups per list
+        w = W.variant(W.C3, B=2, ctx=131072, k=32, steps=10, hot_count=10)
+        slots = 8 * 32 * 2
+    elif name == "fused_select":    # 128 lists: one workgroup per list
+        w = W.variant(W.C4, B=16, ctx=16384, k=16, steps=10, ar_coef=0.4)
+        slots = 8 * 16 + 24
+    else:                           # lists longer than 4096 partitions: scoring and top-k as two kernels
+        w = W.variant(W.C4, B=1, ctx=300000, k=64, steps=8, ar_coef=0.4)
+        slots = 8 * 64 + 64
+    a = _pair(w, slots=slots, oracle=False)
+    b = _pair(w, slots=slots, oracle=False)
+    side_a, side_b = torch.cuda.Stream(), torch.cuda.Stream()
+    for t in range(w.steps):
+        a.spin.step(a.q_dev[t], t, copy_stream=side_a)
+        b.spin.step(b.q_dev[t], t, copy_stream=side_b)
+        torch.cuda.synchronize()
+        assert torch.equal(a.spin.sel, b.spin.sel), t
+        assert torch.equal(a.spin.block_table, b.spin.block_table), t
+        assert torch.equal(a.spin.out, b.spin.out), t
+    st_a, _ = a.spin.stats()
+    st_b, _ = b.spin.stats()
+    assert (st_a.hits, st_a.misses, st_a.evictions) == (st_b.hits, st_b.misses, st_b.evictions)
+    assert st_a.misses > 0
+    sa, sb = a.spin.snapshot(), b.spin.snapshot()
+    for k in sa:
+        assert np.array_equal(sa[k], sb[k]), k
+    a.close()
+    b.close()
