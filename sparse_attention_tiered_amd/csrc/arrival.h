@@ -9,7 +9,7 @@
 
 namespace spin {
 
-constexpr int kXferPagesPerWG = 3, kXferMinWG = 16;
+constexpr int kXferPagesPerWG = 4, kXferMinWG = 16;
 
 // The transfer with the fetched pages attended on arrival: each page also
 // goes into LDS, and wave 0 runs its attention there for the G query heads of
@@ -58,13 +58,14 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = src[u * kRetrieveWG + tid];
   };
-  // A step with few misses spreads them over fewer workgroups, about three
+  // A step with few misses spreads them over fewer workgroups, about four
   // pages each (at least 16 workgroups), so not every page is requested at
   // once: the link still runs full, and the HBM reads of the attention
   // beside it suffer less from the PCIe requests queued with them (measured
-  // on the 128K workload with ~90 misses a step: 0.117 -> 0.113 ms per step;
-  // one or two pages per workgroup, or six, were slower).  From 192 misses
-  // on, every workgroup takes part.
+  // on the 128K workload with ~90 misses a step: 0.117 -> 0.113 ms per step
+  // at three pages, then 0.1065 -> 0.1057 at four once the resident-page
+  // pass took longer splits; one or two pages per workgroup, or six, were
+  // slower).  From 256 misses on, every workgroup takes part.
   {
     const int nact = min(nwg, max(kXferMinWG, (M + kXferPagesPerWG - 1) / kXferPagesPerWG));
     if (wg >= nact) return;
