@@ -477,13 +477,13 @@ def test_runs_are_deterministic(spin_lib, name):
     select forms."""
     import torch
     if name == "split_select":      # few lists, 2 048 partitions each: several workgroups per list
-        w = W.variant(W.C3, B=2, ctx=131072, k=32, steps=10, hot_count=10)
+        w = W.variant(W.C3, B=2, ctx=131072, k=32, steps=48, hot_count=10)
         slots = 8 * 32 * 2
     elif name == "fused_select":    # 128 lists: one workgroup per list
-        w = W.variant(W.C4, B=16, ctx=16384, k=16, steps=10, ar_coef=0.4)
+        w = W.variant(W.C4, B=16, ctx=16384, k=16, steps=24, ar_coef=0.4)
         slots = 8 * 16 + 24
     else:                           # lists longer than 4096 partitions: scoring and top-k as two kernels
-        w = W.variant(W.C4, B=1, ctx=300000, k=64, steps=8, ar_coef=0.4)
+        w = W.variant(W.C4, B=1, ctx=300000, k=64, steps=16, ar_coef=0.4)
         slots = 8 * 64 + 64
     a = _pair(w, slots=slots, oracle=False)
     b = _pair(w, slots=slots, oracle=False)
