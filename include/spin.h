@@ -147,7 +147,11 @@ SPIN_API int spin_workspace_size(const spin_config* cfg, size_t* ws_bytes, size_
 SPIN_API int spin_host_segment_bytes(const spin_config* cfg, size_t* bytes);
 
 /* Derived sizes: directory entries per (request, head) = ceil(max_pages/64),
- * max_blocks = topk * max_pages_per_partition, and attention splits per head. */
+ * max_blocks = topk * max_pages_per_partition, and attention splits per head
+ * of the whole-table pass (spin_attend).  When attend_pages_per_split is 0,
+ * the resident-page pass of the overlapped forms (spin_attend_begin,
+ * spin_transfer_attend, spin_step) may take fewer, longer splits; the
+ * partial buffers are sized for the whole-table count, never exceeded. */
 SPIN_API int spin_derived(const spin_config* cfg, int32_t* ndir, int32_t* max_blocks,
                           int32_t* attend_splits);
 
