@@ -35,9 +35,10 @@ def test_full_size_graph_replays(spin_lib, name):
     7.7K-partition lists) and c5's variable partitions."""
     from tests.gpu_harness import Pair, log
     w = W.get(name)
-    # c4's pool (25% of demand) fills over its first steps; 12 take it well
-    # into eviction every step
-    steps = 12 if name == "c4" else 6
+    # c4's pool (25% of demand) fills over its first steps; 24 take it well
+    # into eviction every step.  c3's hot set drifts every 16 steps; 40
+    # cross two of those boundaries
+    steps = {"c3": 40, "c4": 24, "c5": 12}.get(name, 6)
     log(f"[case] full-size graph replays {w.name}: {steps} steps")
     p = Pair(w, n_steps=steps)
     st, worst = p.run_graph(steps=steps, out_sample=24)
