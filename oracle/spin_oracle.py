@@ -151,10 +151,19 @@ class SpinOracle:
         self.error = None
         self.stats = [dict(hits=0, misses=0, evictions=0, cutoff=-1) for _ in range(B)]
         self._pending = []   # (global slot, b, h, page) copies for retrieve()
+        # decode step of the last resolve: steps never go back, so every age
+        # t - last_use is at least 0 (reading R23)
+        self.last_t = -1
 
     # ------------------------------------------------------------------ Index (+ Offload registration)
     def release(self, b: int):
-        """Return request b's slots and segments (segments pushed in (h, e) order)."""
+        """Request turnover ([XT] part 2: each request owns a GPU area; part 3:
+        second-level segments come from, and go back to, one shared pool).
+        Every segment linked in request b's directory is cleared and pushed
+        back on the pool's stack, in (KV head, directory index) order (R18);
+        every slot of the request becomes free; its budget returns to the
+        whole area.  Other requests keep their state.  Counters (stats) are
+        per request position and are kept."""
         for h in range(self.Hkv):
             for e in range(self.ndir):
                 s = self.directory[b, h, e]
@@ -379,6 +388,11 @@ class SpinOracle:
 
         Returns block tables: per (b, h) a list of (global slot, valid tokens)
         in canonical order."""
+        if t < self.last_t:
+            # a rewound step index would give negative ages; refused before
+            # anything changes (R23)
+            raise ValueError(f"decode step {t} is below the last resolved step {self.last_t}")
+        self.last_t = t
         blocks = [[[] for _ in range(self.Hkv)] for _ in range(self.B)]
         inserts = []
         self._pending = []

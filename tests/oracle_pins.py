@@ -590,9 +590,135 @@ def pin_offload_append(om):
         assert np.allclose(out[0, g], want, rtol=0, atol=2e-6), (g, np.abs(out[0, g] - want).max())
 
 
+def _tagged_host(om, Hkv, pages, b, version):
+    """Host KV whose every page is filled with one tag, unique per (request,
+    version, head, page): the bytes of a retrieved page say which it is."""
+    buf = np.zeros((Hkv, pages, om.PAGE_ELEMS), np.uint16)
+    for h in range(Hkv):
+        for p in range(pages):
+            buf[h, p, :] = _tag(b, version, h, p)
+    return buf.reshape(-1)
+
+
+def _tag(b, version, h, p):
+    return 1 + p + 192 * (h + 2 * (b + 2 * version))
+
+
+def pin_release_reindex(om):
+    """Worked by hand: request turnover.  Two requests, two KV heads, top-2,
+    8 slots each, 192 one-page partitions (3 directory ranges of 64 pages),
+    a shared pool of 6 segments (stack [5 4 3 2 1 0], top last).
+
+    Step 0, hand-picked selections: request 0 head 0 {5, 130}, head 1
+    {70, 71}; request 1 head 0 {0, 1}, head 1 {64, 190}.  Every page misses
+    and takes the free slots in canonical order (slots 0..3 of each request).
+    Inserts, request 0 first, pop a segment on a range's first page:
+    (r0,h0,e0) <- 0, (r0,h0,e2) <- 1, (r0,h1,e1) <- 2 (pages 70 and 71),
+    (r1,h0,e0) <- 3 (pages 0 and 1), (r1,h1,e1) <- 4, (r1,h1,e2) <- 5.
+
+    release(0), after its budget was cut to 5: segments 0, 1, 2 are cleared
+    and pushed in (head, directory index) order, so the stack is [0 1 2];
+    request 0's slots are free, its budget is 8 again; request 1 is as it was.
+
+    Re-index request 0 with new KV of 100 pages; step 1 selects head 0
+    {64, 99}, head 1 {0, 3} for it (request 1 keeps its selection: four
+    hits).  Misses take slots 0..3; (r0,h0,e1) pops 2 (pages 64 and 99 ->
+    entries 0 and 35), (r0,h1,e0) pops 1 (pages 0 and 3 -> entries 0 and 3);
+    the stack is [0].  The pool rows now hold the new KV's pages.
+
+    Re-indexing request 1, which holds segments 3, 4, 5, releases it first:
+    the stack becomes [0 3 4 5] and request 0 is untouched."""
+    F = om.FREE
+    Hkv, C, P0 = 2, 8, 192
+    o = make(om, 2, 2, Hkv, 2, C, P0, n_seg=6)
+    for b in range(2):
+        o.index(b, _tagged_host(om, Hkv, P0, b, 0), np.full(P0, 64))
+    sel = np.array([[[5, 130], [70, 71]], [[0, 1], [64, 190]]])
+    o.resolve_evict(sel, 0)
+    o.retrieve()
+    assert o.directory.tolist() == [[[0, F, 1], [F, 2, F]], [[3, F, F], [F, 4, 5]]], o.directory
+    assert o.free_stack == []
+    assert list(o.seg_live) == [1, 1, 2, 2, 1, 1]
+    assert o.owner[0].tolist() == [5, 130, P0 + 70, P0 + 71, F, F, F, F]
+    assert o.owner[1].tolist() == [0, 1, P0 + 64, P0 + 190, F, F, F, F]
+    want_entries = {(0, 5): 0, (1, 2): 1, (2, 6): 2, (2, 7): 3, (3, 0): 0, (3, 1): 1, (4, 0): 2, (5, 62): 3}
+    for s in range(6):
+        for e in range(64):
+            assert o.segments[s, e] == want_entries.get((s, e), F), (s, e)
+
+    o.set_budget(0, 5)
+    seg_r1 = o.segments[3:].copy()
+    own1, lu1 = o.owner[1].copy(), o.last_use[1].copy()
+    o.release(0)
+    assert o.free_stack == [0, 1, 2], o.free_stack
+    assert np.all(o.segments[:3] == F) and list(o.seg_live) == [0, 0, 0, 2, 1, 1]
+    assert np.array_equal(o.segments[3:], seg_r1)
+    assert o.directory[0].tolist() == [[F, F, F], [F, F, F]]
+    assert o.directory[1].tolist() == [[3, F, F], [F, 4, 5]]
+    assert np.all(o.owner[0] == F) and np.all(o.last_use[0] == F)
+    assert o.budget[0] == C and o.requests[0] is None
+    assert np.array_equal(o.owner[1], own1) and np.array_equal(o.last_use[1], lu1)
+
+    o.index(0, _tagged_host(om, Hkv, 100, 0, 1), np.full(100, 64))
+    sel = np.array([[[64, 99], [0, 3]], [[0, 1], [64, 190]]])
+    blocks = o.resolve_evict(sel, 1)
+    o.retrieve()
+    assert o.free_stack == [0], o.free_stack
+    assert o.directory[0].tolist() == [[F, 2, F], [1, F, F]], o.directory[0]
+    assert o.segments[2, 0] == 0 and o.segments[2, 35] == 1
+    assert o.segments[1, 0] == 2 and o.segments[1, 3] == 3
+    assert list(o.seg_live) == [0, 2, 2, 2, 1, 1]
+    assert o.owner[0].tolist() == [64, 99, P0 + 0, P0 + 3, F, F, F, F]
+    assert o.last_use[0].tolist() == [1, 1, 1, 1, F, F, F, F]
+    assert o.last_use[1].tolist() == [1, 1, 1, 1, F, F, F, F]
+    assert [[s for s, _ in blocks[0][h]] for h in range(2)] == [[0, 1], [2, 3]]
+    assert [[s for s, _ in blocks[1][h]] for h in range(2)] == [[C + 0, C + 1], [C + 2, C + 3]]
+    for slot, (h, p) in enumerate([(0, 64), (0, 99), (1, 0), (1, 3)]):
+        assert np.all(o.pool[slot] == _tag(0, 1, h, p)), slot
+    assert o.stats[0]["misses"] == 8 and o.stats[1]["hits"] == 4 and o.stats[1]["misses"] == 4
+
+    own0, lu0, seg_r0 = o.owner[0].copy(), o.last_use[0].copy(), o.segments[1:3].copy()
+    o.index(1, _tagged_host(om, Hkv, P0, 1, 1), np.full(P0, 64))
+    assert o.free_stack == [0, 3, 4, 5], o.free_stack
+    assert np.all(o.owner[1] == F) and np.all(o.last_use[1] == F)
+    assert np.all(o.segments[3:] == F) and o.directory[1].tolist() == [[F, F, F], [F, F, F]]
+    assert np.array_equal(o.owner[0], own0) and np.array_equal(o.last_use[0], lu0)
+    assert np.array_equal(o.segments[1:3], seg_r0)
+
+
+def pin_step_order(om):
+    """Decode steps never go back (R23): with t below the last resolved step
+    some ages t - last_use would be negative.  Such a resolve is refused with
+    ValueError before anything changes; the same step index again is
+    accepted."""
+    Hkv, C, P0 = 2, 8, 192
+    o = make(om, 2, 2, Hkv, 2, C, P0, n_seg=6)
+    for b in range(2):
+        o.index(b, _tagged_host(om, Hkv, P0, b, 0), np.full(P0, 64))
+    sels = [np.array([[[5, 130], [70, 71]], [[0, 1], [64, 190]]]),
+            np.array([[[6, 130], [70, 72]], [[0, 2], [64, 190]]]),
+            np.array([[[7, 131], [73, 71]], [[3, 1], [65, 190]]])]
+    for t, s in enumerate(sels):
+        o.resolve_evict(s, t)
+    names = ("directory", "segments", "seg_live", "owner", "last_use")
+    before = {n: getattr(o, n).copy() for n in names}
+    stack, stats = list(o.free_stack), [dict(x) for x in o.stats]
+    try:
+        o.resolve_evict(sels[0], 1)
+        raise AssertionError("a rewound step index was accepted")
+    except ValueError:
+        pass
+    for n in names:
+        assert np.array_equal(getattr(o, n), before[n]), n
+    assert o.free_stack == stack and o.stats == stats
+    o.resolve_evict(sels[2], 2)
+    assert o.stats[0]["hits"] == stats[0]["hits"] + 4
+
+
 ALL_PINS = [
     pin_bf16_decode, pin_page_layout, pin_summary_closed_form, pin_score_closed_form,
     pin_topk_bruteforce, pin_lru_hand_example, pin_lru_properties, pin_two_level_table,
     pin_retrieve_bytes, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
-    pin_first_step_slots, pin_budget_shrink, pin_offload_append,
+    pin_first_step_slots, pin_budget_shrink, pin_offload_append, pin_release_reindex,
+    pin_step_order,
 ]

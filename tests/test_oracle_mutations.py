@@ -49,6 +49,16 @@ MUTATIONS = {
                                    "if req.n_parts == 0:"),
     "retrieve_wrong_head": ("self.pool[gslot] = self.requests[b].host[h, page]",
                             "self.pool[gslot] = self.requests[b].host[0, page]"),
+    # request turnover
+    "release_order_reversed": ("for e in range(self.ndir):\n                s = self.directory[b, h, e]\n                if s != FREE:\n",
+                               "for e in reversed(range(self.ndir)):\n                s = self.directory[b, h, e]\n                if s != FREE:\n"),
+    "release_keeps_budget": ("self.budget[b] = self.C\n        self.requests[b] = None", "self.requests[b] = None"),
+    "release_keeps_segment_entries": ("self.segments[s, :] = FREE\n                    self.seg_live[s] = 0",
+                                      "self.seg_live[s] = 0"),
+    "release_keeps_last_use": ("self.owner[b, :] = FREE\n        self.last_use[b, :] = FREE", "self.owner[b, :] = FREE"),
+    "reindex_without_release": ("        self.release(b)\n        req = Request(", "        req = Request("),
+    # step order
+    "rewound_step_accepted": ("if t < self.last_t:", "if t < self.last_t - 10 ** 6:"),
 }
 
 
