@@ -49,16 +49,18 @@
  * spin_get_stats, spin_snapshot, spin_read_summaries and spin_sync_status
  * synchronise.  Errors a kernel detects (a partition id out of range, an
  * exhausted segment pool) set a device error word that the next synchronising
- * call reports as SPIN_EDEVICE; the residency state is then undefined until
- * the requests are indexed again.  A context is not thread-safe; use one per
- * (compute stream, copy stream) pair.  Streams are hipStream_t values passed
- * as void* (NULL = the null stream).  resolve_evict, attention and every call
- * that changes a request (index, offload, append, release) wait for the
- * latest transfer (spin_retrieve, spin_retrieve_attend or
- * spin_transfer_attend); the context records an event only when another
- * stream has to wait, remembers which stream already waited for that
- * transfer and does not wait there twice, so a stream given to a context
- * must not be destroyed (and its handle reused) before the context is.
+ * call reports as SPIN_EDEVICE (SPIN_ESEGPOOL for an exhausted pool); the
+ * residency state is then undefined until the requests are indexed again,
+ * except after SPIN_DEVERR_STEP alone (see spin_resolve_evict).  A context
+ * is not thread-safe; use one per (compute stream, copy stream) pair.
+ * Streams are hipStream_t values passed as void* (NULL = the null stream).
+ * resolve_evict, attention and every call that changes a request (index,
+ * offload, append, release) wait for the latest transfer (spin_retrieve,
+ * spin_retrieve_attend or spin_transfer_attend); the context records an
+ * event only when another stream has to wait, remembers which stream already
+ * waited for that transfer and does not wait there twice, so a stream given
+ * to a context must not be destroyed (and its handle reused) before the
+ * context is.
  */
 #ifndef SPIN_H
 #define SPIN_H
@@ -84,6 +86,8 @@ extern "C" {
 #define SPIN_DEVERR_PARTITION 1   /* a selected partition id is out of range */
 #define SPIN_DEVERR_SEGPOOL 2     /* no free second-level segment for an insert */
 #define SPIN_DEVERR_STATE 4       /* residency state found inconsistent */
+#define SPIN_DEVERR_STEP 8        /* a resolve's step index was below the last resolved
+                                     step; that resolve changed nothing */
 
 typedef struct spin_ctx spin_ctx;
 
@@ -249,7 +253,13 @@ SPIN_API int spin_select(spin_ctx* ctx, const void* d_q, int32_t* d_sel, float* 
  * Emptied segments return to the shared pool; first inserts into an empty
  * directory range take one.  Writes the block tables and the insert lists
  * spin_retrieve reads (so it waits for the previous spin_retrieve).
- * t must not decrease between calls. */
+ * t must not decrease between calls: the ages t - last_use are never
+ * negative.  A host-side t below the last one this call was given returns
+ * SPIN_EINVAL; a step index below the last resolved step that the host
+ * cannot see (the device-side index of spin_step_at, or a mix of both
+ * forms) sets SPIN_DEVERR_STEP, and that resolve changes no residency state
+ * and no counter: it leaves the step's block tables empty (its heads attend
+ * no pages) and its insert lists empty (nothing is transferred). */
 SPIN_API int spin_resolve_evict(spin_ctx* ctx, const int32_t* d_sel, int32_t t,
                                 int32_t* d_block_table, int32_t* d_block_ntok,
                                 int32_t* d_block_count, void* stream);

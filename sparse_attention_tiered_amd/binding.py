@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so"
 
 SPIN_OK, SPIN_EINVAL, SPIN_ECAPACITY, SPIN_ESEGPOOL, SPIN_EHIP, SPIN_EDEVICE, SPIN_ESTATE = \
     0, -1, -2, -3, -4, -5, -6
-DEVERR_PARTITION, DEVERR_SEGPOOL, DEVERR_STATE = 1, 2, 4
+DEVERR_PARTITION, DEVERR_SEGPOOL, DEVERR_STATE, DEVERR_STEP = 1, 2, 4, 8
 PAGE_BYTES = 32768
 
 

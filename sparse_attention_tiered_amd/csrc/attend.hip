@@ -103,7 +103,7 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
     const int s = bt[e];
     const int n = bntok[e];
     // a malformed entry (caller-supplied table) reads slot 0 with every token masked
-    if ((unsigned)s < (unsigned)(d.B * d.C) && n > 0 && n <= kPageTokens) {
+    if ((unsigned)s < (unsigned)d.pool_slots && n > 0 && n <= kPageTokens) {
       my_slot = s;
       my_nt = n;
     }

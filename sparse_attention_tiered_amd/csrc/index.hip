@@ -29,6 +29,7 @@ __global__ void k_init(Dev d) {
   for (size_t i = tid; i < (size_t)d.B; i += nth) {
     d.free_count[i] = d.C;
     d.budget[i] = d.C;
+    d.last_t[i] = -1;
     d.req_parts[i] = 0;
     d.req_pages[i] = 0;
     d.req_stride[i] = 0;

@@ -11,7 +11,9 @@
 //     64-bin histogram of recency buckets, and whole buckets are reclaimed
 //     from the oldest until the shortfall is covered, mandatory pages never
 //     being candidates.
-// Readings where the pages are silent: bucket = 63 - min(63, t - last_use);
+// Readings where the pages are silent: bucket = 63 - min(63, t - last_use),
+// the step index never decreasing (a resolve below the last resolved step is
+// refused with the error word, nothing changed);
 // exactly the shortfall is evicted, lower slot first inside the cutoff
 // bucket; misses take free slots in ascending order; emptied segments return
 // to the pool in (KV head, directory index) order per request, requests in
@@ -66,12 +68,34 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   constexpr int U = 8;  // slots per thread whose loads are in flight together
   const int freec = d.free_count[b];
   const int budget = d.budget[b];
+  const int t_prev = d.last_t[b];
   int ow0[U], lu0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = tid + 1024 * u;
     ow0[u] = c < C ? owner[c] : -1;
     lu0[u] = c < C ? last[c] : 0;
+  }
+  if (t < t_prev) {
+    // Steps never go back: below the last resolved step some ages t -
+    // last_use would be negative.  Refused before anything changes (the
+    // error word reports it); the step's lists are left empty, so the
+    // kernels after this one do nothing for the request and its heads
+    // attend no pages.  (t_prev is one load of one address: the branch is
+    // uniform over the workgroup.)
+    for (int i = tid; i < Hkv * MB; i += 1024) {
+      btb[i] = -1;
+      bnb[i] = 0;
+    }
+    if (tid < Hkv) bcount[(size_t)b * Hkv + tid] = 0;
+    if (tid <= Hkv) d.head_moff[(size_t)b * (Hkv + 1) + tid] = 0;
+    if (tid == 0) {
+      atomicOr(d.err, kErrStep);
+      d.nmiss[b] = 0;
+      d.nfreed[b] = 0;
+      d.nalloc[b] = 0;
+    }
+    return;
   }
   for (int i = tid; i < (C + 31) / 32; i += 1024) mand[i] = 0;
 
@@ -226,7 +250,9 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         } else if ((mand[c >> 5] >> (c & 31)) & 1u) {
           v = kCodePinned;
         } else if (need > 0) {
-          v = (uint8_t)((kBuckets - 1) - min(kBuckets - 1, t - lu[u]));
+          // (t >= the last resolved step >= last_use: the age is never
+          // negative; clamped all the same, so a code is always a bucket)
+          v = (uint8_t)((kBuckets - 1) - min(kBuckets - 1, max(0, t - lu[u])));
           atomicAdd(&hist[v], 1);
         } else {
           v = kCodePinned;  // nothing is evicted this step
@@ -429,6 +455,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     nalloc = ccarry;
   }
   if (tid == 0) {
+    d.last_t[b] = t;
     d.nalloc[b] = nalloc;
     const int ev = need > 0 ? need : 0;
     if (assigned < nmiss) atomicOr(d.err, kErrState);

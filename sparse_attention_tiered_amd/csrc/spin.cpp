@@ -155,7 +155,8 @@ Derived derive(const spin_config* c) {
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
       directory, segments,
-      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, scores, arrive, miss_tmp, ins,
+      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, last_t, scores, arrive,
+      miss_tmp, ins,
       nmiss,
       freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
       total;
@@ -188,6 +189,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.last_use = take(B * C * sizeof(int));
   L.free_count = take(B * sizeof(int));
   L.budget = take(B * sizeof(int));
+  L.last_t = take(B * sizeof(int));
   L.scores = take(B * Hkv * N * sizeof(float));
   L.arrive = take(B * Hkv * sizeof(int));
   L.miss_tmp = take(B * d.max_mand * sizeof(int4));
@@ -321,6 +323,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.pps = d.pps;
   v.splits_res = d.splits_res;
   v.pps_res = d.pps_res;
+  v.pool_slots = cfg->max_batch * cfg->slots_per_request;
   v.summaries = reinterpret_cast<float*>(w + L.summaries);
   v.part_first = reinterpret_cast<int*>(w + L.part_first);
   v.part_len = reinterpret_cast<int*>(w + L.part_len);
@@ -339,6 +342,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.last_use = reinterpret_cast<int*>(w + L.last_use);
   v.free_count = reinterpret_cast<int*>(w + L.free_count);
   v.budget = reinterpret_cast<int*>(w + L.budget);
+  v.last_t = reinterpret_cast<int*>(w + L.last_t);
   v.scores = reinterpret_cast<float*>(w + L.scores);
   v.arrive = reinterpret_cast<int*>(w + L.arrive);
   v.miss_tmp = reinterpret_cast<int4*>(w + L.miss_tmp);

@@ -25,6 +25,7 @@ constexpr int kRetrieveGrid = 64;      // transfer workgroups (see retrieve.hip)
 constexpr int kErrPartition = 1;       // selected partition id out of range
 constexpr int kErrSegPool = 2;         // no free second-level segment
 constexpr int kErrState = 4;           // residency state inconsistent
+constexpr int kErrStep = 8;            // decode step below the last resolved one
 
 // Device-visible view of the workspace, passed by value to kernels.
 struct Dev {
@@ -32,6 +33,7 @@ struct Dev {
   int B, Hq, Hkv, G, k, Nmax, max_pages, max_ppp, C, n_seg, ndir, max_blocks, max_mand;
   int splits, pps;             // attention over the whole block table: splits per head, pages per split
   int splits_res, pps_res;     // the resident-page pass beside the transfer (fewer, longer splits)
+  int pool_slots;              // pages the pool holds (B * C)
   // index tables (written by spin_index)
   float* summaries;            // [B][Hkv][Nmax][128]
   int* part_first;             // [B][Nmax] first page of partition
@@ -51,6 +53,7 @@ struct Dev {
   int* last_use;               // [B][C]
   int* free_count;             // [B]
   int* budget;                 // [B] cap on resident pages (<= C)
+  int* last_t;                 // [B] step of the request's last resolve (-1: none)
   // per-step scratch
   float* scores;               // [B][Hkv][Nmax]
   int* arrive;                 // [B][Hkv] workgroups of the list done scoring (0 between launches)

@@ -1,12 +1,21 @@
 """Drive the HIP library and the CPU oracle side by side on the same seeded inputs.
 
-Stage parity: at every step the GPU's selection is checked against the
-oracle's (exact, except members whose oracle scores are within 1e-5 of the
+Stage parity (Pair.run): at every step the GPU's selection is checked against
+the oracle's (exact, except members whose oracle scores are within 1e-5 of the
 oracle's k-th score); then the GPU's resolve is fed the *oracle's* selection,
 so a legitimate near-tie cannot cascade into a state mismatch, and the whole
-residency state is compared bit for bit; attention outputs are compared within
-max-abs 2e-3.  Inputs flow from the generator to both sides; nothing the GPU
-produces is fed to the oracle.
+residency state is compared bit for bit; every pool slot the step filled is
+compared byte for byte with the oracle's copy of the host page; attention
+outputs are compared within max-abs 2e-3.  Nothing the GPU produces is fed to
+the oracle.
+
+Whole-step parity (Pair.run_graph, the benchmark's captured one-launch step):
+the GPU selects for itself, so once its selection is shown valid (equal to the
+oracle's, or differing only by near-ties within the window) the oracle resolves
+that selection: the one place where a GPU result enters the oracle, and only
+after it has been checked.  The number of lists where the two selections
+differ (tie flips) is counted and must not exceed the run's `max_flips`
+(0 unless a workload is declared to have near-ties).
 """
 from __future__ import annotations
 
@@ -80,9 +89,12 @@ class Pair:
 
     # ------------------------------------------------------------------ checks
     def n_parts(self, b):
-        """Partitions of request b now (appends add some)."""
-        r = self.oracle.requests[b] if self.oracle is not None else None
-        return r.n_parts if r is not None else len(self.geo.lens[b])
+        """Partitions of request b now (appends add some; a released request
+        has none)."""
+        if self.oracle is None:
+            return len(self.geo.lens[b])
+        r = self.oracle.requests[b]
+        return r.n_parts if r is not None else 0
 
     def check_summaries(self):
         for b in range(self.w.B):
@@ -141,6 +153,35 @@ class Pair:
         assert np.array_equal(self.spin.block_table.cpu().numpy(), slots), t
         assert np.array_equal(self.spin.block_ntok.cpu().numpy(), ntok), t
 
+    def _pool_rows(self, gslots):
+        pool = self.spin.pool.view(torch.int16).view(-1, W.PAGE_ELEMS)
+        idx = torch.as_tensor(np.asarray(gslots, np.int64), device=pool.device)
+        return pool.index_select(0, idx).cpu().numpy().view(np.uint16)
+
+    def check_pool(self, gslots, what="step"):
+        """The GPU pool rows of `gslots` (global slots) equal the oracle's,
+        byte for byte (the retrieved K and V bytes are the host page's)."""
+        gslots = np.asarray(gslots, np.int64)
+        for a in range(0, len(gslots), 4096):   # at most 128 MiB at a time
+            part = gslots[a:a + 4096]
+            got = self._pool_rows(part)
+            want = self.oracle.pool[part]
+            if not np.array_equal(got, want):
+                bad = [int(s) for s, g, o in zip(part, got, want) if not np.array_equal(g, o)]
+                raise AssertionError(f"{what}: pool slots {bad[:8]} ({len(bad)} of {len(part)}) "
+                                     "differ from the host pages they hold")
+        return len(gslots)
+
+    def check_inserted(self, t):
+        """Every slot this step's retrieve filled."""
+        return self.check_pool([g for g, *_ in self.oracle._pending], f"step {t} inserts")
+
+    def check_resident(self):
+        """Every resident slot of every request."""
+        o = self.oracle
+        b_idx, c_idx = np.nonzero(o.owner != -1)
+        return self.check_pool(b_idx * o.C + c_idx, "resident pages")
+
     def check_stats(self):
         st, per = self.spin.stats()
         assert st.error_word == 0, st.error_word
@@ -149,6 +190,31 @@ class Pair:
             assert (per[b, 0], per[b, 1], per[b, 2], per[b, 3]) == \
                 (so["hits"], so["misses"], so["evictions"], so["cutoff"]), (b, per[b], so)
         return st
+
+    # ------------------------------------------------------------------ request turnover
+    def release_request(self, b):
+        """Release request b on both sides."""
+        self.spin.release(b)
+        self.oracle.release(b)
+
+    def reindex_request(self, b, n_tokens, seed):
+        """Index request b again, on both sides, with fresh KV of n_tokens tokens
+        in one-page partitions (N(0,1) bf16, zero padding on a partial last
+        page), whatever it held before."""
+        Hkv = self.w.Hkv
+        lens = [64] * (n_tokens // 64) + ([n_tokens % 64] if n_tokens % 64 else [])
+        pages = len(lens)
+        rng = np.random.default_rng([4242, seed, b])
+        bits = W.to_bf16_bits(rng.standard_normal((Hkv, pages, W.PAGE_ELEMS), dtype=np.float32))
+        if n_tokens % 64:
+            tail = n_tokens % 64
+            bits[:, -1, tail * 128: 64 * 128] = 0
+            bits[:, -1, 64 * 128:].reshape(Hkv, 128, 64)[:, :, tail:] = 0
+        t, u16 = bd.pinned_u16(Hkv * max(pages, 1) * W.PAGE_ELEMS)
+        u16[: bits.size] = bits.reshape(-1)
+        self.spin.index(b, t, n_tokens)
+        self.oracle.index(b, u16, np.asarray(lens, np.int64))
+        self.host[b] = (t, u16)
 
     # ------------------------------------------------------------------ stepping
     def append_token(self, t):
@@ -169,13 +235,16 @@ class Pair:
             gpu = self.host[b][1][: req.host.size].reshape(req.host.shape)
             assert np.array_equal(gpu, req.host), b
 
-    def run(self, steps=None, out_sample=None, check_every=1, seed=0, on_step=None, append=False):
+    def run(self, steps=None, out_sample=None, check_every=1, seed=0, on_step=None, append=False,
+            max_flips=0):
         """Full stage parity for `steps` steps.  out_sample=None compares every
         output; an int compares that many (b, g) pairs per step, chosen with a
-        seeded generator, computed one by one by the oracle."""
+        seeded generator, computed one by one by the oracle.  on_step(t) runs
+        before step t (budget changes, releases, re-indexing on both sides)."""
         steps = self.T if steps is None else steps
         rng = np.random.default_rng(seed)
         total_flips = 0
+        checked = 0
         worst = 0.0
         for t in range(steps):
             if on_step is not None:
@@ -209,9 +278,14 @@ class Pair:
                     err = max(err, float(np.max(np.abs(out[b, g] - want))))
             worst = max(worst, err)
             assert err <= OUT_TOL, (t, err)
+            checked += self.check_inserted(t)
         st = self.check_stats()
+        resident = self.check_resident()
+        self.flips = total_flips
         log(f"[parity] {self.w.name}: {steps} steps, hits={st.hits} misses={st.misses} "
-            f"evictions={st.evictions} tie-flips={total_flips} max|out-oracle|={worst:.2e}")
+            f"evictions={st.evictions} tie-flips={total_flips} max|out-oracle|={worst:.2e} "
+            f"pool bytes checked: {checked} inserts, {resident} resident")
+        assert total_flips <= max_flips, f"{total_flips} lists selected differently within the tie window"
         return st, worst
 
     def valid_selection(self, t, sel_gpu):
@@ -236,21 +310,26 @@ class Pair:
                     flips += 1
         return flips
 
-    def run_graph(self, steps=None, out_sample=None, seed=0):
+    def run_graph(self, steps=None, out_sample=None, seed=0, on_step=None, max_flips=0):
         """The benchmark's timed configuration: one spin_step_at call (the
         transfer and the resident-page attention in one launch, the step index
         on the device) captured in a HIP graph and replayed once per step.
         Each step the oracle takes the GPU's selection once it is shown valid,
-        then the whole residency state, the block tables and sampled outputs
-        are compared."""
+        then the whole residency state, the block tables, the pool slots the
+        step filled and sampled outputs are compared.  on_step(t) runs before
+        step t's replay (eager library calls between replays)."""
         steps = self.T if steps is None else steps
         rng = np.random.default_rng(seed)
+        checked = 0
         S, C = torch.cuda.Stream(), torch.cuda.Stream()
         t_dev = torch.zeros(1, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         graph = None
         flips_total, worst = 0, 0.0
         for t in range(steps):
+            if on_step is not None:
+                on_step(t)
+                torch.cuda.synchronize()
             if t == 0:  # eagerly, then capture the step once
                 self.spin.step_at(self.q_dev, t_dev, stream=S, copy_stream=C)
                 torch.cuda.synchronize()
@@ -283,9 +362,14 @@ class Pair:
                     err = max(err, float(np.max(np.abs(out[b, g] - want))))
             worst = max(worst, err)
             assert err <= OUT_TOL, (t, err)
+            checked += self.check_inserted(t)
         st = self.check_stats()
+        resident = self.check_resident()
+        self.flips = flips_total
         log(f"[parity] {self.w.name} graph: {steps} steps, hits={st.hits} misses={st.misses} "
-            f"evictions={st.evictions} tie-flips={flips_total} max|out-oracle|={worst:.2e}")
+            f"evictions={st.evictions} tie-flips={flips_total} max|out-oracle|={worst:.2e} "
+            f"pool bytes checked: {checked} inserts, {resident} resident")
+        assert flips_total <= max_flips, f"{flips_total} lists selected differently within the tie window"
         return st, worst
 
     def close(self):

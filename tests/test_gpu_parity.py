@@ -504,3 +504,83 @@ def test_runs_are_deterministic(spin_lib, name):
         assert np.array_equal(sa[k], sb[k]), k
     a.close()
     b.close()
+
+
+def _turnover_plan(p):
+    """Mid-run request turnover: a request released (its area and segments go
+    back; it selects and attends nothing meanwhile), later indexed again with
+    new, shorter KV; a request re-indexed in place while it holds pages in
+    several directory ranges; another released near the end."""
+    def hook(t):
+        if t == 5:
+            p.release_request(1)
+        elif t == 9:
+            p.reindex_request(1, 9000, seed=1)
+        elif t == 13:
+            p.reindex_request(2, 12345, seed=2)
+        elif t == 17:
+            p.release_request(0)
+    return hook
+
+
+@pytest.mark.parametrize("form", ["staged", "graph"])
+def test_request_turnover(spin_lib, form):
+    """Request turnover ([XT] part 2: each request's GPU area; part 3: segments
+    taken from and returned to one shared pool): releases and re-indexing
+    between steps, with eviction firing, staged or between replays of the
+    captured one-launch step.  Every step: selection, the whole residency
+    state (directory, segments, live counts, free stack, owner, last_use,
+    free counts) bit for bit, block tables, the pool bytes of every insert,
+    every output; the resident pool at the end."""
+    w = W.variant(W.C4, B=4, ctx=16384, k=16, steps=22, ar_coef=0.5)
+    p = _pair(w, slots=8 * 16 + 40)
+    hook = _turnover_plan(p)
+    if form == "staged":
+        st, _ = p.run(on_step=hook)
+    else:
+        st, _ = p.run_graph(on_step=hook)
+    assert st.evictions > 0
+    per = p.spin.stats()[1]
+    assert per[0, 1] > 0 and per[1, 1] > 0
+    p.close()
+
+
+def test_rewound_step_is_refused(spin_lib):
+    """A step index below the last resolved step would make ages negative.
+    Host-side t: spin_resolve_evict refuses it (SPIN_EINVAL).  A device-side
+    index the host cannot see (spin_step_at after host-indexed steps): the
+    resolve sets SPIN_DEVERR_STEP and changes nothing (residency state,
+    counters), the step attends no pages (zero outputs) and moves no bytes;
+    the oracle refuses the same step before changing anything."""
+    import torch
+    from sparse_attention_tiered_amd import binding as bd
+    w = W.variant(W.C1, name="rewind", steps=8, ar_coef=0.2)
+    p = _pair(w, slots=2 * 8 + 4)
+    p.run(steps=5)
+    before = p.spin.snapshot()
+    st0, per0 = p.spin.stats()
+    with pytest.raises(bd.SpinError) as e:
+        p.spin.resolve_evict(3)
+    assert e.value.code == bd.SPIN_EINVAL
+    S, Cs = torch.cuda.Stream(), torch.cuda.Stream()
+    t_dev = torch.full((1,), 2, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    p.spin.out.fill_(1.0)
+    p.spin.step_at(p.q_dev, t_dev, stream=S, copy_stream=Cs)
+    torch.cuda.synchronize()
+    assert p.spin.sync_status() == bd.SPIN_EDEVICE
+    st1, per1 = p.spin.stats()
+    assert st1.error_word == bd.DEVERR_STEP
+    assert (st1.hits, st1.misses, st1.evictions) == (st0.hits, st0.misses, st0.evictions)
+    assert np.array_equal(per0, per1)
+    after = p.spin.snapshot()
+    for key in before:
+        assert np.array_equal(before[key], after[key]), key
+    assert int(p.spin.block_count.sum().item()) == 0
+    assert torch.count_nonzero(p.spin.out).item() == 0
+    assert int(t_dev.item()) == 3
+    sel_o, _ = p.oracle.select(p.draws.q_bits[2])
+    with pytest.raises(ValueError):
+        p.oracle.resolve_evict(sel_o, 2)
+    p.check_state(2)
+    p.close()
