@@ -81,6 +81,11 @@ extern "C" {
 #define SPIN_EHIP (-4)       /* a HIP runtime call failed; see spin_last_hip_error */
 #define SPIN_EDEVICE (-5)    /* device error word set (see spin_get_stats) */
 #define SPIN_ESTATE (-6)     /* call made in the wrong state (e.g. unindexed request) */
+#define SPIN_ESCRATCH (-7)   /* input too large for spin_attend_noalloc's static scratch */
+
+/* Size of the static device array that holds spin_attend_noalloc's scratch
+ * (one per GPU the library runs on, held until the process ends). */
+#define SPIN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* device error-word bits */
 #define SPIN_DEVERR_PARTITION 1   /* a selected partition id is out of range */
@@ -285,6 +290,37 @@ SPIN_API int spin_retrieve_attend(spin_ctx* ctx, const void* d_q, void* copy_str
 SPIN_API int spin_attend(spin_ctx* ctx, const void* d_q, const int32_t* d_block_table,
                          const int32_t* d_block_ntok, const int32_t* d_block_count,
                          float* d_out, void* stream);
+
+/* spin_attend for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops or harnesses that forbid hipMalloc): no
+ * context and no workspace.  The same attention kernels as spin_attend; the
+ * split partials, their only scratch, live in a static device array of
+ * SPIN_NOALLOC_SCRATCH_BYTES per GPU instead of a caller's workspace.
+ * Allocates nothing: the array's address on the current device is looked up
+ * once (hipGetSymbolAddress) on the first call there, which must therefore
+ * run with the stream's device current.
+ *   d_q          device [batch][num_q_heads][128] bf16, 16-byte aligned
+ *   d_pool       device page pool, [pool_pages][page] (layout above)
+ *   d_block_*    device block tables as spin_resolve_evict writes them,
+ *                [batch][num_kv_heads][max_blocks] global pool slots / valid
+ *                tokens, [batch][num_kv_heads] page counts; entries naming a
+ *                slot outside the pool or 0 / >64 tokens are masked out
+ *   d_out        device [batch][num_q_heads][128] float32, 16-byte aligned
+ *   pages_per_split  as spin_config.attend_pages_per_split (0 = automatic);
+ *                with the same batch, heads, max_blocks and split size the
+ *                results equal spin_attend's bit for bit.
+ * SPIN_EINVAL for bad arguments (batch 1..1024, Hkv 1..16, Hq / Hkv <= 16,
+ * max_blocks 1..4096); SPIN_ESCRATCH, before anything is enqueued, when the
+ * partials (batch * num_q_heads * 2 * splits * 520 bytes, none for a single
+ * split per head) exceed the array.  Stream-ordered, waits for nothing else.
+ * Every call on one GPU shares that GPU's array and leaves its partials
+ * there: calls that overlap in time on one GPU (on different streams or
+ * threads) race and must not be issued. */
+SPIN_API int spin_attend_noalloc(const void* d_q, const void* d_pool, int64_t pool_pages,
+                                 const int32_t* d_block_table, const int32_t* d_block_ntok,
+                                 const int32_t* d_block_count, float* d_out, int32_t batch,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t max_blocks,
+                                 int32_t pages_per_split, void* stream);
 
 /* Retrieve overlapped with attention (the pages' ideal serving envelope
  * hides the transfer; [XT] problem section, Fig. 1).  spin_attend_begin runs

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspin.so"
 
 SPIN_OK, SPIN_EINVAL, SPIN_ECAPACITY, SPIN_ESEGPOOL, SPIN_EHIP, SPIN_EDEVICE, SPIN_ESTATE = \
     0, -1, -2, -3, -4, -5, -6
+SPIN_ESCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DEVERR_PARTITION, DEVERR_SEGPOOL, DEVERR_STATE, DEVERR_STEP = 1, 2, 4, 8
 PAGE_BYTES = 32768
 
@@ -65,6 +67,8 @@ SIGNATURES = {
     "spin_retrieve_attend": (c_int, [_P, _P, _P]),
     "spin_transfer_attend": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "spin_attend_noalloc": (c_int, [_P, _P, c_int64, _P, _P, _P, _P, c_int32, c_int32, c_int32,
+                                    c_int32, c_int32, _P]),
     "spin_attend_begin": (c_int, [_P, _P, _P, _P, _P, _P]),
     "spin_attend_finish": (c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "spin_step": (c_int, [_P, _P, c_int32, _P, _P, _P, _P, _P, _P, _P]),
@@ -333,6 +337,26 @@ class Spin:
             self.close()
         except Exception:
             pass
+
+
+def attend_noalloc(q, pool, block_table, block_ntok, block_count, out, batch=None, Hq=None,
+                   Hkv=None, pages_per_split=0, stream=None):
+    """spin_attend_noalloc over device tensors: q [B][Hq][128] bf16 bits
+    (int16), pool (any dtype, whole 32 KiB pages), block tables
+    [>=batch][Hkv][max_blocks] int32, block_count [>=batch][Hkv] int32, out
+    [>=batch][Hq][128] float32.  batch defaults to the tables' first
+    dimension."""
+    lib = load()
+    Hkv = block_table.shape[1] if Hkv is None else Hkv
+    Hq = q.shape[1] if Hq is None else Hq
+    batch = block_table.shape[0] if batch is None else batch
+    pool_pages = pool.numel() * pool.element_size() // PAGE_BYTES
+    rc = lib.spin_attend_noalloc(_ptr(q), _ptr(pool), pool_pages, _ptr(block_table), _ptr(block_ntok),
+                                 _ptr(block_count), _ptr(out), int(batch), int(Hq), int(Hkv),
+                                 int(block_table.shape[2]), int(pages_per_split), _stream(stream))
+    if rc != SPIN_OK:
+        raise SpinError("spin_attend_noalloc", rc)
+    return out
 
 
 def read_stream(buf, sink, stream=None):

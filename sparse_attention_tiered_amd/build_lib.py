@@ -29,7 +29,7 @@ FLAGS = [
 ]
 
 SOURCES = ["spin.cpp", "index.hip", "select.hip", "resolve.hip", "retrieve.hip", "attend.hip",
-           "diag.hip"]
+           "diag.hip", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

@@ -118,20 +118,28 @@ int check(const spin_config* c) {
   return SPIN_OK;
 }
 
+}  // namespace
+
+int spin::whole_table_pages_per_split(long long work, int pages_per_split) {
+  if (pages_per_split > 0) return (pages_per_split + 3) / 4 * 4;  // whole pages per wave
+  // about one workgroup per CU over the worst-case page count: long-lived
+  // waves keep their page pipeline full (measured best on MI355X)
+  const int pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 255) / 256));
+  return (pps + 3) / 4 * 4;
+}
+
+namespace {
+
 Derived derive(const spin_config* c) {
   Derived d;
   d.G = c->num_q_heads / c->num_kv_heads;
   d.ndir = (c->max_pages + spin::kSegEntries - 1) / spin::kSegEntries;
   d.max_blocks = c->topk * c->max_pages_per_partition;
   d.max_mand = c->num_kv_heads * d.max_blocks;
-  int pps = (c->attend_pages_per_split + 3) / 4 * 4;  // whole pages per wave
+  const long long work = (long long)c->max_batch * c->num_kv_heads * d.max_blocks;
+  const int pps = spin::whole_table_pages_per_split(work, c->attend_pages_per_split);
   int pps_res = pps;
-  if (pps == 0) {
-    // about one workgroup per CU over the worst-case page count: long-lived
-    // waves keep their page pipeline full (measured best on MI355X)
-    const long long work = (long long)c->max_batch * c->num_kv_heads * d.max_blocks;
-    pps = (int)std::min<long long>(64, std::max<long long>(4, (work + 255) / 256));
-    pps = (pps + 3) / 4 * 4;
+  if (c->attend_pages_per_split == 0) {
     // the resident-page pass runs beside the transfer, which it must only
     // keep up with: about half a workgroup per CU, each streaming pages
     // while the PCIe pulls are in flight, contends less with them (128K
@@ -861,6 +869,7 @@ SPIN_API const char* spin_strerror(int code) {
     case SPIN_EHIP: return "HIP runtime error";
     case SPIN_EDEVICE: return "device error word set";
     case SPIN_ESTATE: return "call made in the wrong state";
+    case SPIN_ESCRATCH: return "input too large for the static scratch of spin_attend_noalloc";
     default: return "unknown error";
   }
 }

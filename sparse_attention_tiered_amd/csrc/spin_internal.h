@@ -82,6 +82,11 @@ struct Dev {
   long long q_step;            // elements between consecutive steps' queries
 };
 
+// Pages per split of the whole-table attention pass: pages_per_split rounded
+// up to whole pages per wave, or (0) about one workgroup per CU over `work`,
+// the worst-case page count of the batch (B * Hkv * max_blocks).
+int whole_table_pages_per_split(long long work, int pages_per_split);
+
 // launchers (each returns the hipError_t of its launch)
 // The queries of this step: q itself, or q + t * q_step with a device-side step index.
 __device__ __forceinline__ const uint16_t* step_queries(const Dev& d, const uint16_t* q) {

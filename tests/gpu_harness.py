@@ -264,6 +264,7 @@ class Pair:
                 self.check_blocks(t, blocks)
             self.spin.retrieve()
             self.oracle.retrieve()
+            self.last_blocks = blocks
             out = self.spin.attend(q).cpu().numpy()
             qb = self.draws.q_bits[t]
             if out_sample is None:
