@@ -2,16 +2,35 @@
 
 A step is one pass of the whole decode path for a batch: select (score +
 top-k), two-level resolve with bucketed-LRU eviction, retrieve of missed pages
-from pinned host memory (on a second stream), and paged sparse attention.
-Inputs (host KV, queries for every step) are resident before the timed
-region.  Runs step 0 (all misses) with stage events, W-1 more warm-up steps,
-K timed steps (`value`: replays of one captured HIP graph of the
-device-indexed whole-step call, as a serving loop would run them; --eager
-calls spin_step per step instead), K more steps with an event between stages
-(stage times, the transfer's rate), then
-isolated replays of select and attention on the last step's data, warm and
-after a 512 MB read that evicts the memory-side cache (cold).  Prints one
-JSON line.
+from pinned host memory, and paged sparse attention.  Inputs (host KV, queries
+for every step) are resident before the timed region.
+
+Steps are numbered from 0 (every mandatory page a miss).  The timed window is
+K consecutive steps: by default every configured step of the workload after a
+warm-up of min(8, steps/4) (the 128K pressure workload: steps 8-127); with
+--steps K, the last K configured steps, never starting before step W (the
+query stream continues past the configured steps when W + K exceeds them).
+Two contexts are indexed from the same pinned host KV and driven through the
+same steps; the path is deterministic, so both pass through the same states
+(their counters are compared):
+
+  context A  the steps before the window as untimed warm-up, then the window
+             as replays of one captured HIP graph of the device-indexed
+             whole-step call, back to back, with a timing event between
+             replays: `ms_per_step` is the median step of the window and
+             `value` = B * Hq / ms_per_step (the mean is reported beside it);
+  context B  the same warm-up, then the same window with an event between
+             stages on the stream each stage runs on: stage times per step,
+             the transfer launch's duration (the roofline of the dominant
+             kernel) and the device counters after each step (its bytes);
+             then isolated replays of select, attention and the transfer on
+             the window's last step, warm and after a 512 MB read that evicts
+             the memory-side cache (cold).
+
+Warm-up steps run the serial form of the step (the transfer, then attention),
+so the one-launch transfer kernel runs only inside the two windows and a
+kernel trace of this command averages it over exactly those steps.  Prints
+one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config c4] [--gpus 1]
 """
@@ -114,39 +133,74 @@ def select_kernels(B, Hkv, max_parts):
     return ["k_score", "k_topk"]
 
 
-def cpu_baseline(w, geo, draws, host_np, budget_s=20.0):
-    """The CPU oracle as it stands, on the same workload from step 0, for as
-    many whole decode steps as fit in about budget_s seconds (at least one)."""
+
+
+def timed_window(configured_steps, warmup=None, steps=None):
+    """(start, end, steps to draw): the timed steps are start .. end-1.  By
+    default every configured step after a warm-up of min(8, steps / 4); with
+    an explicit step count K, the last K configured steps, never starting
+    before the warm-up (the query stream then runs past the configured
+    steps)."""
+    warm = warmup if warmup is not None else min(8, configured_steps // 4)
+    K = steps if steps is not None else configured_steps - warm
+    start = max(warm, configured_steps - K)
+    return start, start + K, max(configured_steps, start + K)
+
+
+def cpu_baseline(w, geo, draws, host_np, start, end, budget_s=20.0):
+    """The CPU oracle as it stands, on the same workload and the same steps as
+    the GPU's timed window: steps 0 .. start-1 bring its state there untimed
+    (select, resolve/evict and retrieve only: attention changes no state),
+    then whole decode steps from `start` are timed, as many as fit in about
+    budget_s seconds (at least one, at most the window).  BLAS is held to one
+    thread and the control flow is single-threaded Python, so the oracle uses
+    exactly one core."""
+    import contextlib
+
     from oracle.spin_oracle import SpinOracle
     try:
-        from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas_default = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        one_thread = threadpool_limits(limits=1)
     except Exception:  # noqa: BLE001
-        blas = 1
-    n_seg = min(w.B * w.slots_per_request, w.B * w.Hkv * ((geo.max_pages + 63) // 64))
-    o = SpinOracle(w.B, w.Hq, w.Hkv, w.k, w.slots_per_request, geo.max_pages, n_seg)
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        o.index(b, host_np[b], geo.lens[b])
-    t_index = time.perf_counter() - t0
-    steps, t0 = 0, time.perf_counter()
-    while True:
-        o.step(draws.q_bits[steps], steps)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or steps >= draws.q_bits.shape[0]:
-            break
-    return {"value": w.B * w.Hq * steps / el, "unit": "head-tokens/s", "cores": int(blas),
-            "kind": "oracle",
-            "sample": f"first {steps} decode steps of {w.name} (full batch), float64 numpy "
-                      f"oracle, {el:.1f} s; index (not timed) took {t_index:.1f} s"}
+        blas_default, one_thread = None, None
+    with one_thread if one_thread is not None else contextlib.nullcontext():
+        n_seg = min(w.B * w.slots_per_request, w.B * w.Hkv * ((geo.max_pages + 63) // 64))
+        o = SpinOracle(w.B, w.Hq, w.Hkv, w.k, w.slots_per_request, geo.max_pages, n_seg)
+        t0 = time.perf_counter()
+        for b in range(w.B):
+            o.index(b, host_np[b], geo.lens[b])
+        for t in range(start):
+            sel, _ = o.select(draws.q_bits[t])
+            o.resolve_evict(sel, t)
+            o.retrieve()
+        t_setup = time.perf_counter() - t0
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            o.step(draws.q_bits[start + steps], start + steps)
+            steps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or start + steps >= end:
+                break
+    limit = one_thread
+    return {"value": w.B * w.Hq * steps / el, "unit": "head-tokens/s",
+            "cores": 1 if limit is not None else blas_default, "kind": "oracle",
+            "host_cores_available": len(os.sched_getaffinity(0)),
+            "blas_threads_default": blas_default, "blas_threads_used": 1 if limit is not None else blas_default,
+            "steps_timed": [start, start + steps - 1],
+            "sample": f"decode steps {start}-{start + steps - 1} of {w.name} (full batch; the first "
+                      f"{steps} steps of the GPU's timed window), float64 numpy oracle, one thread, "
+                      f"{el:.1f} s; index and steps 0-{start - 1} (untimed, no attention) took "
+                      f"{t_setup:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=120)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: every configured step after the warm-up)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the window, at least (default: min(8, steps / 4))")
     ap.add_argument("--config", default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -177,44 +231,55 @@ def main():
     from sparse_attention_tiered_amd import binding as bd
     from sparse_attention_tiered_amd import workload as W
 
-    if args.warmup < 1:
-        ap.error("--warmup must be at least 1 (step 0 is timed on its own)")
-    use_graph = not args.eager and not args.no_overlap
     w = W.get(args.config)
-    n_steps = max(w.steps, args.warmup + 2 * args.steps)
+    T = w.steps
+    warm = args.warmup if args.warmup is not None else min(8, T // 4)
+    if warm < 1:
+        ap.error("--warmup must be at least 1 (step 0 is timed on its own)")
+    if args.steps is not None and args.steps < 1:
+        ap.error("--steps must be at least 1")
+    start, end, n_steps = timed_window(T, warm, args.steps)   # the window: steps start .. end-1
+    K = end - start
+    use_graph = not args.eager and not args.no_overlap
+    overlap = not args.single_stream and not args.no_overlap
+
     t0 = time.time()
     geo = W.geometry(w)
     draws = W.draw_queries(w, geo, n_steps)
     host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
     W.fill_all(w, geo, draws, [h[1] for h in host])
     log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f}s "
-        f"({sum(h[0].numel() * 2 for h in host) / 1e9:.2f} GB pinned host KV)")
+        f"({sum(h[0].numel() * 2 for h in host) / 1e9:.2f} GB pinned host KV); "
+        f"timed window: steps {start}-{end - 1}")
     cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts, geo.max_pages, w.k, w.slots_per_request,
                          max_pages_per_partition=geo.max_ppp, attend_pages_per_split=args.pps,
                          host_segments=args.host_segments)
-    spin = bd.Spin(cfg)
-    t0 = time.time()
-    for b in range(w.B):
-        spin.index(b, host[b][0], w.ctx[b], geo.lens[b] if w.var_len is not None else None)
-    log(f"[bench] index (summaries over PCIe) {time.time() - t0:.2f}s; attend splits={spin.splits}")
     budget = w.slots_per_request
     if args.budget_ratio is not None:
         mand = w.Hkv * w.k * geo.max_ppp
         budget = min(w.slots_per_request, int(round(mand * (1 + args.budget_ratio))))
+    ctx = []
+    for name in ("A", "B"):
+        spin = bd.Spin(cfg)
+        t0 = time.time()
         for b in range(w.B):
-            spin.set_budget(b, budget)
+            spin.index(b, host[b][0], w.ctx[b], geo.lens[b] if w.var_len is not None else None)
+            if budget != w.slots_per_request:
+                spin.set_budget(b, budget)
+        log(f"[bench] context {name}: index (summaries over PCIe) {time.time() - t0:.2f}s; "
+            f"attend splits={spin.splits}")
+        ctx.append(spin)
+    A, Bx = ctx
     q = torch.from_numpy(draws.q_bits.view(np.int16)).to("cuda")
     S = torch.cuda.Stream()  # a created stream: HIP graphs cannot capture the null stream
     Cs = S if args.single_stream else torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    overlap = not args.single_stream and not args.no_overlap
-
-    def step(t, ev=None):
+    def staged(spin, t, ev=None, ovl=overlap):
         # the stages of spin_step, one call each
-        # events (instrumented pass only): 0 start, 1 select done, 2 resolve
-        # done; 3 / 4 around the transfer (with the resident-page attention
-        # in the same launch when overlapped); 6 attention done
+        # events: 0 start, 1 select done, 2 resolve done; 3 / 4 around the
+        # transfer (with the resident-page attention in the same launch when
+        # overlapped); 6 attention done
         if ev is not None:
             ev[0].record(S)
         spin.select(q[t], stream=S)
@@ -223,7 +288,7 @@ def main():
         spin.resolve_evict(t, stream=S)
         if ev is not None:
             ev[2].record(S)
-        if overlap:
+        if ovl:
             # as the whole-step call: one launch pulls the missed pages
             # (attending each on arrival) while it attends the resident ones
             if ev is not None:
@@ -231,7 +296,6 @@ def main():
             spin.transfer_attend(q[t], stream=S)
             if ev is not None:
                 ev[4].record(S)
-                ev[5].record(S)
             spin.attend_finish(q[t], stream=S)
         else:
             if ev is not None:
@@ -241,87 +305,96 @@ def main():
             spin.retrieve(copy_stream=Cs)
             if ev is not None:
                 ev[4].record(Cs)
-                ev[5].record(S)
             spin.attend(q[t], stream=S)
         if ev is not None:
             ev[6].record(S)
 
-    # step 0 (every mandatory page a miss) with stage events, reported on its own
+    def warm_up(spin, t_from):
+        # untimed steps in the serial form (transfer, then attention)
+        for t in range(t_from, start):
+            spin.step(q[t], t, stream=S, copy_stream=S)
+
+    # ---- context A: step 0 (every mandatory page a miss, serial form, stage
+    # events), the rest of the warm-up, then the timed window
     ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-    step(0, ev0)
+    staged(A, 0, ev0, ovl=False)
     torch.cuda.synchronize()
-    st_s0, _ = spin.stats()
+    st_s0, _ = A.stats()
     s0_ret_ms = ev0[3].elapsed_time(ev0[4])
-    step0 = {"ms": ev0[0].elapsed_time(ev0[6]), "misses": st_s0.misses,
+    step0 = {"ms": ev0[0].elapsed_time(ev0[6]), "misses": st_s0.misses, "kernel": "k_retrieve",
              "retrieve_ms": s0_ret_ms,
              "retrieve_GBps": st_s0.misses * PAGE_BYTES / (s0_ret_ms * 1e-3) / 1e9}
-    for t in range(1, args.warmup):
-        step(t)
+    warm_up(A, 1)
     torch.cuda.synchronize()
-    st0, _ = spin.stats()
-    K = args.steps
-    # timed pass: the steps alone (a timing event costs the GPU several
-    # microseconds, so the per-stage events go in a second pass)
+    stA0, _ = A.stats()
     graph = None
     if use_graph:
         # one step captured with the device-side step index, replayed K times
-        t_dev = torch.full((1,), args.warmup, dtype=torch.int32, device="cuda")
+        t_dev = torch.full((1,), start, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=S):
-            spin.step_at(q, t_dev, stream=S, copy_stream=Cs)
+            A.step_at(q, t_dev, stream=S, copy_stream=Cs)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(S)
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evt[0].record(S)
     for i in range(K):
+        t = start + i
         if graph is not None:
             with torch.cuda.stream(S):
                 graph.replay()
         elif overlap or args.single_stream:
-            # the library's whole-step call (one entry into the library)
-            spin.step(q[args.warmup + i], args.warmup + i, stream=S, copy_stream=Cs)
+            A.step(q[t], t, stream=S, copy_stream=Cs)  # the library's whole-step call
         else:
-            step(args.warmup + i)
-    end.record(S)
+            staged(A, t)
+        evt[i + 1].record(S)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    st1, _ = spin.stats()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / K
+    stA1, _ = A.stats()
+    step_times = [evt[i].elapsed_time(evt[i + 1]) for i in range(K)]
+    total_ms = evt[0].elapsed_time(evt[K])
+    ms_per_step = float(np.median(step_times))
+    mean_ms = total_ms / K
     value = w.B * w.Hq / (ms_per_step * 1e-3)
 
-    # instrumented pass: the next K steps with an event between stages
-    # (the device counters are read after every step: the transfer's bytes per step)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    # ---- context B: the same warm-up, then the same window with stage events
+    staged(Bx, 0, None, ovl=False)
+    warm_up(Bx, 1)
     torch.cuda.synchronize()
-    step_miss = []
-    prev = st1.misses
+    stB0, _ = Bx.stats()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
+    step_miss, step_hit = [], []
+    prev_m, prev_h = stB0.misses, stB0.hits
     for i in range(K):
-        step(args.warmup + K + i, evs[i])
-        st_i, _ = spin.stats()
-        step_miss.append(st_i.misses - prev)
-        prev = st_i.misses
-    st2 = st_i
-    stage = {"select": 0.0, "resolve_evict": 0.0, "retrieve": 0.0, "attend": 0.0}
-    instr_ms = 0.0
-    step_ms, ret_ms = [], []
+        staged(Bx, start + i, evs[i])
+        st_i, _ = Bx.stats()
+        step_miss.append(st_i.misses - prev_m)
+        step_hit.append(st_i.hits - prev_h)
+        prev_m, prev_h = st_i.misses, st_i.hits
+    stB1 = st_i
+    same_steps = ((stA1.hits - stA0.hits, stA1.misses - stA0.misses, stA1.evictions - stA0.evictions) ==
+                  (stB1.hits - stB0.hits, stB1.misses - stB0.misses, stB1.evictions - stB0.evictions)
+                  and stA0.misses == stB0.misses)
+    if not same_steps:
+        log("[bench] WARNING: the two contexts' counters differ over the window")
+    stage = {"select": [], "resolve_evict": [], "retrieve": [], "attend": []}
+    instr_step = []
     for e in evs:
-        step_ms.append(e[0].elapsed_time(e[6]))
-        ret_ms.append(e[3].elapsed_time(e[4]))
-        stage["select"] += e[0].elapsed_time(e[1])
-        stage["resolve_evict"] += e[1].elapsed_time(e[2])
-        stage["retrieve"] += e[3].elapsed_time(e[4])
+        instr_step.append(e[0].elapsed_time(e[6]))
+        stage["select"].append(e[0].elapsed_time(e[1]))
+        stage["resolve_evict"].append(e[1].elapsed_time(e[2]))
+        stage["retrieve"].append(e[3].elapsed_time(e[4]))
         # after the transfer: the merge (or the whole attention without overlap)
-        stage["attend"] += max(e[4].elapsed_time(e[6]), 0.0)
-        instr_ms += e[0].elapsed_time(e[6])
-    stage_ms = {k: v / K for k, v in stage.items()}
+        stage["attend"].append(max(e[4].elapsed_time(e[6]), 0.0))
+    stage_ms = {k: float(np.mean(v)) for k, v in stage.items()}
+    ret_ms = stage["retrieve"]
 
-    # kernel-isolated replays on the last step's live data (select and
+    # ---- kernel-isolated replays on the window's last step (select and
     # attention only read the residency state), so the HBM rooflines are not
     # mixed with the transfer that overlaps them inside a step
-    last = args.warmup + 2 * K - 1
+    spin = Bx
+    last = end - 1
     reps = 10
     iso = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
@@ -340,7 +413,7 @@ def main():
     # pages to the same slots (idempotent), no attention beside it, so the
     # rate is the transfer's own for this many pages
     iso_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    spin.retrieve(copy_stream=S)  # untimed: the kernel's first launch in the process loads it
+    spin.retrieve(copy_stream=S)
     iso_r[0].record(S)
     for _ in range(reps):
         spin.retrieve(copy_stream=S)
@@ -376,26 +449,27 @@ def main():
     # valid tokens of every (request, KV head) block table of the last step
     attended_tokens = int(spin.block_ntok.sum().item())
 
-    hits = st1.hits - st0.hits
-    misses = st1.misses - st0.misses
-    evictions = st1.evictions - st0.evictions
+    hits = stA1.hits - stA0.hits
+    misses = stA1.misses - stA0.misses
+    evictions = stA1.evictions - stA0.evictions
     # algorithmic bytes per launch (one step)
     attend_bytes = (hits + misses) * PAGE_BYTES / K + w.B * w.Hq * 128 * (2 + 4)
     n_parts = sum(len(l) for l in geo.lens)
     score_bytes = w.Hkv * n_parts * 128 * 4 + w.B * w.Hq * 128 * 2 + w.Hkv * n_parts * 4
-    # the transfer's bytes per launch in the instrumented pass it is timed in
-    retrieve_bytes = (st2.misses - st1.misses) * PAGE_BYTES / K
+    # the transfer's bytes per launch over the window (the same steps in both
+    # contexts), and its duration per launch measured in context B
+    retrieve_bytes = sum(step_miss) * PAGE_BYTES / K
     last_step_bytes = step_miss[-1] * PAGE_BYTES
     # everything the transfer launch itself reads and writes: each missed page
     # read over the link and written to its slot; with the overlap, also the
     # resident pages it attends (read once) and the queries
-    instr_hits = (st2.hits - st1.hits) / K
     launch_bytes = 2 * retrieve_bytes
     if overlap:
-        launch_bytes += instr_hits * PAGE_BYTES + w.B * w.Hq * 128 * 2
+        launch_bytes += sum(step_hit) / K * PAGE_BYTES + w.B * w.Hq * 128 * 2
     iso_attend_bytes = last_pages * PAGE_BYTES + w.B * w.Hq * 128 * (2 + 4)
     link = pcie_link()
     memcpy_gbs = memcpy_h2d_gbs()
+    transfer_ms = float(np.mean(ret_ms))
     rl = {
         "attend": {"bound": "hbm",
                    "achieved": iso_attend_bytes / (iso_attend_ms * 1e-3) / 1e9,
@@ -408,8 +482,10 @@ def main():
                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": score_bytes,
                    "kernels": select_kernels(w.B, w.Hkv, geo.max_parts)},
         "retrieve": {"bound": "pcie",
-                     "achieved": retrieve_bytes / (stage_ms["retrieve"] * 1e-3) / 1e9 if retrieve_bytes else 0.0,
-                     "launch_ms": stage_ms["retrieve"],
+                     "achieved": retrieve_bytes / (transfer_ms * 1e-3) / 1e9 if retrieve_bytes else 0.0,
+                     "launch_ms": transfer_ms,
+                     "launch_ms_median": float(np.median(ret_ms)),
+                     "steps": [start, end - 1],
                      "peak": PCIE_GEN5_X16_GBS, "unit": "GB/s", "bytes_per_launch": retrieve_bytes,
                      "launch_work_bytes": launch_bytes,
                      "kernels": ["k_transfer_attend" if overlap else "k_retrieve"]},
@@ -446,7 +522,7 @@ def main():
     roof["traffic"] = rl[dominant]["traffic"]
     line = {
         "metric": "sparse decode head-tokens/s + achieved HBM GB/s vs peak; H2D GB/s vs PCIe",
-        "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": K, "warmup": start,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
@@ -456,9 +532,16 @@ def main():
                    "segment_tables": "host" if args.host_segments else "gpu",
                    "parallelism": "single-gpu"},
         "roofline": roof,
+        "timed_steps": [start, end - 1],
+        "configured_steps": T,
+        "ms_per_step_is": "median of the window's steps",
+        "mean_ms_per_step": mean_ms,
+        "step_ms_p10_p90": [float(np.percentile(step_times, 10)), float(np.percentile(step_times, 90))],
+        "value_at_mean": w.B * w.Hq / (mean_ms * 1e-3),
         "stages_ms": stage_ms,
-        "ms_per_step_instrumented": instr_ms / K,
-        "median_step_ms_instrumented": float(np.median(step_ms)),
+        "instrumented_steps": [start, end - 1],
+        "median_step_ms_instrumented": float(np.median(instr_step)),
+        "contexts_agree_over_window": bool(same_steps),
         "attended_head_tokens_per_s": attended_tokens / (iso_attend_ms * 1e-3),
         "overlap_retrieve_attend": overlap,
         "timed_as_graph_replays": graph is not None,
@@ -472,7 +555,7 @@ def main():
     # metadata footprint (two-level table vs a flat one), measured now and
     # projected to a server provisioned for the worst case: 256 requests of
     # 1M tokens on every layer of the model, with this run's live working set
-    md = spin.metadata()
+    md = A.metadata()
     prov_batch, prov_ctx = 256, 1 << 20
     prov_pages = prov_ctx // 64
     seg_b = 64 * 4 + 8
@@ -501,11 +584,13 @@ def main():
         torch.cuda.synchronize()
         line["copy_calibration"] = {"kernel": "elementwise neg (torch)", "bytes_read": 4 * n,
                                     "bytes_written": 4 * n, "launches": 3}
+    A.close()
+    Bx.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        line["cpu_baseline"] = cpu_baseline(w, geo, draws, [h[1] for h in host], args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline(w, geo, draws, [h[1] for h in host], start, end,
+                                            args.cpu_budget)
     print(json.dumps(line), flush=True)
-    spin.close()
 
 
 if __name__ == "__main__":

@@ -45,3 +45,36 @@ def test_counter_traffic_needs_matching_sources(tmp_path, monkeypatch):
     (prof / "cx_hbm_counters.md").write_text(stale + "\n")
     assert bench.counter_traffic("cx", "attend", 1000.0) is None
     assert bench.counter_traffic("nope", "attend", 1000.0) is None
+
+
+def test_timed_window():
+    """The default window is every configured step after min(8, steps / 4)
+    warm-up steps; an explicit K times the last K configured steps, not
+    before the warm-up; past the configured steps the queries continue."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.timed_window(128) == (8, 128, 128)         # the 128K workloads: steps 8-127
+    assert bench.timed_window(64) == (8, 64, 64)
+    assert bench.timed_window(16) == (4, 16, 16)            # min(8, 16 / 4)
+    assert bench.timed_window(128, 5, 20) == (108, 128, 128)
+    assert bench.timed_window(128, 8, 120) == (8, 128, 128)
+    assert bench.timed_window(64, 8, 120) == (8, 128, 128)  # runs past the configured 64
+
+
+def test_cpu_baseline_runs_the_oracle_on_the_window():
+    """The CPU baseline (the oracle, one thread) on the tiny workload: state
+    brought to the window's first step untimed, then timed whole steps from
+    there, never past the window."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+
+    import bench
+    from sparse_attention_tiered_amd import workload as W
+    w = W.get("c1")
+    geo = W.geometry(w)
+    draws = W.draw_queries(w, geo)
+    host = [np.zeros(w.Hkv * geo.pages[b] * W.PAGE_ELEMS, np.uint16) for b in range(w.B)]
+    W.fill_all(w, geo, draws, host)
+    r = bench.cpu_baseline(w, geo, draws, host, 4, 7, budget_s=30.0)
+    assert r["cores"] == 1 and r["blas_threads_used"] == 1 and r["kind"] == "oracle"
+    assert r["steps_timed"] == [4, 6] and r["value"] > 0
