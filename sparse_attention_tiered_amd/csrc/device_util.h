@@ -13,15 +13,51 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Cross-lane moves on the VALU (DPP), not through the LDS crossbar: a
+// wave64 is four rows of 16 lanes; row_shr:n (control 0x110 + n) reads lane
+// i - n of the same row, row_bcast:15 / row_bcast:31 (0x142 / 0x143) read
+// the last lane of the row before / of row 1.  Lanes whose source lies
+// outside the row, or whose row is masked off, receive `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside
+// each row (shifts 1, 2, 4, 8), then row 0's total into row 1 and row 2's
+// into row 3, then row 1's (now rows 0-1) into rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(v, o, 64);
-    if (lane >= o) v += n;
-  }
+  v += dpp_move<0x111, 0xf>(0, v);
+  v += dpp_move<0x112, 0xf>(0, v);
+  v += dpp_move<0x114, 0xf>(0, v);
+  v += dpp_move<0x118, 0xf>(0, v);
+  v += dpp_move<0x142, 0xa>(0, v);
+  v += dpp_move<0x143, 0xc>(0, v);
   return v;
+}
+
+// Largest / smallest value over the 64 lanes of a wave, in every lane (the
+// same steps as wave_incl_scan with max / min; lane 63 ends with the whole
+// wave's, read back as a scalar).
+__device__ __forceinline__ float wave_max(float v) {
+  const int lo = (int)0xFF800000u;  // -inf: neutral for max
+  v = fmaxf(v, __int_as_float(dpp_move<0x111, 0xf>(lo, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x112, 0xf>(lo, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x114, 0xf>(lo, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x118, 0xf>(lo, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x142, 0xa>(lo, __float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp_move<0x143, 0xc>(lo, __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_min(float v) {
+  const int hi = (int)0x7F800000u;  // +inf: neutral for min
+  v = fminf(v, __int_as_float(dpp_move<0x111, 0xf>(hi, __float_as_int(v))));
+  v = fminf(v, __int_as_float(dpp_move<0x112, 0xf>(hi, __float_as_int(v))));
+  v = fminf(v, __int_as_float(dpp_move<0x114, 0xf>(hi, __float_as_int(v))));
+  v = fminf(v, __int_as_float(dpp_move<0x118, 0xf>(hi, __float_as_int(v))));
+  v = fminf(v, __int_as_float(dpp_move<0x142, 0xa>(hi, __float_as_int(v))));
+  v = fminf(v, __int_as_float(dpp_move<0x143, 0xc>(hi, __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64,

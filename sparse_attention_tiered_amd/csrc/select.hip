@@ -143,11 +143,8 @@ __device__ void topk_select(TopkLds<NT>& L, float* vals, int n, int k, float mn,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int i = tid; i < kTopkBins; i += NT) L.hist[i] = 0;
   for (int i = tid; i < (n + 31) / 32; i += NT) L.chosen[i] = 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
   if (lane == 0) {
     L.rmin[wv] = mn;
     L.rmax[wv] = mx;
@@ -294,6 +291,182 @@ __device__ void topk_select(TopkLds<NT>& L, float* vals, int n, int k, float mn,
     if (((L.chosen[i >> 5] >> (i & 31)) & 1u) && pos < k) out[pos++] = i;
 }
 
+// The same selection in fewer dependent steps (each step of a 1024-thread
+// workgroup is a barrier and an LDS round trip, which is what the top-k's time
+// goes into): the scores are spread over 256 value bins linearly between the
+// list's minimum and maximum, so one wave finds the boundary bin with a single
+// prefix scan; the bins above it are taken, the boundary bin's members
+// (usually a handful) are ranked exactly, and the chosen ids are written in
+// ascending order from a popcount prefix over the chosen bitmask.  A crowded
+// boundary bin (more than kTopkCand members: many equal or nearly equal
+// scores) goes to topk_select, which splits it further.
+constexpr int kCoarseBins = 256;
+
+struct BinMap {
+  float mn, scale;
+};
+
+// Monotone map of [mn, mx] onto the coarse bins; a range too narrow for a
+// finite scale puts every score into bin 0.  Clamped in float before the
+// conversion, so any input lands in a valid bin.
+__device__ __forceinline__ BinMap coarse_map(float mn, float mx) {
+  float scale = (float)kCoarseBins / (mx - mn);
+  if (!(scale < 3.0e38f)) scale = 0.f;
+  return BinMap{mn, scale};
+}
+__device__ __forceinline__ int coarse_bin(float v, BinMap m) {
+  return (int)fminf(fmaxf((v - m.mn) * m.scale, 0.f), (float)(kCoarseBins - 1));
+}
+
+// Clears what the coarse selection accumulates into: the first kCoarseBins
+// histogram entries, the chosen bitmask over n ids and the member counter.
+// Must be followed by a barrier before the histogram is filled.
+template <int NT>
+__device__ __forceinline__ void topk_coarse_clear(TopkLds<NT>& L, int n) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kCoarseBins; i += NT) L.hist[i] = 0;
+  for (int i = tid; i < (n + 31) / 32; i += NT) L.chosen[i] = 0;
+  if (tid == 0) L.sh[2] = 0;
+}
+
+// The selection once the n > k scores sit in vals (LDS) and each is counted
+// once in L.hist[coarse_bin(score, m)], with a barrier passed since (and the
+// bitmask and member counter cleared before it).  mn, mx: the list's range,
+// for the fallback.  Writes the k chosen ids, ascending, to out.  Every
+// thread of the workgroup calls it.
+template <int NT>
+__device__ void topk_coarse(TopkLds<NT>& L, float* vals, int n, int k, BinMap m, float mn, float mx,
+                            int* out) {
+  static_assert(NT >= kTopkCand && kCoarseBins == 4 * 64, "four bins per lane of one wave");
+  const int tid = threadIdx.x, lane = tid & 63;
+  // 1. the boundary bin: counts from the top, four bins per lane of wave 0
+  if (tid < 64) {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = L.hist[kCoarseBins - 1 - 4 * lane - j];
+      sum += c[j];
+    }
+    const int inc = wave_incl_scan(sum);
+    const int lead = __ffsll((long long)__ballot(inc >= k)) - 1;  // exists: the total is n > k
+    if (lane == lead) {
+      int above = inc - sum, b = kCoarseBins - 1 - 4 * lane, mem = c[0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        b = kCoarseBins - 1 - 4 * lane - j;
+        mem = c[j];
+        if (above + c[j] >= k) break;
+        above += c[j];
+      }
+      L.sh[0] = b;
+      L.sh[1] = above;
+      L.sh[3] = mem;
+    }
+  }
+  __syncthreads();
+  const int cut = L.sh[0];
+  const int need = k - L.sh[1];  // >= 1: taken from the boundary bin
+  const int mem = L.sh[3];       // its members
+  if (mem > kTopkCand) {         // (uniform over the workgroup)
+    topk_select<NT>(L, vals, n, k, mn, mx, out);
+    return;
+  }
+  // 2. every score above the boundary bin is taken; the bin's members listed
+  for (int i = tid; i < n; i += NT) {
+    const float v = vals[i];
+    const int bk = coarse_bin(v, m);
+    if (bk > cut) {
+      atomicOr(&L.chosen[i >> 5], 1u << (i & 31));
+    } else if (bk == cut) {
+      const int slot = atomicAdd(&L.sh[2], 1);
+      L.cand[slot] = i;
+      L.candv[slot] = v;
+    }
+  }
+  __syncthreads();
+  // 3. the members ranked exactly: higher score first, the lower id on a tie.
+  //    Up to 64 members sit in wave 0's lanes and are compared through
+  //    readlane (no LDS round trip per comparison), and the same wave goes on
+  //    to step 4 with no barrier between; more members take one thread each.
+  if (mem > 64) {
+    if (tid < mem) {
+      const int me = L.cand[tid];
+      const float v = L.candv[tid];
+      int rank = 0;
+      for (int j = 0; j < mem; ++j) {
+        const int o = L.cand[j];
+        const float w = L.candv[j];
+        rank += (w > v || (w == v && o < me)) ? 1 : 0;
+      }
+      if (rank < need) atomicOr(&L.chosen[me >> 5], 1u << (me & 31));
+    }
+    __syncthreads();
+  } else if (tid < 64) {
+    const int me = lane < mem ? L.cand[lane] : 0;
+    const float v = lane < mem ? L.candv[lane] : 0.f;
+    int rank = 0;
+    for (int j = 0; j < mem; ++j) {
+      const int o = __builtin_amdgcn_readlane(me, j);
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+      rank += (w > v || (w == v && o < me)) ? 1 : 0;
+    }
+    if (lane < mem && rank < need) atomicOr(&L.chosen[me >> 5], 1u << (me & 31));
+  }
+  // 4. ids ascending: an exclusive prefix of the bitmask words' popcounts
+  //    (wave 0, consecutive words per lane), into the histogram's space.  In
+  //    the readlane case wave 0 set the members' bits itself just before:
+  //    one wave's LDS accesses take effect in program order.
+  const int nw = (n + 31) / 32;
+  int* wpre = L.hist;
+  if (tid < 64) {
+    const int W = (nw + 63) / 64;
+    const int w0 = lane * W, w1 = min(nw, w0 + W);
+    int sum = 0;
+    for (int w = w0; w < w1; ++w) sum += __popc(L.chosen[w]);
+    int ex = wave_incl_scan(sum) - sum;
+    for (int w = w0; w < w1; ++w) {
+      wpre[w] = ex;
+      ex += __popc(L.chosen[w]);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) {
+    const uint32_t word = L.chosen[i >> 5];
+    if ((word >> (i & 31)) & 1u) {
+      const int pos = wpre[i >> 5] + __popc(word & ((1u << (i & 31)) - 1u));
+      if (pos < k) out[pos] = i;
+    }
+  }
+}
+
+// The coarse selection from scores that each thread wrote to vals itself,
+// with each thread's own minimum and maximum of them: the range is combined
+// over the workgroup (one barrier), every score binned, then topk_coarse.
+// Clears its own accumulators.  Every thread calls it.
+template <int NT>
+__device__ void topk_from_lds(TopkLds<NT>& L, float* vals, int n, int k, float mn, float mx, int* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  topk_coarse_clear<NT>(L, n);
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) {
+    L.rmin[wv] = mn;
+    L.rmax[wv] = mx;
+  }
+  __syncthreads();
+  mn = L.rmin[0];
+  mx = L.rmax[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) {
+    mn = fminf(mn, L.rmin[w]);
+    mx = fmaxf(mx, L.rmax[w]);
+  }
+  const BinMap m = coarse_map(mn, mx);
+  for (int i = tid; i < n; i += NT) atomicAdd(&L.hist[coarse_bin(vals[i], m)], 1);
+  __syncthreads();
+  topk_coarse<NT>(L, vals, n, k, m, mn, mx, out);
+}
+
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ scores,
                                              int* __restrict__ sel) {
@@ -316,7 +489,7 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
   }
-  topk_select<NT>(L, vals, n, k, mn, mx, out);
+  topk_from_lds<NT>(L, vals, n, k, mn, mx, out);
 }
 
 // Scoring and top-k of one (request, KV head) in one 1024-thread workgroup,
@@ -419,8 +592,7 @@ __global__ __launch_bounds__(1024) void k_select_fused(Dev d, const uint16_t* __
     for (int i = tid; i < k; i += 1024) out[i] = i < n ? i : -1;
     return;
   }
-  __syncthreads();
-  topk_select<1024>(L, vals, n, k, mn, mx, out);
+  topk_from_lds<1024>(L, vals, n, k, mn, mx, out);
 }
 
 // Scoring and top-k in one launch for batches with fewer lists than CUs.
@@ -522,33 +694,59 @@ __global__ __launch_bounds__(1024) void k_select_split(Dev d, const uint16_t* __
     acc[it] = a;
   }
   // lane r < ROWS of the group writes row pw + r
+  float smin = INFINITY, smax = -INFINITY;
   if (r < ROWS) {
     float mine = acc[0];
 #pragma unroll
     for (int it = 1; it < ROWS; ++it) mine = (r == it) ? acc[it] : mine;
     const int p = pw + r;
-    if (p < n) __hip_atomic_store(&srow[p], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else if (p < d.Nmax) srow[p] = -INFINITY;
+    if (p < n) {
+      __hip_atomic_store(&srow[p], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      smin = smax = mine;
+    } else if (p < d.Nmax) {
+      srow[p] = -INFINITY;
+    }
   }
   if (n <= k) return;
+  // this wave's score range goes beside the scores, so the last workgroup can
+  // bin the list's scores as they arrive, without combining ranges first
+  smin = wave_min(smin);
+  smax = wave_max(smax);
+  const int chunks = (n + kRows - 1) / kRows;
+  float* rg = d.srange + (size_t)bh * kSplitRangeSlots * 2;
+  if (lane == 0) {
+    float* mine = rg + 2 * (blockIdx.x * 16 + wave);
+    __hip_atomic_store(mine, smin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(mine + 1, smax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  topk_coarse_clear<1024>(L, n);  // (only the last workgroup of the list uses them)
 
-  // count this workgroup in once every wave's score stores have completed
+  // count this workgroup in once every wave's score and range stores have
+  // completed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int chunks = (n + kRows - 1) / kRows;
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(&arrive[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == chunks - 1;
   __syncthreads();
   if (!s_last) return;
   if (tid == 0) __hip_atomic_store(&arrive[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // the list's range from every wave's (one entry per lane), then the scores,
+  // each binned as it arrives
   float mn = INFINITY, mx = -INFINITY;
+  for (int e = lane; e < chunks * 16; e += 64) {
+    mn = fminf(mn, __hip_atomic_load(rg + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    mx = fmaxf(mx, __hip_atomic_load(rg + 2 * e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  const BinMap m = coarse_map(mn, mx);
   for (int i = tid; i < n; i += 1024) {
     const float x = __hip_atomic_load(&srow[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     vals[i] = x;
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+    atomicAdd(&L.hist[coarse_bin(x, m)], 1);
   }
-  topk_select<1024>(L, vals, n, k, mn, mx, out);
+  __syncthreads();
+  topk_coarse<1024>(L, vals, n, k, m, mn, mx, out);
 }
 
 hipError_t launch_score(const Dev& d, const uint16_t* q, float* scores, hipStream_t s) {

@@ -163,7 +163,7 @@ Derived derive(const spin_config* c) {
 struct Layout {
   size_t summaries, part_first, part_len, req_parts, req_pages, req_stride, tail_sum, host_base,
       directory, segments,
-      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, last_t, scores, arrive,
+      seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, last_t, scores, arrive, srange,
       miss_tmp, ins,
       nmiss,
       freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
@@ -200,6 +200,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.last_t = take(B * sizeof(int));
   L.scores = take(B * Hkv * N * sizeof(float));
   L.arrive = take(B * Hkv * sizeof(int));
+  L.srange = take(B * Hkv * spin::kSplitRangeSlots * 2 * sizeof(float));
   L.miss_tmp = take(B * d.max_mand * sizeof(int4));
   L.ins = take(B * d.max_mand * sizeof(int4));
   L.nmiss = take(B * sizeof(int));
@@ -353,6 +354,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.last_t = reinterpret_cast<int*>(w + L.last_t);
   v.scores = reinterpret_cast<float*>(w + L.scores);
   v.arrive = reinterpret_cast<int*>(w + L.arrive);
+  v.srange = reinterpret_cast<float*>(w + L.srange);
   v.miss_tmp = reinterpret_cast<int4*>(w + L.miss_tmp);
   v.ins = reinterpret_cast<int4*>(w + L.ins);
   v.nmiss = reinterpret_cast<int*>(w + L.nmiss);

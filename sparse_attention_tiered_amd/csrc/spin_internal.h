@@ -57,6 +57,7 @@ struct Dev {
   // per-step scratch
   float* scores;               // [B][Hkv][Nmax]
   int* arrive;                 // [B][Hkv] workgroups of the list done scoring (0 between launches)
+  float* srange;               // [B][Hkv][kSplitRangeSlots][2] each scoring wave's (min, max) score
   int4* miss_tmp;              // [B][max_mand] (h, page, block position, valid tokens)
   int4* ins;                   // [B][max_mand] (slot, h, page, 0)
   int* nmiss;                  // [B]
@@ -106,6 +107,9 @@ hipError_t launch_topk(const Dev& d, const float* scores, int* sel, hipStream_t 
 // 2048-partition lists, slower at 7.7K, where the last workgroup's top-k
 // tail outweighs the launch it saves)
 constexpr int kSplitSelectMaxParts = 4096;
+// one (min, max) per wave of every workgroup of a list: 512-partition
+// workgroups of 16 waves over at most kSplitSelectMaxParts partitions
+constexpr int kSplitRangeSlots = kSplitSelectMaxParts / 512 * 16;
 hipError_t launch_select_split(const Dev& d, const uint16_t* q, float* scores, int* sel,
                                hipStream_t s);
 hipError_t launch_select_fused(const Dev& d, const uint16_t* q, float* scores, int* sel,
