@@ -21,12 +21,15 @@
 // each wave takes a contiguous quarter of it, keeps an fp32 online softmax per
 // head, and pipelines its page loads (next keys during this page's softmax and
 // PV, next values during the next logits), with the block-table entries of
-// its pages loaded once up front.  The waves merge through LDS.  A head whose
-// pages fit in one workgroup is finished there; otherwise k_attend_merge
-// combines the split partials (log-sum-exp).  (Merging in the last workgroup
-// to finish, with the partials handed over as agent-scope atomic stores and
-// loads, measured no faster than the second launch; with a device-scope
-// fence per workgroup, which writes back the whole L2, it was far slower.)
+// its pages loaded once up front, beside the head's page count.  The waves
+// merge through LDS.  A head whose pages fit in one workgroup is finished
+// there; in the whole-table pass the split that finishes last merges the
+// head's split partials (log-sum-exp), handed over as agent-scope stores and
+// loads within the launch (on the 128K workload with 64-page heads, 4 splits:
+// 24 + 4.6 us with a merge launch -> 26.6 us; a device-scope fence per
+// workgroup instead, which writes back the whole L2, was far slower).  The
+// overlapped passes' partials are merged by k_attend_merge or
+// k_attend_merge_arrival after the launch.
 // The resident-page pass that runs beside the transfer uses its own, longer
 // splits (d.pps_res): it only has to keep pace with the transfer, and fewer
 // attention workgroups contend less with the PCIe pulls.
@@ -39,6 +42,19 @@
 namespace spin {
 
 constexpr int kAttWG = 256;
+
+// Two floats as one 64-bit agent-scope (write-through) store / load: the
+// hand-over of split partials between workgroups of one launch.
+__device__ __forceinline__ void store_pair_agent(float* p, float a, float b) {
+  const unsigned long long v = ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void load_pair_agent(const float* p, float& a, float& b) {
+  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  a = __uint_as_float((uint32_t)v);
+  b = __uint_as_float((uint32_t)(v >> 32));
+}
 
 // Pages per split of a head with cnt pages: its pages spread evenly over the
 // head's `nsp` workgroups (whole pages per wave), so heads with fewer pages
@@ -73,10 +89,24 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
   const int bh = wg / nsp;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
   const int G = d.G;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  // The block-table entries this wave takes when the head's split size is the
+  // grid's (a head with every page it can have: a full selection of
+  // one-page partitions), loaded beside the head's page count instead of
+  // after it; another split size loads them again below.
+  const int pps_g = nsp == d.splits ? d.pps : d.pps_res;
+  const int p0_g = split * pps_g + wave * (pps_g / 4);
+  int g_slot = 0, g_nt = 0, g_miss = 0;
+  if (lane < pps_g / 4 && p0_g + lane < d.max_blocks) {
+    const size_t e = (size_t)bh * d.max_blocks + p0_g + lane;
+    g_slot = bt[e];
+    g_nt = bntok[e];
+    if (mode != kAttendAll) g_miss = d.bmiss[e];
+  }
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
   const int pps = head_pps(cnt, nsp);
   const int ns = (cnt + pps - 1) / pps;  // splits that hold pages
-  const int tid = threadIdx.x;
   const int hh = tid >> 4, dc = (tid & 15) * 8;  // merge layout: head, 8 dims
   float* orow = out + ((size_t)b * d.Hq + (size_t)h * G) * kHeadDim;
   if (cnt == 0) {  // no pages: the head's output is zero
@@ -88,7 +118,6 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
     return;
   }
   if (split >= ns) return;
-  const int wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, g = lane >> 4;
   const int ppw = pps / 4;
   const int p0 = split * pps + wave * ppw;
@@ -100,14 +129,16 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
   bool keep = false;
   if (lane < np) {
     const size_t e = (size_t)bh * d.max_blocks + p0 + lane;
-    const int s = bt[e];
-    const int n = bntok[e];
+    const bool same = pps == pps_g;  // (then p0 == p0_g)
+    const int s = same ? g_slot : bt[e];
+    const int n = same ? g_nt : bntok[e];
     // a malformed entry (caller-supplied table) reads slot 0 with every token masked
     if ((unsigned)s < (unsigned)d.pool_slots && n > 0 && n <= kPageTokens) {
       my_slot = s;
       my_nt = n;
     }
-    keep = mode == kAttendAll || (d.bmiss[e] != 0) == (mode == kAttendFetched);
+    const int fetched = mode == kAttendAll ? 0 : same ? g_miss : d.bmiss[e];
+    keep = mode == kAttendAll || (fetched != 0) == (mode == kAttendFetched);
   }
   unsigned long long pages = __ballot(keep);  // lanes holding this wave's pages, in order
 
@@ -238,19 +269,87 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
     }
     return;
   }
-  // publish this split's partial for k_attend_merge (fetched-page partials
-  // sit after the resident-page ones)
+  // publish this split's partial (fetched-page partials sit after the
+  // resident-page ones)
+  const int slot_s = mode == kAttendFetched ? d.splits + split : split;
   if (hh < G) {
-    const int slot_s = mode == kAttendFetched ? d.splits + split : split;
     const size_t pi = ((size_t)bh * 2 * d.splits + slot_s) * G + hh;
-    float4* po = reinterpret_cast<float4*>(d.part_o + pi * kHeadDim + dc);
-    po[0] = make_float4(o[0], o[1], o[2], o[3]);
-    po[1] = make_float4(o[4], o[5], o[6], o[7]);
-    if (dc == 0) {
-      d.part_ml[2 * pi] = M;
-      d.part_ml[2 * pi + 1] = L;
+    float* po = d.part_o + pi * kHeadDim + dc;
+    if (mode == kAttendAll) {
+      // read back within this launch by the head's last split, maybe on
+      // another XCD: agent-scope stores, which write through its L2
+      store_pair_agent(po, o[0], o[1]);
+      store_pair_agent(po + 2, o[2], o[3]);
+      store_pair_agent(po + 4, o[4], o[5]);
+      store_pair_agent(po + 6, o[6], o[7]);
+      if (dc == 0) store_pair_agent(d.part_ml + 2 * pi, M, L);
+    } else {  // for k_attend_merge / k_attend_merge_arrival, after this launch
+      float4* p4 = reinterpret_cast<float4*>(po);
+      p4[0] = make_float4(o[0], o[1], o[2], o[3]);
+      p4[1] = make_float4(o[4], o[5], o[6], o[7]);
+      if (dc == 0) {
+        d.part_ml[2 * pi] = M;
+        d.part_ml[2 * pi + 1] = L;
+      }
     }
   }
+  if (mode != kAttendAll) return;
+  // The whole-table pass merges its splits in this launch: once every wave's
+  // partial stores have completed the workgroup counts itself in on its
+  // head; the split that completes the count folds every split's partial
+  // (its own from registers, the others with agent-scope loads, which miss
+  // stale lines of its own L2) in split order, so the result does not depend
+  // on which split finished last, and resets the counter for the next launch.
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(&d.att_arrive[bh], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) __hip_atomic_store(&d.att_arrive[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (hh >= G) return;
+  float Mf = -INFINITY, Lf = 0.f, of[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) of[e] = 0.f;
+  constexpr int UX = 8;  // partials' loads in flight at a time
+  for (int x0 = 0; x0 < ns; x0 += UX) {
+    float ms[UX], ls[UX], a[UX][8];
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+      const int x = x0 + u;
+      ms[u] = -INFINITY;
+      ls[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[u][e] = 0.f;
+      if (x < ns && x != split) {
+        const size_t pi = ((size_t)bh * 2 * d.splits + x) * G + hh;
+        load_pair_agent(d.part_ml + 2 * pi, ms[u], ls[u]);
+        const float* po = d.part_o + pi * kHeadDim + dc;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) load_pair_agent(po + e, a[u][e], a[u][e + 1]);
+      } else if (x == split) {
+        ms[u] = M;
+        ls[u] = L;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[u][e] = o[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+      if (ms[u] == -INFINITY) continue;
+      const float Mn = fmaxf(Mf, ms[u]);
+      const float fo = Mf == -INFINITY ? 0.f : exp2f(Mf - Mn), fn = exp2f(ms[u] - Mn);
+      Mf = Mn;
+      Lf = Lf * fo + ls[u] * fn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) of[e] = of[e] * fo + a[u][e] * fn;
+    }
+  }
+  const float inv = Lf > 0.f ? 1.f / Lf : 0.f;
+  float4* o4 = reinterpret_cast<float4*>(orow + (size_t)hh * kHeadDim + dc);
+  o4[0] = make_float4(of[0] * inv, of[1] * inv, of[2] * inv, of[3] * inv);
+  o4[1] = make_float4(of[4] * inv, of[5] * inv, of[6] * inv, of[7] * inv);
 }
 
 __global__ __launch_bounds__(kAttWG, 2) void k_attend(Dev d, const uint16_t* __restrict__ q,
@@ -363,21 +462,17 @@ __device__ void merge_head(const Dev& d, int bh, int n_all, Part part, float* __
   o4[1] = make_float4(o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
-// One workgroup per (request, KV head): merge its split partials and
-// normalise.  `both` merges the resident-page and fetched-page passes;
-// otherwise only heads spanning several splits need it (the rest were
-// finished by k_attend).
+// One workgroup per (request, KV head): merge the split partials of the
+// resident-page pass and of the fetched-page pass, and normalise.
 __global__ __launch_bounds__(kAttWG) void k_attend_merge(Dev d, const int* __restrict__ bcount,
-                                                         float* __restrict__ out, int both) {
+                                                         float* __restrict__ out) {
   const int bh = blockIdx.x;
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  // splits holding pages: of the whole-table pass, or of the resident-page
-  // pass followed by the fetched-page pass
+  // splits holding pages: of the resident-page pass, then of the fetched-page pass
   const int ns = (cnt + head_pps(cnt, d.splits) - 1) / head_pps(cnt, d.splits);
-  if (!both && ns <= 1) return;  // (the whole workgroup)
-  const int ns_res = both ? (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res) : ns;
+  const int ns_res = (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res);
   const int G = d.G;
-  merge_head(d, bh, both ? ns_res + ns : ns,
+  merge_head(d, bh, ns_res + ns,
              [&](int x, int hh, int dc, const float*& ml, const float*& po) {
                const int slot = x < ns_res ? x : d.splits + (x - ns_res);
                const size_t pi = ((size_t)bh * 2 * d.splits + slot) * G + hh;
@@ -439,10 +534,10 @@ hipError_t launch_attend(const Dev& d, const uint16_t* q, const int* bt, const i
   hipLaunchKernelGGL(k_attend, dim3(d.B * d.Hkv * nsp), dim3(kAttWG), 0, s, d, q, bt, bntok,
                      bcount, out, mode);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || mode == kAttendResident) return e;
-  const int both = mode == kAttendFetched;
-  if (!both && d.splits == 1) return e;
-  hipLaunchKernelGGL(k_attend_merge, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out, both);
+  // the whole-table pass merges its splits itself; the fetched-page pass
+  // is merged with the resident-page one by a second launch
+  if (e != hipSuccess || mode != kAttendFetched) return e;
+  hipLaunchKernelGGL(k_attend_merge, dim3(d.B * d.Hkv), dim3(kAttWG), 0, s, d, bcount, out);
   return hipGetLastError();
 }
 

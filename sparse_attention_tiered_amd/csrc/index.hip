@@ -25,7 +25,10 @@ __global__ void k_init(Dev d) {
     d.owner[i] = -1;
     d.last_use[i] = -1;
   }
-  for (size_t i = tid; i < (size_t)d.B * d.Hkv; i += nth) d.arrive[i] = 0;
+  for (size_t i = tid; i < (size_t)d.B * d.Hkv; i += nth) {
+    d.arrive[i] = 0;
+    d.att_arrive[i] = 0;
+  }
   for (size_t i = tid; i < (size_t)d.B; i += nth) {
     d.free_count[i] = d.C;
     d.budget[i] = d.C;

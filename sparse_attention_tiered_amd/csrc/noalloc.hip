@@ -9,8 +9,9 @@
 // current) on the entry point's first call there and kept; the array's name
 // itself is only a host-side stand-in and is never passed to a kernel.  Every
 // call on a GPU shares that GPU's array: calls that overlap in time on one
-// GPU race on it.  Nothing in it has to start at zero: each split writes its
-// partial before the merge of the same call reads it.
+// GPU race on it.  The per-head counters of the split merge start at zero
+// (cleared on the first call) and every call leaves them at zero; the
+// partials are written before the same call reads them.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -18,17 +19,28 @@
 #include "spin.h"
 #include "spin_internal.h"
 
-// split partials of spin_attend_noalloc (part_o, then part_ml)
+// spin_attend_noalloc's scratch: the per-head counters of the split merge
+// (kCounterBytes: one int per (request, KV head) of the largest batch), then
+// the split partials (part_o, then part_ml)
 static __device__ __align__(256) unsigned char scratch[SPIN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
+constexpr size_t kCounterBytes = 1024 * spin::kMaxKvHeads * sizeof(int);
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_scratch[kMaxDevices];  // device address of `scratch` on each device
 
-// The current device's copy of the array (looked up on first use there).
-hipError_t scratch_on_current_device(void** out) {
+// The counters start at zero, and every launch leaves them at zero (the
+// head's last split resets its own); they are cleared once, by a kernel on
+// the first call's stream, before the first attention that counts on them.
+__global__ void k_clear_counters(int* c, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0;
+}
+
+// The current device's copy of the array (looked up, and its counters
+// cleared on `s`, on first use there).
+hipError_t scratch_on_current_device(hipStream_t s, void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -37,6 +49,10 @@ hipError_t scratch_on_current_device(void** out) {
   if (!g_scratch[dev]) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    const int n = (int)(kCounterBytes / sizeof(int));
+    hipLaunchKernelGGL(k_clear_counters, dim3(16), dim3(256), 0, s, static_cast<int*>(p), n);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     g_scratch[dev] = p;
   }
@@ -70,13 +86,15 @@ extern "C" SPIN_API int spin_attend_noalloc(const void* d_q, const void* d_pool,
       (long long)batch * num_kv_heads * max_blocks, pages_per_split);
   const int splits = (max_blocks + pps - 1) / pps;
   // the partials, laid out as in a context's workspace: [B * Hkv][2 * splits][G]
-  // rows of 128 floats, then their (max, sum) pairs; a single split needs none
+  // rows of 128 floats, then their (max, sum) pairs, after the counters; a
+  // single split per head needs none
   const size_t rows = (size_t)batch * num_kv_heads * 2 * splits * G;
   const size_t o_bytes = rows * spin::kHeadDim * sizeof(float);
-  const size_t need = splits > 1 ? o_bytes + rows * 2 * sizeof(float) : 0;
+  const size_t need = splits > 1 ? kCounterBytes + o_bytes + rows * 2 * sizeof(float) : 0;
   if (need > SPIN_NOALLOC_SCRATCH_BYTES) return SPIN_ESCRATCH;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   void* base = nullptr;
-  if (scratch_on_current_device(&base) != hipSuccess) return SPIN_EHIP;
+  if (scratch_on_current_device(s, &base) != hipSuccess) return SPIN_EHIP;
   spin::Dev d{};
   d.B = batch;
   d.Hq = num_q_heads;
@@ -89,13 +107,13 @@ extern "C" SPIN_API int spin_attend_noalloc(const void* d_q, const void* d_pool,
   d.splits_res = splits;
   d.pool_slots = (int)pool_pages;
   d.pool = static_cast<uint16_t*>(const_cast<void*>(d_pool));
-  d.part_o = static_cast<float*>(base);
-  d.part_ml = reinterpret_cast<float*>(static_cast<char*>(base) + o_bytes);
+  d.att_arrive = static_cast<int*>(base);
+  d.part_o = reinterpret_cast<float*>(static_cast<char*>(base) + kCounterBytes);
+  d.part_ml = reinterpret_cast<float*>(static_cast<char*>(base) + kCounterBytes + o_bytes);
   d.step_t = nullptr;
   d.q_step = 0;
   if (spin::launch_attend(d, static_cast<const uint16_t*>(d_q), d_block_table, d_block_ntok,
-                          d_block_count, d_out, spin::kAttendAll,
-                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+                          d_block_count, d_out, spin::kAttendAll, s) != hipSuccess)
     return SPIN_EHIP;
   return SPIN_OK;
 }

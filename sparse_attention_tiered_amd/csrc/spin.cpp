@@ -166,7 +166,7 @@ struct Layout {
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, last_t, scores, arrive, srange,
       miss_tmp, ins,
       nmiss,
-      freed, nfreed, alloc, nalloc, bmiss, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
+      freed, nfreed, alloc, nalloc, bmiss, att_arrive, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
       total;
 };
 
@@ -209,6 +209,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.alloc = take(B * Hkv * d.ndir * sizeof(int));
   L.nalloc = take(B * sizeof(int));
   L.bmiss = take(B * Hkv * d.max_blocks);
+  L.att_arrive = take(B * Hkv * sizeof(int));
   L.part_o = take(B * Hkv * 2 * d.splits * d.G * spin::kHeadDim * sizeof(float));
   L.part_ml = take(B * Hkv * 2 * d.splits * d.G * 2 * sizeof(float));
   L.arr_o = take(B * d.max_mand * d.G * spin::kHeadDim * sizeof(float));
@@ -363,6 +364,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.alloc = reinterpret_cast<int*>(w + L.alloc);
   v.nalloc = reinterpret_cast<int*>(w + L.nalloc);
   v.bmiss = reinterpret_cast<unsigned char*>(w + L.bmiss);
+  v.att_arrive = reinterpret_cast<int*>(w + L.att_arrive);
   v.part_o = reinterpret_cast<float*>(w + L.part_o);
   v.part_ml = reinterpret_cast<float*>(w + L.part_ml);
   v.arr_o = reinterpret_cast<float*>(w + L.arr_o);

@@ -66,6 +66,7 @@ struct Dev {
   int* alloc;                  // [B][Hkv * ndir] directory entries that need a segment
   int* nalloc;                 // [B]
   unsigned char* bmiss;        // [B][Hkv][max_blocks] 1 = block fetched by this step's retrieve
+  int* att_arrive;             // [B][Hkv] splits of the whole-table pass done (0 between launches)
   float* part_o;               // [B * Hkv][2 * splits][G][128]
   float* part_ml;              // [B * Hkv][2 * splits][G][2] (max in log2 units, sum)
   // attention of each fetched page on arrival, indexed by its place in the
