@@ -10,15 +10,20 @@ K consecutive steps: by default every configured step of the workload after a
 warm-up of min(8, steps/4) (the 128K pressure workload: steps 8-127); with
 --steps K, the last K configured steps, never starting before step W (the
 query stream continues past the configured steps when W + K exceeds them).
-Two contexts are indexed from the same pinned host KV and driven through the
-same steps; the path is deterministic, so both pass through the same states
-(their counters are compared):
+Three contexts are indexed from the same pinned host KV and driven through
+the same steps; the path is deterministic, so all pass through the same
+states (their counters over the window are compared):
 
   context A  the steps before the window as untimed warm-up, then the window
              as replays of one captured HIP graph of the device-indexed
-             whole-step call, back to back, with a timing event between
-             replays: `ms_per_step` is the median step of the window and
-             `value` = B * Hq / ms_per_step (the mean is reported beside it);
+             whole-step call, back to back, events only at the window's
+             ends: `mean_ms_per_step`, the whole window's throughput
+             (`value_at_mean`);
+  context C  the same, with a timing event between replays:
+             `ms_per_step` is the median step of the window and `value` =
+             B * Hq / ms_per_step (each event adds a few microseconds of idle
+             to the step it closes: `mean_ms_per_step_with_step_events`
+             minus `mean_ms_per_step`);
   context B  the same warm-up, then the same window with an event between
              stages on the stream each stage runs on: stage times per step,
              the transfer launch's duration (the roofline of the dominant
@@ -28,7 +33,7 @@ same steps; the path is deterministic, so both pass through the same states
              the memory-side cache (cold).
 
 Warm-up steps run the serial form of the step (the transfer, then attention),
-so the one-launch transfer kernel runs only inside the two windows and a
+so the one-launch transfer kernel runs only inside the three windows and a
 kernel trace of this command averages it over exactly those steps.  Prints
 one JSON line.
 
@@ -259,7 +264,7 @@ def main():
         mand = w.Hkv * w.k * geo.max_ppp
         budget = min(w.slots_per_request, int(round(mand * (1 + args.budget_ratio))))
     ctx = []
-    for name in ("A", "B"):
+    for name in ("A", "B", "C"):
         spin = bd.Spin(cfg)
         t0 = time.time()
         for b in range(w.B):
@@ -269,7 +274,7 @@ def main():
         log(f"[bench] context {name}: index (summaries over PCIe) {time.time() - t0:.2f}s; "
             f"attend splits={spin.splits}")
         ctx.append(spin)
-    A, Bx = ctx
+    A, Bx, Cx = ctx
     q = torch.from_numpy(draws.q_bits.view(np.int16)).to("cuda")
     S = torch.cuda.Stream()  # a created stream: HIP graphs cannot capture the null stream
     Cs = S if args.single_stream else torch.cuda.Stream()
@@ -327,36 +332,61 @@ def main():
     warm_up(A, 1)
     torch.cuda.synchronize()
     stA0, _ = A.stats()
-    graph = None
-    if use_graph:
+
+    def capture(spin):
         # one step captured with the device-side step index, replayed K times
         t_dev = torch.full((1,), start, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=S):
-            A.step_at(q, t_dev, stream=S, copy_stream=Cs)
-    torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=S):
+            spin.step_at(q, t_dev, stream=S, copy_stream=Cs)
+        torch.cuda.synchronize()
+        return g
+
+    def window(spin, g, evt=None):
+        # steps start .. end-1; an event after each step when evt is given
+        for i in range(K):
+            t = start + i
+            if g is not None:
+                with torch.cuda.stream(S):
+                    g.replay()
+            elif overlap or args.single_stream:
+                spin.step(q[t], t, stream=S, copy_stream=Cs)  # the library's whole-step call
+            else:
+                staged(spin, t)
+            if evt is not None:
+                evt[i + 1].record(S)
+
+    graph = capture(A) if use_graph else None
     w0 = time.perf_counter()
-    evt = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    evt[0].record(S)
-    for i in range(K):
-        t = start + i
-        if graph is not None:
-            with torch.cuda.stream(S):
-                graph.replay()
-        elif overlap or args.single_stream:
-            A.step(q[t], t, stream=S, copy_stream=Cs)  # the library's whole-step call
-        else:
-            staged(A, t)
-        evt[i + 1].record(S)
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ends[0].record(S)
+    window(A, graph)
+    ends[1].record(S)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     stA1, _ = A.stats()
+    mean_ms = ends[0].elapsed_time(ends[1]) / K
+
+    # ---- context C: the same steps again, with a timing event between steps
+    # (their median is the figure the measurement plan asks for; each event
+    # adds a few microseconds of idle to the step it closes, which the
+    # difference of the two means shows)
+    staged(Cx, 0, None, ovl=False)
+    warm_up(Cx, 1)
+    torch.cuda.synchronize()
+    stC0, _ = Cx.stats()
+    graph_c = capture(Cx) if use_graph else None
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evt[0].record(S)
+    window(Cx, graph_c, evt)
+    torch.cuda.synchronize()
+    stC1, _ = Cx.stats()
     step_times = [evt[i].elapsed_time(evt[i + 1]) for i in range(K)]
-    total_ms = evt[0].elapsed_time(evt[K])
     ms_per_step = float(np.median(step_times))
-    mean_ms = total_ms / K
+    mean_ms_evented = evt[0].elapsed_time(evt[K]) / K
     value = w.B * w.Hq / (ms_per_step * 1e-3)
+    del graph, graph_c
 
     # ---- context B: the same warm-up, then the same window with stage events
     staged(Bx, 0, None, ovl=False)
@@ -373,11 +403,13 @@ def main():
         step_hit.append(st_i.hits - prev_h)
         prev_m, prev_h = st_i.misses, st_i.hits
     stB1 = st_i
-    same_steps = ((stA1.hits - stA0.hits, stA1.misses - stA0.misses, stA1.evictions - stA0.evictions) ==
-                  (stB1.hits - stB0.hits, stB1.misses - stB0.misses, stB1.evictions - stB0.evictions)
-                  and stA0.misses == stB0.misses)
+
+    def window_counts(s0, s1):
+        return (s0.misses, s1.hits - s0.hits, s1.misses - s0.misses, s1.evictions - s0.evictions)
+
+    same_steps = (window_counts(stA0, stA1) == window_counts(stB0, stB1) == window_counts(stC0, stC1))
     if not same_steps:
-        log("[bench] WARNING: the two contexts' counters differ over the window")
+        log("[bench] WARNING: the contexts' counters differ over the window")
     stage = {"select": [], "resolve_evict": [], "retrieve": [], "attend": []}
     instr_step = []
     for e in evs:
@@ -534,8 +566,10 @@ def main():
         "roofline": roof,
         "timed_steps": [start, end - 1],
         "configured_steps": T,
-        "ms_per_step_is": "median of the window's steps",
+        "ms_per_step_is": "median of the window's steps (an event between steps)",
         "mean_ms_per_step": mean_ms,
+        "mean_ms_per_step_is": "the window's steps back to back, events only at its ends",
+        "mean_ms_per_step_with_step_events": mean_ms_evented,
         "step_ms_p10_p90": [float(np.percentile(step_times, 10)), float(np.percentile(step_times, 90))],
         "value_at_mean": w.B * w.Hq / (mean_ms * 1e-3),
         "stages_ms": stage_ms,
@@ -544,7 +578,7 @@ def main():
         "contexts_agree_over_window": bool(same_steps),
         "attended_head_tokens_per_s": attended_tokens / (iso_attend_ms * 1e-3),
         "overlap_retrieve_attend": overlap,
-        "timed_as_graph_replays": graph is not None,
+        "timed_as_graph_replays": use_graph,
         "rooflines": rl,
         "residency": {"hits_per_step": hits / K, "misses_per_step": misses / K,
                       "evictions_per_step": evictions / K},
@@ -586,6 +620,7 @@ def main():
                                     "bytes_written": 4 * n, "launches": 3}
     A.close()
     Bx.close()
+    Cx.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         line["cpu_baseline"] = cpu_baseline(w, geo, draws, [h[1] for h in host], start, end,
