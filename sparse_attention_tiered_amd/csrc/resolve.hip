@@ -35,6 +35,11 @@ static_assert(kMaxKvHeads * (kMaxPartitions * kMaxPPP / kSegEntries) <= kMaxSlot
 // slot codes besides the recency buckets 0..63 of eviction candidates
 constexpr uint8_t kCodeVictim = 0xFD, kCodeFree = 0xFE, kCodePinned = 0xFF;
 
+// misses of a request's step kept in LDS besides the workspace list (which
+// the transfer reads), with the directory entry translation read for each:
+// steps 4 and 5 read them back without a global round trip
+constexpr int kLdsMisses = 2048;
+
 __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__ sel, int t,
                                                   int* __restrict__ bt, int* __restrict__ bntok,
                                                   int* __restrict__ bcount) {
@@ -44,6 +49,8 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   __shared__ int hist[kBuckets];
   __shared__ int tmp[17];
   __shared__ int sh_cut, sh_below;
+  __shared__ int4 lmiss[kLdsMisses];  // (h, page, block position, valid tokens)
+  __shared__ int ldir[kLdsMisses];    // the miss's directory entry before step 3
 
   if (d.step_t) t = *d.step_t;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -148,6 +155,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   for (int base = 0; base < n_items; base += 1024) {
     const int i = base + tid;
     int nm = 0, p = -1, h = 0, np = 0, pos0 = 0, pf0 = 0, pl = 0;
+    int segv[kMaxPPP];  // directory entry of each page's range
     unsigned missmask = 0;
     if (i < n_items) {
       p = base == 0 ? p_keep : selb[i];
@@ -162,6 +170,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         for (int j = 0; j < kMaxPPP; ++j) {
           const int page = pf0 + j;
           const int seg = j < np ? dir[h * d.ndir + (page >> 6)] : -1;
+          segv[j] = seg;
           slots[j] = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
         }
 #pragma unroll
@@ -193,8 +202,15 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     if (nm) {
       int rnk = mcarry + ex;
       for (int j = 0; j < np; ++j)
-        if (missmask & (1u << j))
-          misses[rnk++] = make_int4(h, pf0 + j, pos0 + j, min(kPageTokens, pl - kPageTokens * j));
+        if (missmask & (1u << j)) {
+          const int4 mv = make_int4(h, pf0 + j, pos0 + j, min(kPageTokens, pl - kPageTokens * j));
+          misses[rnk] = mv;
+          if (rnk < kLdsMisses) {
+            lmiss[rnk] = mv;
+            ldir[rnk] = segv[j];
+          }
+          ++rnk;
+        }
     }
     mcarry += tot;
   }
@@ -202,14 +218,16 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   if (tid == 0) d.head_moff[(size_t)b * (Hkv + 1) + Hkv] = nmiss;
   __syncthreads();
   // the first 1024 misses, the one before each, and each one's directory
-  // entry as it stands before step 3, loaded now for steps 4 and 5 (step 3
-  // can only clear directory entries, and it flags each one it clears)
+  // entry as it stands before step 3 (as step 2 read it), for steps 4 and 5
+  // (step 3 can only clear directory entries, and it flags each one it
+  // clears)
+  auto miss_at = [&](int j) { return j < kLdsMisses ? lmiss[j] : misses[j]; };
   int4 m_pre = make_int4(0, 0, 0, 0), m_prev = make_int4(-1, 0, 0, 0);
   int dir_pre = -1;
   if (tid < nmiss) {
-    m_pre = misses[tid];
-    if (tid > 0) m_prev = misses[tid - 1];
-    dir_pre = dir[m_pre.x * d.ndir + (m_pre.y >> 6)];
+    m_pre = lmiss[tid];
+    if (tid > 0) m_prev = lmiss[tid - 1];
+    dir_pre = ldir[tid];
   }
 
   // 3. bucketed LRU, only when the resident pages plus the misses exceed the
@@ -412,7 +430,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     __syncthreads();
     for (int j = tid; j < assigned; j += 1024) {
       const int c = lds_slots ? slot_of[j] : insb[j].x;
-      const int4 m = j == tid ? m_pre : misses[j];  // (h, page, block position, valid tokens)
+      const int4 m = j == tid ? m_pre : miss_at(j);  // (h, page, block position, valid tokens)
       owner[c] = m.x * d.max_pages + m.y;
       last[c] = t;
       btb[m.x * MB + m.z] = b * C + c;
@@ -434,11 +452,11 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
       const int r = base + tid;
       int fl = 0, e = 0;
       if (r < assigned) {
-        const int4 m = base == 0 ? m_pre : misses[r];
+        const int4 m = base == 0 ? m_pre : miss_at(r);
         e = m.x * d.ndir + (m.y >> 6);
         bool first = true;
         if (r > 0) {
-          const int4 pm = base == 0 ? m_prev : misses[r - 1];
+          const int4 pm = base == 0 ? m_prev : miss_at(r - 1);
           first = (pm.x * d.ndir + (pm.y >> 6)) != e;
         }
         // the entry now: step 3 emptied it (and flagged it) or left it as it was

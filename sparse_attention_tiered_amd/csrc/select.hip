@@ -730,8 +730,16 @@ __global__ __launch_bounds__(1024) void k_select_split(Dev d, const uint16_t* __
   __syncthreads();
   if (!s_last) return;
   if (tid == 0) __hip_atomic_store(&arrive[bh], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // the list's range from every wave's (one entry per lane), then the scores,
-  // each binned as it arrives
+  // the list's first kHeld * 1024 scores and every wave's range (one entry
+  // per lane) loaded together, so the two wait out one round trip; then the
+  // range combined, and each score binned
+  constexpr int kHeld = 4;
+  float held[kHeld];
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) {
+    const int i = tid + 1024 * j;
+    held[j] = i < n ? __hip_atomic_load(&srow[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+  }
   float mn = INFINITY, mx = -INFINITY;
   for (int e = lane; e < chunks * 16; e += 64) {
     mn = fminf(mn, __hip_atomic_load(rg + 2 * e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -740,7 +748,15 @@ __global__ __launch_bounds__(1024) void k_select_split(Dev d, const uint16_t* __
   mn = wave_min(mn);
   mx = wave_max(mx);
   const BinMap m = coarse_map(mn, mx);
-  for (int i = tid; i < n; i += 1024) {
+#pragma unroll
+  for (int j = 0; j < kHeld; ++j) {
+    const int i = tid + 1024 * j;
+    if (i < n) {
+      vals[i] = held[j];
+      atomicAdd(&L.hist[coarse_bin(held[j], m)], 1);
+    }
+  }
+  for (int i = tid + 1024 * kHeld; i < n; i += 1024) {
     const float x = __hip_atomic_load(&srow[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     vals[i] = x;
     atomicAdd(&L.hist[coarse_bin(x, m)], 1);
