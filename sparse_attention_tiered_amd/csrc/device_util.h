@@ -123,9 +123,4 @@ __device__ __forceinline__ int owner_of(const int* prefix, int nb, int j) {
   return lo;
 }
 
-// Relaxed device-scope load that does not use a stale L1 line.
-__device__ __forceinline__ int load_device(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 }  // namespace spin

@@ -40,6 +40,11 @@ constexpr uint8_t kCodeVictim = 0xFD, kCodeFree = 0xFE, kCodePinned = 0xFF;
 // steps 4 and 5 read them back without a global round trip
 constexpr int kLdsMisses = 2048;
 
+// a request's directory (Hkv * ndir entries) is copied to LDS when it fits:
+// every lookup of the launch (the misses' translation, the victims' ranges,
+// the ranges step 5 checks) is then an LDS read
+constexpr int kLdsDir = 4096;
+
 __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__ sel, int t,
                                                   int* __restrict__ bt, int* __restrict__ bntok,
                                                   int* __restrict__ bcount) {
@@ -51,6 +56,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   __shared__ int sh_cut, sh_below;
   __shared__ int4 lmiss[kLdsMisses];  // (h, page, block position, valid tokens)
   __shared__ int ldir[kLdsMisses];    // the miss's directory entry before step 3
+  __shared__ int sdir[kLdsDir];       // the request's directory, when it fits
 
   if (d.step_t) t = *d.step_t;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -76,40 +82,35 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   const int freec = d.free_count[b];
   const int budget = d.budget[b];
   const int t_prev = d.last_t[b];
+  // (every load is issued, from a clamped index, and its value dropped
+  // afterwards if out of range: loads under a condition each sit in their own
+  // branch, where the compiler waits for each before the next is issued)
   int ow0[U], lu0[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = tid + 1024 * u;
-    ow0[u] = c < C ? owner[c] : -1;
-    lu0[u] = c < C ? last[c] : 0;
+    const int c = tid + 1024 * u, cc = min(c, C - 1);
+    const int o = owner[cc], lv = last[cc];
+    ow0[u] = c < C ? o : -1;
+    lu0[u] = c < C ? lv : 0;
   }
-  if (t < t_prev) {
-    // Steps never go back: below the last resolved step some ages t -
-    // last_use would be negative.  Refused before anything changes (the
-    // error word reports it); the step's lists are left empty, so the
-    // kernels after this one do nothing for the request and its heads
-    // attend no pages.  (t_prev is one load of one address: the branch is
-    // uniform over the workgroup.)
-    for (int i = tid; i < Hkv * MB; i += 1024) {
-      btb[i] = -1;
-      bnb[i] = 0;
-    }
-    if (tid < Hkv) bcount[(size_t)b * Hkv + tid] = 0;
-    if (tid <= Hkv) d.head_moff[(size_t)b * (Hkv + 1) + tid] = 0;
-    if (tid == 0) {
-      atomicOr(d.err, kErrStep);
-      d.nmiss[b] = 0;
-      d.nfreed[b] = 0;
-      d.nalloc[b] = 0;
-    }
-    return;
+  // the directory, stored to LDS at the end of step 1
+  const int ne = Hkv * d.ndir;
+  const bool dir_lds = ne <= kLdsDir;
+  int dv0[kLdsDir / 1024];
+#pragma unroll
+  for (int u = 0; u < kLdsDir / 1024; ++u) {
+    const int e = tid + 1024 * u;
+    const int v = dir[min(e, ne - 1)];
+    dv0[u] = e < ne ? v : -1;
   }
+  auto dir_at = [&](int e) { return dir_lds ? sdir[e] : dir[e]; };
   for (int i = tid; i < (C + 31) / 32; i += 1024) mand[i] = 0;
 
   // 1. position of every selected partition in the canonical page list (the
   //    first 1024 items' ids, lengths and first pages stay in registers for 2)
   int carry = 0;
   int p_keep = -1, len_keep = 0, first_keep = 0;
+  bool bad_part = false;  // reported once the step is known not to go back
   for (int base = 0; base < n_items; base += 1024) {
     const int i = base + tid;
     int np = 0;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
             first_keep = pf;
           }
         } else {
-          atomicOr(d.err, kErrPartition);
+          bad_part = true;
         }
       }
     }
@@ -137,7 +138,38 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   }
   if (tid == 0) item_off[n_items] = carry;
   const int M = carry;
+  if (dir_lds) {
+#pragma unroll
+    for (int u = 0; u < kLdsDir / 1024; ++u) {
+      const int e = tid + 1024 * u;
+      if (e < ne) sdir[e] = dv0[u];
+    }
+  }
   __syncthreads();
+  if (t < t_prev) {
+    // Steps never go back: below the last resolved step some ages t -
+    // last_use would be negative.  Refused before anything in global memory
+    // changes (step 1 above only read it; the error word reports the
+    // rewind); the step's lists are left empty, so the kernels after this
+    // one do nothing for the request and its heads attend no pages.  Checked
+    // here rather than first so that step 1's loads do not wait for the two
+    // step indices.  (t_prev is one load of one address: the branch is
+    // uniform over the workgroup.)
+    for (int i = tid; i < Hkv * MB; i += 1024) {
+      btb[i] = -1;
+      bnb[i] = 0;
+    }
+    if (tid < Hkv) bcount[(size_t)b * Hkv + tid] = 0;
+    if (tid <= Hkv) d.head_moff[(size_t)b * (Hkv + 1) + tid] = 0;
+    if (tid == 0) {
+      atomicOr(d.err, kErrStep);
+      d.nmiss[b] = 0;
+      d.nfreed[b] = 0;
+      d.nalloc[b] = 0;
+    }
+    return;
+  }
+  if (bad_part) atomicOr(d.err, kErrPartition);
 
   // block counts per head; clear the unused tail of the block table
   for (int i = tid; i < Hkv * MB; i += 1024) {
@@ -169,7 +201,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
 #pragma unroll
         for (int j = 0; j < kMaxPPP; ++j) {
           const int page = pf0 + j;
-          const int seg = j < np ? dir[h * d.ndir + (page >> 6)] : -1;
+          const int seg = j < np ? dir_at(h * d.ndir + (page >> 6)) : -1;
           segv[j] = seg;
           slots[j] = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
         }
@@ -254,8 +286,10 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
           ow[u] = ow0[u];
           lu[u] = lu0[u];
         } else {
-          ow[u] = c < C ? owner[c] : -1;
-          lu[u] = (c < C && need > 0) ? last[c] : 0;
+          const int cc = min(c, C - 1);
+          const int o = owner[cc], lv = last[cc];
+          ow[u] = c < C ? o : -1;
+          lu[u] = c < C ? lv : 0;
         }
       }
 #pragma unroll
@@ -280,6 +314,10 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     }
   }
   __syncthreads();
+  // from here on the bitmask flags the directory ranges whose segment this
+  // step empties (set by the victims' loop, listed in step 3's last scan)
+  if (need > 0)
+    for (int i = tid; i < (ne + 31) / 32; i += 1024) mand[i] = 0;
   const int E = (C + 1023) / 1024;  // contiguous slots per thread
   const int lo = min(C, tid * E), hi = min(C, lo + E);
   if (need > 0) {
@@ -350,17 +388,23 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         seg[u] = -2;  // not a victim
         if (own[u] >= 0) {
           const int h = own[u] / d.max_pages, page = own[u] - h * d.max_pages;
-          seg[u] = h < Hkv ? dir[h * d.ndir + (page >> 6)] : -1;
+          seg[u] = h < Hkv ? dir_at(h * d.ndir + (page >> 6)) : -1;
         }
       }
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
         if (seg[u] == -2) continue;
         const int c = cs[u];
-        const int page = own[u] % d.max_pages;
+        const int h = own[u] / d.max_pages, page = own[u] - h * d.max_pages;
         if (seg[u] >= 0 && seg[u] < d.n_seg) {
           d.segments[(size_t)seg[u] * kSegEntries + (page & 63)] = -1;
-          atomicSub(&d.seg_live[seg[u]], 1);
+          // the victim that takes its segment's live count to zero flags the
+          // range: every linked segment holds at least one resident page, so
+          // these are exactly the segments this step empties
+          if (atomicSub(&d.seg_live[seg[u]], 1) == 1) {
+            const int e = h * d.ndir + (page >> 6);
+            atomicOr(&mand[e >> 5], 1u << (e & 31));
+          }
         } else {
           atomicOr(d.err, kErrState);
         }
@@ -371,30 +415,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     }
     __syncthreads();
     // emptied segments leave the directory, in (head, directory index) order:
-    // flag them (a bit per directory entry, reusing the mandatory bitmask,
-    // which is no longer read), then list them with one ordered scan
-    const int ne = Hkv * d.ndir;
-    for (int i = tid; i < (ne + 31) / 32; i += 1024) mand[i] = 0;
-    __syncthreads();
-    constexpr int UE = 4;  // entries whose loads are in flight together
-    for (int e0 = tid; e0 < ne; e0 += 1024 * UE) {
-      int seg[UE], live[UE];
-#pragma unroll
-      for (int u = 0; u < UE; ++u) {
-        const int e = e0 + 1024 * u;
-        seg[u] = e < ne ? dir[e] : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < UE; ++u)
-        live[u] = (seg[u] >= 0 && seg[u] < d.n_seg) ? load_device(&d.seg_live[seg[u]]) : 1;
-#pragma unroll
-      for (int u = 0; u < UE; ++u)
-        if (live[u] == 0) {
-          const int e = e0 + 1024 * u;
-          atomicOr(&mand[e >> 5], 1u << (e & 31));
-        }
-    }
-    __syncthreads();
+    // one ordered scan over the flags the victims set
     const int Ed = (ne + 1023) / 1024;
     const int elo = min(ne, tid * Ed), ehi = min(ne, elo + Ed);
     int nf = 0;
@@ -402,8 +423,9 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
     int r = block_excl_scan<1024>(nf, tmp, &nfreed);
     for (int e = elo; e < ehi; ++e)
       if ((mand[e >> 5] >> (e & 31)) & 1u) {
-        d.freed[(size_t)b * ne + r++] = dir[e];
+        d.freed[(size_t)b * ne + r++] = dir_at(e);
         dir[e] = -1;
+        if (dir_lds) sdir[e] = -1;
       }
   }
 
@@ -446,7 +468,6 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
   //    (canonical order; inserts of one range are consecutive)
   int nalloc = 0;
   {
-    const int ne = Hkv * d.ndir;
     int ccarry = 0;
     for (int base = 0; base < assigned; base += 1024) {
       const int r = base + tid;
@@ -462,7 +483,7 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         // the entry now: step 3 emptied it (and flagged it) or left it as it was
         int dv;
         if (base == 0) dv = (need > 0 && ((mand[e >> 5] >> (e & 31)) & 1u)) ? -1 : dir_pre;
-        else dv = dir[e];
+        else dv = dir_at(e);
         fl = (first && dv < 0) ? 1 : 0;
       }
       int tot;
