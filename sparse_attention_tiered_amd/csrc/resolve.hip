@@ -197,13 +197,34 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         pl = base == 0 ? len_keep : plen[p];
         np = (pl + kPageTokens - 1) / kPageTokens;
         pos0 = item_off[i] - item_off[h * k];
+        // every page's segment entry loaded before any is tested (a page
+        // past the partition, or in a range without a valid segment, loads
+        // the first page's entry again and drops it; with one page per
+        // partition, a uniform case, only that page is loaded)
         int slots[kMaxPPP];
+        bool ok[kMaxPPP];
+        size_t at[kMaxPPP];
 #pragma unroll
         for (int j = 0; j < kMaxPPP; ++j) {
           const int page = pf0 + j;
           const int seg = j < np ? dir_at(h * d.ndir + (page >> 6)) : -1;
           segv[j] = seg;
-          slots[j] = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
+          ok[j] = seg >= 0 && seg < d.n_seg;
+          at[j] = ok[j] ? (size_t)seg * kSegEntries + (page & 63) : 0;
+        }
+        if (!ok[0]) at[0] = 0;
+        if (d.max_ppp == 1) {
+          slots[0] = d.segments[at[0]];
+#pragma unroll
+          for (int j = 1; j < kMaxPPP; ++j) slots[j] = -1;
+        } else {
+#pragma unroll
+          for (int j = 0; j < kMaxPPP; ++j) slots[j] = d.segments[ok[j] ? at[j] : at[0]];
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxPPP; ++j) {
+          asm volatile("" : "+v"(slots[j]));
+          if (!ok[j]) slots[j] = -1;
         }
 #pragma unroll
         for (int j = 0; j < kMaxPPP; ++j) {
@@ -391,20 +412,20 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
           seg[u] = h < Hkv ? dir_at(h * d.ndir + (page >> 6)) : -1;
         }
       }
+      // the live-count decrements of all eight issued before any result is
+      // read; the victim that takes its segment's count to zero flags the
+      // range: every linked segment holds at least one resident page, so
+      // these are exactly the segments this step empties
+      int before[UV];
 #pragma unroll
       for (int u = 0; u < UV; ++u) {
+        before[u] = 0;
         if (seg[u] == -2) continue;
         const int c = cs[u];
-        const int h = own[u] / d.max_pages, page = own[u] - h * d.max_pages;
+        const int page = own[u] % d.max_pages;
         if (seg[u] >= 0 && seg[u] < d.n_seg) {
           d.segments[(size_t)seg[u] * kSegEntries + (page & 63)] = -1;
-          // the victim that takes its segment's live count to zero flags the
-          // range: every linked segment holds at least one resident page, so
-          // these are exactly the segments this step empties
-          if (atomicSub(&d.seg_live[seg[u]], 1) == 1) {
-            const int e = h * d.ndir + (page >> 6);
-            atomicOr(&mand[e >> 5], 1u << (e & 31));
-          }
+          before[u] = atomicSub(&d.seg_live[seg[u]], 1);
         } else {
           atomicOr(d.err, kErrState);
         }
@@ -412,6 +433,18 @@ __global__ __launch_bounds__(1024) void k_resolve(Dev d, const int* __restrict__
         last[c] = -1;
         code[c] = kCodeFree;
       }
+      // (an empty asm that takes each result as a register keeps the
+      // compiler from testing it inside its own branch, which would wait for
+      // every decrement before issuing the next)
+#pragma unroll
+      for (int u = 0; u < UV; ++u) asm volatile("" : "+v"(before[u]));
+#pragma unroll
+      for (int u = 0; u < UV; ++u)
+        if (before[u] == 1) {
+          const int h = own[u] / d.max_pages, page = own[u] - h * d.max_pages;
+          const int e = h * d.ndir + (page >> 6);
+          atomicOr(&mand[e >> 5], 1u << (e & 31));
+        }
     }
     __syncthreads();
     // emptied segments leave the directory, in (head, directory index) order:
