@@ -492,13 +492,17 @@ __global__ __launch_bounds__(kAttWG) void k_attend_merge_arrival(Dev d, const in
   __shared__ int tmp[kAttWG / 64 + 1];
   const int bh = blockIdx.x;
   const int b = bh / d.Hkv, h = bh - b * d.Hkv;
-  if (advance && bh == 0 && threadIdx.x == 0) *advance += 1;  // the next step's index
-  request_offsets<kAttWG>(d.nmiss, d.B, pm, tmp);
+  // the next step's index (an atomic whose result is not read: nothing waits
+  // for it here, and the next step's kernels run after this launch)
+  if (advance && bh == 0 && threadIdx.x == 0) atomicAdd(advance, 1);
+  // the head's own counts first, so their loads overlap the batch's prefix
   const int cnt = max(0, min(bcount[bh], d.max_blocks));
-  const int ns = (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res);  // resident-page splits
   const int nm = d.nmiss[b];
   const int* mo = d.head_moff + (size_t)b * (d.Hkv + 1);
-  const int j0 = pm[b] + min(max(mo[h], 0), nm), j1 = pm[b] + min(max(mo[h + 1], 0), nm);
+  const int mo0 = mo[h], mo1 = mo[h + 1];
+  request_offsets<kAttWG>(d.nmiss, d.B, pm, tmp);
+  const int ns = (cnt + head_pps(cnt, d.splits_res) - 1) / head_pps(cnt, d.splits_res);  // resident-page splits
+  const int j0 = pm[b] + min(max(mo0, 0), nm), j1 = pm[b] + min(max(mo1, 0), nm);
   const int G = d.G;
   merge_head(d, bh, ns + (j1 - j0),
              [&](int x, int hh, int dc, const float*& ml, const float*& po) {
