@@ -43,18 +43,19 @@ namespace spin {
 
 constexpr int kAttWG = 256;
 
-// Two floats as one 64-bit agent-scope (write-through) store / load: the
-// hand-over of split partials between workgroups of one launch.
+// Two floats as one 64-bit agent-scope (write-through) store, and the 64-bit
+// agent-scope load that reads them back with its two halves: the hand-over
+// of split partials between workgroups of one launch.
 __device__ __forceinline__ void store_pair_agent(float* p, float a, float b) {
   const unsigned long long v = ((unsigned long long)__float_as_uint(b) << 32) | __float_as_uint(a);
   __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void load_pair_agent(const float* p, float& a, float& b) {
-  const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-  a = __uint_as_float((uint32_t)v);
-  b = __uint_as_float((uint32_t)(v >> 32));
+__device__ __forceinline__ unsigned long long load_u64_agent(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ float lo_float(unsigned long long v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_float(unsigned long long v) { return __uint_as_float((uint32_t)(v >> 32)); }
 
 // Pages per split of a head with cnt pages: its pages spread evenly over the
 // head's `nsp` workgroups (whole pages per wave), so heads with fewer pages
@@ -314,36 +315,53 @@ __device__ __forceinline__ void attend_wg(const Dev& d, const uint16_t* __restri
   for (int e = 0; e < 8; ++e) of[e] = 0.f;
   constexpr int UX = 8;  // partials' loads in flight at a time
   for (int x0 = 0; x0 < ns; x0 += UX) {
-    float ms[UX], ls[UX], a[UX][8];
+    // each partial as five 64-bit words ((max, sum), then 8 dims), loaded
+    // under its condition and passed through an empty asm before anything
+    // reads them: otherwise the compiler unpacks each word inside its load's
+    // branch and waits for it there, before the next partial's loads
+    unsigned long long w[UX][5];
 #pragma unroll
     for (int u = 0; u < UX; ++u) {
       const int x = x0 + u;
-      ms[u] = -INFINITY;
-      ls[u] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[u][e] = 0.f;
+      for (int k = 0; k < 5; ++k) w[u][k] = 0ull;
       if (x < ns && x != split) {
         const size_t pi = ((size_t)bh * 2 * d.splits + x) * G + hh;
-        load_pair_agent(d.part_ml + 2 * pi, ms[u], ls[u]);
+        w[u][0] = load_u64_agent(d.part_ml + 2 * pi);
         const float* po = d.part_o + pi * kHeadDim + dc;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) load_pair_agent(po + e, a[u][e], a[u][e + 1]);
-      } else if (x == split) {
-        ms[u] = M;
-        ls[u] = L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[u][e] = o[e];
+        for (int k = 0; k < 4; ++k) w[u][1 + k] = load_u64_agent(po + 2 * k);
       }
     }
 #pragma unroll
-    for (int u = 0; u < UX; ++u) {
-      if (ms[u] == -INFINITY) continue;
-      const float Mn = fmaxf(Mf, ms[u]);
-      const float fo = Mf == -INFINITY ? 0.f : exp2f(Mf - Mn), fn = exp2f(ms[u] - Mn);
-      Mf = Mn;
-      Lf = Lf * fo + ls[u] * fn;
+    for (int u = 0; u < UX; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) of[e] = of[e] * fo + a[u][e] * fn;
+      for (int k = 0; k < 5; ++k) asm volatile("" : "+v"(w[u][k]));
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+      const int x = x0 + u;
+      float ms = -INFINITY, ls = 0.f, a[8];
+      if (x < ns && x != split) {
+        ms = lo_float(w[u][0]);
+        ls = hi_float(w[u][0]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[2 * k] = lo_float(w[u][1 + k]);
+          a[2 * k + 1] = hi_float(w[u][1 + k]);
+        }
+      } else if (x == split) {
+        ms = M;
+        ls = L;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = o[e];
+      }
+      if (ms == -INFINITY) continue;
+      const float Mn = fmaxf(Mf, ms);
+      const float fo = Mf == -INFINITY ? 0.f : exp2f(Mf - Mn), fn = exp2f(ms - Mn);
+      Mf = Mn;
+      Lf = Lf * fo + ls * fn;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) of[e] = of[e] * fo + a[e] * fn;
     }
   }
   const float inv = Lf > 0.f ? 1.f / Lf : 0.f;
