@@ -43,7 +43,7 @@ class Pair:
 
     def __init__(self, w: W.Workload, n_steps=None, attend_pps=0, num_segments=None,
                  slots=None, oracle=True, threads=None, offload_extra_pages=None,
-                 host_segments=False):
+                 host_segments=False, max_pages=None):
         t0 = time.time()
         self.w = w
         self.geo = geo = W.geometry(w)
@@ -51,7 +51,13 @@ class Pair:
         self.T = self.draws.q_bits.shape[0]
         C = w.slots_per_request if slots is None else slots
         extra = offload_extra_pages or 0
+        sized_pages = max_pages
         max_parts, max_pages = geo.max_parts + extra, geo.max_pages + extra
+        if sized_pages is not None:
+            # a context sized for longer requests than it holds: a larger
+            # directory (and partition table) than the data needs
+            max_pages = max(sized_pages, max_pages)
+            max_parts = max(max_parts, -(-max_pages // geo.max_ppp))
         self.cfg = bd.make_config(w.B, w.Hq, w.Hkv, max_parts, max_pages, w.k, C,
                                   num_segments=num_segments, max_pages_per_partition=geo.max_ppp,
                                   attend_pages_per_split=attend_pps, host_segments=host_segments)

@@ -294,6 +294,21 @@ def test_size_limits(spin_lib):
     p.close()
 
 
+def test_directory_beyond_lds(spin_lib):
+    """A request directory larger than the resolve kernel keeps in LDS (16 KV
+    heads x 313 ranges of 64 pages = 5008 entries > 4096): every lookup and
+    the emptied-range returns go through global memory, under a tight budget
+    so the bucketed LRU empties segments every step."""
+    w = W.variant(W.C5, name="dir_global", B=2, Hq=16, Hkv=16, ctx=(40000, 23000), k=12, steps=10,
+                  n_centroids=64, ar_coef=0.3)
+    p = _pair(w, slots=16 * 12 * 4 + 24, max_pages=20000)
+    assert p.cfg.num_kv_heads * ((p.cfg.max_pages + 63) // 64) > 4096
+    p.check_summaries()
+    st, _ = p.run()
+    assert st.evictions > 0
+    p.close()
+
+
 def test_tight_budget_with_limits(spin_lib):
     """Eviction at k = 1024 with variable partitions of up to 4 pages."""
     w = W.variant(W.C5, name="limits_var", B=1, Hq=16, Hkv=1, ctx=(300000,), k=1024, steps=4,
