@@ -339,8 +339,11 @@ __device__ void topk_coarse(TopkLds<NT>& L, float* vals, int n, int k, BinMap m,
                             int* out) {
   static_assert(NT >= kTopkCand && kCoarseBins == 4 * 64, "four bins per lane of one wave");
   const int tid = threadIdx.x, lane = tid & 63;
-  // 1. the boundary bin: counts from the top, four bins per lane of wave 0
-  if (tid < 64) {
+  // 1. the boundary bin: counts from the top, four bins per lane, found by
+  //    every wave on its own (the same scan of the same counts, so the same
+  //    answer in each, and no barrier to pass it on)
+  int cut, above, mem;
+  {
     int c[4], sum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -349,25 +352,21 @@ __device__ void topk_coarse(TopkLds<NT>& L, float* vals, int n, int k, BinMap m,
     }
     const int inc = wave_incl_scan(sum);
     const int lead = __ffsll((long long)__ballot(inc >= k)) - 1;  // exists: the total is n > k
-    if (lane == lead) {
-      int above = inc - sum, b = kCoarseBins - 1 - 4 * lane, mem = c[0];
+    int ab = inc - sum, b = kCoarseBins - 1 - 4 * lane, mb = c[0];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        b = kCoarseBins - 1 - 4 * lane - j;
-        mem = c[j];
-        if (above + c[j] >= k) break;
-        above += c[j];
-      }
-      L.sh[0] = b;
-      L.sh[1] = above;
-      L.sh[3] = mem;
+    for (int j = 0; j < 4; ++j) {
+      b = kCoarseBins - 1 - 4 * lane - j;
+      mb = c[j];
+      if (ab + c[j] >= k) break;
+      ab += c[j];
     }
+    cut = __builtin_amdgcn_readlane(b, lead);
+    above = __builtin_amdgcn_readlane(ab, lead);
+    mem = __builtin_amdgcn_readlane(mb, lead);
   }
-  __syncthreads();
-  const int cut = L.sh[0];
-  const int need = k - L.sh[1];  // >= 1: taken from the boundary bin
-  const int mem = L.sh[3];       // its members
-  if (mem > kTopkCand) {         // (uniform over the workgroup)
+  const int need = k - above;  // >= 1: taken from the boundary bin
+  if (mem > kTopkCand) {  // (uniform over the workgroup)
+    __syncthreads();       // every wave is done reading the counts it reuses
     topk_select<NT>(L, vals, n, k, mn, mx, out);
     return;
   }
