@@ -411,29 +411,26 @@ __device__ void topk_coarse(TopkLds<NT>& L, float* vals, int n, int k, BinMap m,
     }
     if (lane < mem && rank < need) atomicOr(&L.chosen[me >> 5], 1u << (me & 31));
   }
-  // 4. ids ascending: an exclusive prefix of the bitmask words' popcounts
-  //    (wave 0, consecutive words per lane), into the histogram's space.  In
-  //    the readlane case wave 0 set the members' bits itself just before:
-  //    one wave's LDS accesses take effect in program order.
-  const int nw = (n + 31) / 32;
-  int* wpre = L.hist;
+  // 4. ids ascending, written by wave 0 alone: consecutive bitmask words per
+  //    lane, an exclusive prefix of their popcounts, then each lane writes
+  //    the ids of its words' set bits (no barrier, no pass over every id by
+  //    the whole workgroup).  In the readlane case wave 0 set the members'
+  //    bits itself just before: one wave's LDS accesses take effect in
+  //    program order.
   if (tid < 64) {
+    const int nw = (n + 31) / 32;
     const int W = (nw + 63) / 64;
     const int w0 = lane * W, w1 = min(nw, w0 + W);
     int sum = 0;
     for (int w = w0; w < w1; ++w) sum += __popc(L.chosen[w]);
-    int ex = wave_incl_scan(sum) - sum;
+    int pos = wave_incl_scan(sum) - sum;
     for (int w = w0; w < w1; ++w) {
-      wpre[w] = ex;
-      ex += __popc(L.chosen[w]);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) {
-    const uint32_t word = L.chosen[i >> 5];
-    if ((word >> (i & 31)) & 1u) {
-      const int pos = wpre[i >> 5] + __popc(word & ((1u << (i & 31)) - 1u));
-      if (pos < k) out[pos] = i;
+      uint32_t word = L.chosen[w];
+      while (word != 0u) {
+        if (pos < k) out[pos] = 32 * w + __builtin_ctz(word);
+        ++pos;
+        word &= word - 1u;
+      }
     }
   }
 }
