@@ -87,7 +87,7 @@ class Pair:
                 lens = geo.lens[b] if w.var_len is not None else None
                 self.spin.offload(b, d_kv, t, w.ctx[b], lens)
                 if oracle:
-                    self.oracle.offload(b, pages.reshape(w.Hkv, geo.pages[b], -1), geo.lens[b], cap)
+                    self.oracle.offload(b, pages.reshape(w.Hkv, geo.pages[b], W.PAGE_ELEMS), geo.lens[b], cap)
         self.q_dev = torch.from_numpy(self.draws.q_bits.view(np.int16)).to("cuda")
         self.scores = torch.empty((w.B, w.Hkv, max_parts), dtype=torch.float32, device="cuda")
         log(f"[setup] {w.name} B={w.B} ctx={w.ctx[0]} C={C} segs={self.cfg.num_segments} "

@@ -21,7 +21,7 @@ from tests.conftest import gpu_available
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-N_CASES = 32
+N_CASES = 96
 
 
 def random_case(i: int):
@@ -81,7 +81,7 @@ def test_random_shape_parity(spin_lib, i):
     p.close()
 
 
-N_VARIANTS = 16
+N_VARIANTS = 48
 
 
 def variant_case(i: int):
