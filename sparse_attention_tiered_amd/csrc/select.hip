@@ -479,11 +479,22 @@ __global__ __launch_bounds__(NT) void k_topk(Dev d, const float* __restrict__ sc
   }
   const float* srow = scores + (size_t)bh * d.Nmax;
   float mn = INFINITY, mx = -INFINITY;
-  for (int i = tid; i < n; i += NT) {
-    const float v = srow[i];
-    vals[i] = v;
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
+  // eight scores' loads in flight per thread (from clamped indices, so no
+  // load sits in a branch of its own), one round trip per 8 NT scores
+  constexpr int U = 8;
+  for (int i0 = tid; i0 < n; i0 += NT * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = srow[min(i0 + NT * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + NT * u;
+      if (i < n) {
+        vals[i] = v[u];
+        mn = fminf(mn, v[u]);
+        mx = fmaxf(mx, v[u]);
+      }
+    }
   }
   topk_from_lds<NT>(L, vals, n, k, mn, mx, out);
 }
