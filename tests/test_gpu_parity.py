@@ -294,6 +294,19 @@ def test_size_limits(spin_lib):
     p.close()
 
 
+def test_split_select_at_its_limit(spin_lib):
+    """The several-workgroups-per-list select at the longest lists it takes:
+    4096 partitions (eight 512-row workgroups, 128 score ranges handed over)
+    and a ragged 4001 (a last workgroup with one row)."""
+    w = W.variant(W.C3, name="split_limit", B=2, Hq=16, Hkv=2, ctx=(4096 * 64, 4000 * 64 + 17), k=64,
+                  steps=6, hot_count=8)
+    p = _pair(w, slots=2 * 64 * 3)
+    assert p.geo.max_parts == 4096
+    st, _ = p.run()
+    assert st.misses > 0
+    p.close()
+
+
 def test_directory_beyond_lds(spin_lib):
     """A request directory larger than the resolve kernel keeps in LDS (16 KV
     heads x 313 ranges of 64 pages = 5008 entries > 4096): every lookup and
