@@ -327,8 +327,8 @@ def main():
     st_s0, _ = A.stats()
     s0_ret_ms = ev0[3].elapsed_time(ev0[4])
     step0 = {"ms": ev0[0].elapsed_time(ev0[6]), "misses": st_s0.misses, "kernel": "k_retrieve",
-             "retrieve_ms": s0_ret_ms,
-             "retrieve_GBps": st_s0.misses * PAGE_BYTES / (s0_ret_ms * 1e-3) / 1e9}
+             "retrieve_ms": s0_ret_ms, "bytes": st_s0.h2d_bytes,
+             "retrieve_GBps": st_s0.h2d_bytes / (s0_ret_ms * 1e-3) / 1e9}
     warm_up(A, 1)
     torch.cuda.synchronize()
     stA0, _ = A.stats()
@@ -394,14 +394,15 @@ def main():
     torch.cuda.synchronize()
     stB0, _ = Bx.stats()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(K)]
-    step_miss, step_hit = [], []
-    prev_m, prev_h = stB0.misses, stB0.hits
+    step_miss, step_hit, step_bytes = [], [], []
+    prev_m, prev_h, prev_b = stB0.misses, stB0.hits, stB0.h2d_bytes
     for i in range(K):
         staged(Bx, start + i, evs[i])
         st_i, _ = Bx.stats()
         step_miss.append(st_i.misses - prev_m)
         step_hit.append(st_i.hits - prev_h)
-        prev_m, prev_h = st_i.misses, st_i.hits
+        step_bytes.append(st_i.h2d_bytes - prev_b)  # read over the link: valid chunks only
+        prev_m, prev_h, prev_b = st_i.misses, st_i.hits, st_i.h2d_bytes
     stB1 = st_i
 
     def window_counts(s0, s1):
@@ -446,12 +447,15 @@ def main():
     # rate is the transfer's own for this many pages
     iso_r = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     spin.retrieve(copy_stream=S)
+    torch.cuda.synchronize()
+    h2d0 = spin.stats()[0].h2d_bytes
     iso_r[0].record(S)
     for _ in range(reps):
         spin.retrieve(copy_stream=S)
     iso_r[1].record(S)
     torch.cuda.synchronize()
     iso_retrieve_ms = iso_r[0].elapsed_time(iso_r[1]) / reps
+    iso_retrieve_bytes = (spin.stats()[0].h2d_bytes - h2d0) / reps
     # cold replays: a 512 MB read before each one fills the 256 MB memory-side
     # cache with clean lines of another buffer, so the kernel reads HBM (a write
     # would leave dirty lines whose write-back the kernel would pay for); an
@@ -518,13 +522,15 @@ def main():
     # algorithmic bytes per launch (one step)
     attend_bytes = (hits + misses) * PAGE_BYTES / K + w.B * w.Hq * 128 * (2 + 4)
     # the transfer's bytes per launch over the window (the same steps in both
-    # contexts), and its duration per launch measured in context B
-    retrieve_bytes = sum(step_miss) * PAGE_BYTES / K
-    last_step_bytes = step_miss[-1] * PAGE_BYTES
+    # contexts): what it read over the link (each missed page's chunks that
+    # hold valid tokens, 32 KiB for a full page), and its duration per launch
+    # measured in context B
+    retrieve_bytes = sum(step_bytes) / K
+    last_step_bytes = iso_retrieve_bytes
     # everything the transfer launch itself reads and writes: each missed page
-    # read over the link and written to its slot; with the overlap, also the
-    # resident pages it attends (read once) and the queries
-    launch_bytes = 2 * retrieve_bytes
+    # read over the link and written whole to its slot; with the overlap,
+    # also the resident pages it attends (read once) and the queries
+    launch_bytes = retrieve_bytes + sum(step_miss) * PAGE_BYTES / K
     if overlap:
         launch_bytes += sum(step_hit) / K * PAGE_BYTES + w.B * w.Hq * 128 * 2
     link = pcie_link()
@@ -552,10 +558,10 @@ def main():
     }
     # the transfer over the steps that move at least 8 MB (small transfers are
     # dominated by a fixed latency), and step 0 on its own
-    big = [i for i in range(K) if step_miss[i] * PAGE_BYTES >= 8e6]
+    big = [i for i in range(K) if step_bytes[i] >= 8e6]
     rl["retrieve"]["steps_ge_8MB"] = len(big)
     rl["retrieve"]["achieved_ge_8MB"] = (
-        sum(step_miss[i] for i in big) * PAGE_BYTES / (sum(ret_ms[i] for i in big) * 1e-3) / 1e9
+        sum(step_bytes[i] for i in big) / (sum(ret_ms[i] for i in big) * 1e-3) / 1e9
         if big else None)
     rl["retrieve"]["step0"] = step0
     rl["retrieve"]["isolated_last_step"] = {

@@ -21,7 +21,10 @@
  *   page     64 token slots of one KV head, 32768 bytes:
  *            keys   [64 tokens][128 dims] bf16, token-major, then
  *            values [128 dims][64 tokens] bf16, dim-major (transposed).
- *            Slots past a partition's last token are ignored.
+ *            Slots past a partition's last token are ignored: a transfer
+ *            reads the key rows of the valid tokens and the whole value
+ *            half from host memory, and writes zeros over the other key
+ *            rows of the pool slot.
  *   host KV  one pinned, device-mapped buffer per request:
  *            [Hkv][pages][page]; partition i of every head starts on page
  *            sum_{j<i} ceil(len_j / 64) ([GP] B: physical pages per head).
@@ -120,7 +123,9 @@ typedef struct spin_stats {
   uint64_t hits;           /* mandatory pages found resident, summed over steps */
   uint64_t misses;         /* mandatory pages fetched from host memory */
   uint64_t evictions;      /* pages reclaimed by the bucketed LRU */
-  uint64_t h2d_bytes;      /* misses * 32768 */
+  uint64_t h2d_bytes;      /* bytes the transfers read from host memory: per fetched
+                              page 256 per valid token's key row + 16384 of values
+                              (32768 for a full page); replays count again */
   int32_t live_segments;   /* segments linked into the directory now */
   int32_t error_word;      /* SPIN_DEVERR_* bits */
 } spin_stats;

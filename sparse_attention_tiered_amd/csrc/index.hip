@@ -48,6 +48,7 @@ __global__ void k_init(Dev d) {
   if (tid == 0) {
     d.seg_ctl[0] = d.n_seg;
     d.err[0] = 0;
+    d.h2d[0] = 0;
   }
 }
 

@@ -3,9 +3,10 @@
 // from the CPU page table, then the transfer is issued; [GP] B: pages are per
 // KV head, so only the needed head's 32 KiB crosses the link).
 //
-// The GPU pulls the pages itself: each workgroup reads whole 32 KiB pages
-// through the host buffer's device-mapped address with 16-byte loads per lane
-// (two pages, sixteen loads, in flight per lane) and writes them to HBM.  The host never reads the miss count: the grid is fixed and
+// The GPU pulls the pages itself: each workgroup reads 32 KiB pages through
+// the host buffer's device-mapped address with 16-byte loads per lane (two
+// pages, sixteen loads, in flight per lane; key rows of valid tokens only)
+// and writes them whole to HBM.  The host never reads the miss count: the grid is fixed and
 // every workgroup strides over the batch's insert lists, which k_resolve
 // writes, so the transfer does not wait for the segment-pool pass.
 #include "arrival.h"
@@ -30,34 +31,46 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
   // where each request's misses start in the batch-wide concatenation of the
   // insert lists k_resolve wrote (requests ascending, canonical order)
   const int M = request_offsets<kRetrieveWG>(d.nmiss, d.B, pm, tmp);
-  // a page's source and destination, or null when its entry is out of range
-  auto page = [&](int j, const u32x4*& src, u32x4*& dst) {
+  // a page's source, destination and valid tokens, or null when its entry
+  // is out of range
+  auto page = [&](int j, const u32x4*& src, u32x4*& dst, int& ntok) {
     src = nullptr;
     dst = nullptr;
+    ntok = 0;
     if (j >= M) return;
     const int b = owner_of(pm, d.B, j);
-    const int4 m = d.ins[(size_t)b * d.max_mand + (j - pm[b])];  // (slot, KV head, page)
+    const size_t e = (size_t)b * d.max_mand + (j - pm[b]);
+    const int4 m = d.ins[e];  // (slot, KV head, page)
     if ((unsigned)m.x >= (unsigned)d.C || (unsigned)m.y >= (unsigned)d.Hkv ||
         (unsigned)m.z >= (unsigned)d.req_pages[b])
       return;
+    ntok = d.miss_tmp[e].w;
     src = reinterpret_cast<const u32x4*>(d.host_base[b] +
                                          ((size_t)m.y * d.req_stride[b] + m.z) * (size_t)kPageBytes);
     dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)b * d.C + m.x) * kPageElems);
   };
   // two pages in flight per workgroup (pages j and j + grid), 64 KiB
   const int nwg = gridDim.x;
+  unsigned long long moved = 0;  // bytes this workgroup read over the link
   for (int j = blockIdx.x; j < M; j += 2 * nwg) {
     const u32x4 *s0, *s1;
     u32x4 *d0, *d1;
-    page(j, s0, d0);
-    page(j + nwg, s1, d1);
+    int n0, n1;
+    page(j, s0, d0, n0);
+    page(j + nwg, s1, d1, n1);
     u32x4 v[8], w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0) v[u] = s0[u * kRetrieveWG + tid];
+    for (int u = 0; u < 8; ++u) {
+      const int c = u * kRetrieveWG + tid;
+      if (s0) v[u] = chunk_live(c, n0) ? s0[c] : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s1) w[u] = s1[u * kRetrieveWG + tid];
+    for (int u = 0; u < 8; ++u) {
+      const int c = u * kRetrieveWG + tid;
+      if (s1) w[u] = chunk_live(c, n1) ? s1[c] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (s0) moved += link_bytes(n0);
+    if (s1) moved += link_bytes(n1);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (d0) __builtin_nontemporal_store(v[u], d0 + u * kRetrieveWG + tid);
@@ -65,6 +78,7 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
     for (int u = 0; u < 8; ++u)
       if (d1) __builtin_nontemporal_store(w[u], d1 + u * kRetrieveWG + tid);
   }
+  if (tid == 0 && moved) atomicAdd(d.h2d, moved);
 }
 
 __global__ __launch_bounds__(kRetrieveWG) void k_retrieve_attend(Dev d, const uint16_t* __restrict__ q) {

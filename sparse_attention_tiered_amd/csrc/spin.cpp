@@ -166,7 +166,7 @@ struct Layout {
       seg_live, seg_stack, seg_ctl, owner, last_use, free_count, budget, last_t, scores, arrive, srange,
       miss_tmp, ins,
       nmiss,
-      freed, nfreed, alloc, nalloc, bmiss, att_arrive, part_o, part_ml, arr_o, arr_ml, head_moff, stats, err,
+      freed, nfreed, alloc, nalloc, bmiss, att_arrive, part_o, part_ml, arr_o, arr_ml, head_moff, stats, h2d, err,
       total;
 };
 
@@ -216,6 +216,7 @@ Layout layout(const spin_config* c, const Derived& d) {
   L.arr_ml = take(B * d.max_mand * d.G * 2 * sizeof(float));
   L.head_moff = take(B * (Hkv + 1) * sizeof(int));
   L.stats = take(B * 4 * sizeof(long long));
+  L.h2d = take(sizeof(unsigned long long));
   L.err = take(4 * sizeof(int));
   L.total = o;
   return L;
@@ -371,6 +372,7 @@ SPIN_API int spin_create_ex(const spin_config* cfg, void* d_ws, size_t ws_bytes,
   v.arr_ml = reinterpret_cast<float*>(w + L.arr_ml);
   v.head_moff = reinterpret_cast<int*>(w + L.head_moff);
   v.stats = reinterpret_cast<long long*>(w + L.stats);
+  v.h2d = reinterpret_cast<unsigned long long*>(w + L.h2d);
   v.err = reinterpret_cast<int*>(w + L.err);
   v.pool = static_cast<uint16_t*>(d_pool);
   v.step_t = nullptr;
@@ -769,7 +771,9 @@ SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* st, int64_t* per_request)
   HIPCHK(ctx, hipDeviceSynchronize());
   std::vector<long long> s(4 * (size_t)v.B);
   int top = 0, err = 0;
+  unsigned long long h2d = 0;
   HIPCHK(ctx, hipMemcpy(s.data(), v.stats, s.size() * sizeof(long long), hipMemcpyDeviceToHost));
+  HIPCHK(ctx, hipMemcpy(&h2d, v.h2d, sizeof(h2d), hipMemcpyDeviceToHost));
   HIPCHK(ctx, hipMemcpy(&top, v.seg_ctl, sizeof(int), hipMemcpyDeviceToHost));
   HIPCHK(ctx, hipMemcpy(&err, v.err, sizeof(int), hipMemcpyDeviceToHost));
   if (st) {
@@ -779,7 +783,7 @@ SPIN_API int spin_get_stats(spin_ctx* ctx, spin_stats* st, int64_t* per_request)
       st->misses += s[4 * b + 1];
       st->evictions += s[4 * b + 2];
     }
-    st->h2d_bytes = st->misses * (uint64_t)spin::kPageBytes;
+    st->h2d_bytes = h2d;
     st->live_segments = v.n_seg - top;
     st->error_word = err;
   }

@@ -75,6 +75,7 @@ struct Dev {
   float* arr_ml;               // [B * max_mand][G][2]
   int* head_moff;              // [B][Hkv + 1] first insert-list index of each head; [Hkv] = count
   long long* stats;            // [B][4] hits, misses, evictions, last cutoff
+  unsigned long long* h2d;     // [1] bytes the transfers read over the link, cumulative
   int* err;                    // [1] error bits
   uint16_t* pool;              // [B * C][kPageElems]
   // Device-side step index (spin_step_at): when set, kernels take the step t

@@ -5,9 +5,11 @@ the oracle's (exact, except members whose oracle scores are within 1e-5 of the
 oracle's k-th score); then the GPU's resolve is fed the *oracle's* selection,
 so a legitimate near-tie cannot cascade into a state mismatch, and the whole
 residency state is compared bit for bit; every pool slot the step filled is
-compared byte for byte with the oracle's copy of the host page; attention
-outputs are compared within max-abs 2e-3.  Nothing the GPU produces is fed to
-the oracle.
+compared byte for byte with the oracle's copy of the host page (whose token
+slots past the valid ones are zero, as the transfer leaves them), and the
+device's count of bytes read over the link must have grown by exactly the
+valid key rows and the value halves of those pages; attention outputs are
+compared within max-abs 2e-3.  Nothing the GPU produces is fed to the oracle.
 
 Whole-step parity (Pair.run_graph, the benchmark's captured one-launch step):
 the GPU selects for itself, so once its selection is shown valid (equal to the
@@ -182,6 +184,21 @@ class Pair:
         """Every slot this step's retrieve filled."""
         return self.check_pool([g for g, *_ in self.oracle._pending], f"step {t} inserts")
 
+    def check_link_bytes(self, t, blocks):
+        """The step's transfer read over the link exactly the key rows of each
+        inserted page's valid tokens (256 bytes each) and its whole value half
+        (16 KiB): the device's byte counter moved by that much since the last
+        check."""
+        ntok = {}
+        for b in range(self.w.B):
+            for h in range(self.w.Hkv):
+                for g, n in blocks[b][h]:
+                    ntok[g] = n
+        want = sum(256 * ntok[g] + 16384 for g, *_ in self.oracle._pending)
+        now = self.spin.stats()[0].h2d_bytes
+        assert now - self._h2d == want, (t, now - self._h2d, want)
+        self._h2d = now
+
     def check_resident(self):
         """Every resident slot of every request."""
         o = self.oracle
@@ -252,6 +269,7 @@ class Pair:
         total_flips = 0
         checked = 0
         worst = 0.0
+        self._h2d = self.spin.stats()[0].h2d_bytes
         for t in range(steps):
             if on_step is not None:
                 on_step(t)
@@ -270,6 +288,7 @@ class Pair:
                 self.check_blocks(t, blocks)
             self.spin.retrieve()
             self.oracle.retrieve()
+            self.check_link_bytes(t, blocks)
             self.last_blocks = blocks
             out = self.spin.attend(q).cpu().numpy()
             qb = self.draws.q_bits[t]
@@ -333,6 +352,7 @@ class Pair:
         torch.cuda.synchronize()
         graph = None
         flips_total, worst = 0, 0.0
+        self._h2d = self.spin.stats()[0].h2d_bytes
         for t in range(steps):
             if on_step is not None:
                 on_step(t)
@@ -356,6 +376,7 @@ class Pair:
             self.check_state(t)
             self.check_blocks(t, blocks)
             self.oracle.retrieve()
+            self.check_link_bytes(t, blocks)
             out = self.spin.out.cpu().numpy()
             qb = self.draws.q_bits[t]
             if out_sample is None:
