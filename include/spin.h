@@ -21,10 +21,10 @@
  *   page     64 token slots of one KV head, 32768 bytes:
  *            keys   [64 tokens][128 dims] bf16, token-major, then
  *            values [128 dims][64 tokens] bf16, dim-major (transposed).
- *            Slots past a partition's last token are ignored: a transfer
- *            reads the key rows of the valid tokens and the whole value
- *            half from host memory, and writes zeros over the other key
- *            rows of the pool slot.
+ *            Slots past a partition's last token are ignored and may hold
+ *            anything in host memory: a transfer reads the key rows of the
+ *            valid tokens and the whole value half, and the pool slot gets
+ *            zeros in every key and value entry of the other token slots.
  *   host KV  one pinned, device-mapped buffer per request:
  *            [Hkv][pages][page]; partition i of every head starts on page
  *            sum_{j<i} ceil(len_j / 64) ([GP] B: physical pages per head).

@@ -12,17 +12,37 @@ namespace spin {
 constexpr int kXferPagesPerWG = 4, kXferMinWG = 16;
 
 // A transfer reads the key rows of a page's valid tokens (its partition's
-// tokens on that page) and every value row, and writes zeros over the key
-// rows past them, which attention never uses.  Keys are token-major, 256
-// contiguous bytes (16 chunks of 16 bytes) per token, so a partly filled page
-// skips a contiguous tail; values are dim-major, where the valid tokens are a
-// prefix of each 128-byte dimension row: reading only those prefixes measured
-// no faster than reading the rows whole (a 1M-token workload with variable
-// partitions: 1312 us per step's transfer either way, against 1450 us for
-// whole pages), so the value half moves whole.
-__device__ __forceinline__ bool chunk_live(int c, int ntok) {
-  return c >= kPageTokens * kHeadDim / 8 || (c >> 4) < ntok;
+// tokens on that page) and every value row, and leaves zeros in the pool slot
+// for every token slot past them, whatever the host buffer holds there
+// (attention gives those slots zero weight, and a zero value keeps a product
+// with that weight zero, where a NaN in host padding would not).  Keys are
+// token-major, 256 contiguous bytes (16 chunks of 16 bytes) per token, so a
+// partly filled page skips a contiguous tail; values are dim-major, where the
+// valid tokens are a prefix of each 128-byte dimension row: reading only
+// those prefixes measured no faster than reading the rows whole (a 1M-token
+// workload with variable partitions: 1312 us per step's transfer either way,
+// against 1450 us for whole pages), so the value half moves whole and its
+// entries past the valid tokens are zeroed in registers.
+constexpr int kKeyChunks = kPageTokens * kHeadDim / 8;  // 16-byte chunks of the key half
+
+__device__ __forceinline__ bool chunk_live(int c, int ntok) { return c >= kKeyChunks || (c >> 4) < ntok; }
+
+// chunk c of a page as it goes to the pool: a value chunk (8 consecutive
+// tokens of one dimension, two bf16 per word, the lower token in the low
+// half) with the entries of tokens at or past ntok set to zero
+__device__ __forceinline__ u32x4 pool_chunk(u32x4 v, int c, int ntok) {
+  if (c < kKeyChunks) return v;
+  const int keep = ntok - ((c & 7) << 3);  // tokens of this chunk below ntok
+  if (keep < 8) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned m = (2 * w < keep ? 0x0000ffffu : 0u) | (2 * w + 1 < keep ? 0xffff0000u : 0u);
+      v[w] &= m;
+    }
+  }
+  return v;
 }
+
 // the bytes a transfer reads over the link for a page of ntok valid tokens
 __device__ __forceinline__ unsigned long long link_bytes(int ntok) {
   return 256ull * (unsigned)ntok + (unsigned long long)kPageTokens * kHeadDim * 2;
@@ -116,8 +136,9 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
       u32x4* dst = reinterpret_cast<u32x4*>(d.pool + ((size_t)cur.b * d.C + cur.m.x) * kPageElems);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        __builtin_nontemporal_store(v[u], dst + u * kRetrieveWG + tid);
-        page[u * kRetrieveWG + tid] = v[u];
+        const u32x4 x = pool_chunk(v[u], u * kRetrieveWG + tid, cur.ntok);
+        __builtin_nontemporal_store(x, dst + u * kRetrieveWG + tid);
+        page[u * kRetrieveWG + tid] = x;
       }
     }
     __syncthreads();

@@ -73,10 +73,10 @@ __global__ __launch_bounds__(kRetrieveWG) void k_retrieve(Dev d) {
     if (s1) moved += link_bytes(n1);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (d0) __builtin_nontemporal_store(v[u], d0 + u * kRetrieveWG + tid);
+      if (d0) __builtin_nontemporal_store(pool_chunk(v[u], u * kRetrieveWG + tid, n0), d0 + u * kRetrieveWG + tid);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (d1) __builtin_nontemporal_store(w[u], d1 + u * kRetrieveWG + tid);
+      if (d1) __builtin_nontemporal_store(pool_chunk(w[u], u * kRetrieveWG + tid, n1), d1 + u * kRetrieveWG + tid);
   }
   if (tid == 0 && moved) atomicAdd(d.h2d, moved);
 }

@@ -45,7 +45,7 @@ class Pair:
 
     def __init__(self, w: W.Workload, n_steps=None, attend_pps=0, num_segments=None,
                  slots=None, oracle=True, threads=None, offload_extra_pages=None,
-                 host_segments=False, max_pages=None):
+                 host_segments=False, max_pages=None, pad_fill=None):
         t0 = time.time()
         self.w = w
         self.geo = geo = W.geometry(w)
@@ -71,6 +71,8 @@ class Pair:
             # the full KV starts in pinned host memory and is indexed there
             self.host = [bd.pinned_u16(w.Hkv * max(geo.pages[b], 1) * W.PAGE_ELEMS) for b in range(w.B)]
             W.fill_all(w, geo, self.draws, [h[1] for h in self.host], threads)
+            if pad_fill is not None:
+                self._fill_padding(pad_fill)
             for b in range(w.B):
                 lens = geo.lens[b] if w.var_len is not None else None
                 self.spin.index(b, self.host[b][0], w.ctx[b], lens)
@@ -94,6 +96,49 @@ class Pair:
         self.scores = torch.empty((w.B, w.Hkv, max_parts), dtype=torch.float32, device="cuda")
         log(f"[setup] {w.name} B={w.B} ctx={w.ctx[0]} C={C} segs={self.cfg.num_segments} "
             f"splits={self.spin.splits} in {time.time() - t0:.1f}s")
+
+    def _page_ntok(self, b):
+        """Valid tokens of each page of request b (partitions start on fresh pages)."""
+        out = []
+        for L in self.geo.lens[b]:
+            L = int(L)
+            out += [min(W.PAGE_TOKENS, L - W.PAGE_TOKENS * j) for j in range(-(-L // W.PAGE_TOKENS))]
+        return out
+
+    def _fill_padding(self, value):
+        """Write `value` into every key and value entry of every token slot
+        past a page's valid tokens, in the host copy (which the library is
+        told to ignore)."""
+        self.pad_zeroed = True
+        D, T = W.HEAD_DIM, W.PAGE_TOKENS
+        for b in range(self.w.B):
+            ntok = self._page_ntok(b)
+            pages = self.host[b][1][: self.w.Hkv * len(ntok) * W.PAGE_ELEMS].reshape(
+                self.w.Hkv, len(ntok), W.PAGE_ELEMS)
+            for p, n in enumerate(ntok):
+                if n < T:
+                    for h in range(self.w.Hkv):
+                        pages[h, p, n * D:T * D] = value
+                        pages[h, p, T * D:].reshape(D, T)[:, n:] = value  # (a view: rows are contiguous)
+
+    def _expected_pool(self, part):
+        """The oracle's pool rows of global slots `part`; with padding written
+        into the host copy, as the transfer leaves them: zeros past each
+        page's valid tokens."""
+        want = self.oracle.pool[part]
+        if not getattr(self, "pad_zeroed", False):
+            return want
+        want = want.copy()
+        D, T = W.HEAD_DIM, W.PAGE_TOKENS
+        o = self.oracle
+        for i, g in enumerate(part):
+            b, c = divmod(int(g), o.C)
+            page = int(o.owner[b, c]) % o.max_pages
+            n = self._page_ntok(b)[page]
+            if n < T:
+                want[i, n * D:T * D] = 0
+                want[i, T * D:].reshape(D, T)[:, n:] = 0
+        return want
 
     # ------------------------------------------------------------------ checks
     def n_parts(self, b):
@@ -173,7 +218,7 @@ class Pair:
         for a in range(0, len(gslots), 4096):   # at most 128 MiB at a time
             part = gslots[a:a + 4096]
             got = self._pool_rows(part)
-            want = self.oracle.pool[part]
+            want = self._expected_pool(part)
             if not np.array_equal(got, want):
                 bad = [int(s) for s, g, o in zip(part, got, want) if not np.array_equal(g, o)]
                 raise AssertionError(f"{what}: pool slots {bad[:8]} ({len(bad)} of {len(part)}) "

@@ -332,6 +332,22 @@ def test_tight_budget_with_limits(spin_lib):
     p.close()
 
 
+@pytest.mark.parametrize("form", ["staged", "graph"])
+def test_host_padding_is_never_used(spin_lib, form):
+    """Token slots past a partition's last token may hold anything in host
+    memory: here bf16 NaN in every key and value entry of every partly filled
+    page.  The transfer leaves zeros there in the pool (every filled and every
+    resident slot equals its host page with that padding zeroed), so the
+    outputs stay those of the valid tokens alone, within the usual tolerance
+    of the oracle (which reads only those), with eviction and re-fetches."""
+    w = W.variant(W.C5, name="nan_padding", cfg_id=77, B=2, Hq=8, Hkv=2, ctx=(6000, 4000), k=8,
+                  steps=16, n_centroids=16, var_len=(16, 200), ar_coef=0.5)
+    p = _pair(w, slots=2 * 8 * 4 + 2, pad_fill=0x7FC0)
+    st, worst = p.run() if form == "staged" else p.run_graph()
+    assert st.evictions > 0 and np.isfinite(worst)
+    p.close()
+
+
 # every key of a head is one vector (hot partitions shifted): scores tie
 # exactly inside each group, so the lower-id rule alone decides the selection
 TIES = {
