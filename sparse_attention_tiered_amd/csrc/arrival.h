@@ -111,13 +111,27 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
     if (wg >= nact) return;
     nwg = nact;
   }
+  // wave 0's queries for a page's G heads (zeros past G), loaded with the
+  // page's own loads, a page ahead, so no round trip of its own stands
+  // between a page's arrival and its attention (next to the PCIe pulls an
+  // HBM round trip takes many times longer than alone)
+  auto load_q = [&](const Item& it, bf16x8 (&qq)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qq[kb] = bf16x8{};
+    if (wave != 0 || !it.ok || r >= G) return;
+    const uint16_t* qp = q + ((size_t)it.b * d.Hq + (size_t)it.m.y * G + r) * kHeadDim;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qq[kb] = *reinterpret_cast<const bf16x8*>(qp + 32 * kb + 8 * g);
+  };
   int j = wg;
   Item cur;
   u32x4 v[8], vn[8];
+  bf16x8 qc[4], qn[4];
   unsigned long long moved = 0;  // bytes this workgroup read over the link
   if (j < M) {
     cur = item(j);
     load(cur, v);
+    load_q(cur, qc);
   }
   for (; j < M; j += nwg) {
     float* po = d.arr_o + (size_t)j * G * kHeadDim;
@@ -130,6 +144,7 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
     if (jn < M) {
       nxt = item(jn);
       load(nxt, vn);
+      load_q(nxt, qn);
     }
     if (cur.ok) {
       moved += link_bytes(cur.ntok);
@@ -149,16 +164,8 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
         pml[2 * r + 1] = 0.f;
       }
     } else if (wave == 0) {
-      const int b = cur.b, ntok = cur.ntok;
-      bf16x8 qb[4];
-      if (r < G) {
-        const uint16_t* qp = q + ((size_t)b * d.Hq + (size_t)cur.m.y * G + r) * kHeadDim;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qb[kb] = *reinterpret_cast<const bf16x8*>(qp + 32 * kb + 8 * g);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qb[kb] = bf16x8{};
-      }
+      const int ntok = cur.ntok;
+      const bf16x8* qb = qc;
       const uint16_t* P = reinterpret_cast<const uint16_t*>(page);
       bf16x8 ka[4][4];
       load_keys(P, r, g, ka);
@@ -225,6 +232,8 @@ __device__ __forceinline__ void retrieve_attend_wg(const Dev& d, const uint16_t*
     cur = nxt;
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = vn[u];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) qc[kb] = qn[kb];
   }
   if (tid == 0 && moved) atomicAdd(d.h2d, moved);
 }
