@@ -1,14 +1,15 @@
 // Retrieve: copy the step's missed pages from pinned host memory into their
 // GPU slots ([XT] design part 2, Fig. 5 steps 3-4: the host address comes
 // from the CPU page table, then the transfer is issued; [GP] B: pages are per
-// KV head, so only the needed head's 32 KiB crosses the link).
+// KV head, so only the needed head's page, at most 32 KiB, crosses the link).
 //
 // The GPU pulls the pages itself: each workgroup reads 32 KiB pages through
 // the host buffer's device-mapped address with 16-byte loads per lane (two
 // pages, sixteen loads, in flight per lane; key rows of valid tokens only)
-// and writes them whole to HBM.  The host never reads the miss count: the grid is fixed and
-// every workgroup strides over the batch's insert lists, which k_resolve
-// writes, so the transfer does not wait for the segment-pool pass.
+// and writes them whole to HBM.  The host never reads the miss count: the
+// grid is fixed and every workgroup strides over the batch's insert lists,
+// which k_resolve writes, so the transfer does not wait for the segment-pool
+// pass.
 #include "arrival.h"
 #include "device_util.h"
 #include "spin_internal.h"
