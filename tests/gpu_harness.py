@@ -98,12 +98,16 @@ class Pair:
             f"splits={self.spin.splits} in {time.time() - t0:.1f}s")
 
     def _page_ntok(self, b):
-        """Valid tokens of each page of request b (partitions start on fresh pages)."""
-        out = []
-        for L in self.geo.lens[b]:
-            L = int(L)
-            out += [min(W.PAGE_TOKENS, L - W.PAGE_TOKENS * j) for j in range(-(-L // W.PAGE_TOKENS))]
-        return out
+        """Valid tokens of each page of request b (partitions start on fresh
+        pages), as indexed (the padding test appends no tokens)."""
+        cache = self.__dict__.setdefault("_ntok_cache", {})
+        if b not in cache:
+            out = []
+            for L in self.geo.lens[b]:
+                L = int(L)
+                out += [min(W.PAGE_TOKENS, L - W.PAGE_TOKENS * j) for j in range(-(-L // W.PAGE_TOKENS))]
+            cache[b] = out
+        return cache[b]
 
     def _fill_padding(self, value):
         """Write `value` into every key and value entry of every token slot
