@@ -38,7 +38,8 @@ What each part follows:
   offload()        [XT] part 1 / Fig. 3: prefill KV copied to host, indexed.
   append()         decode-time append of a token (reading stated there).
   retrieve()       [XT] part 2 / Fig. 5 steps 3-4: host address from the CPU
-                   page table, copy of the missed pages.
+                   page table, copy of the missed pages' valid tokens (the
+                   token slots past them arrive as zeros, reading R25).
   attend()         [XT] part 1 / Fig. 3: attention over the selected
                    partitions only (softmax(q K^T / sqrt(D)) V).
 
@@ -150,7 +151,7 @@ class SpinOracle:
         self.budget = [slots_per_request] * B
         self.error = None
         self.stats = [dict(hits=0, misses=0, evictions=0, cutoff=-1) for _ in range(B)]
-        self._pending = []   # (global slot, b, h, page) copies for retrieve()
+        self._pending = []   # (global slot, b, h, page, valid tokens) copies for retrieve()
         # decode step of the last resolve: steps never go back, so every age
         # t - last_use is at least 0 (reading R23)
         self.last_t = -1
@@ -428,17 +429,26 @@ class SpinOracle:
                 self.owner[b, c] = h * self.max_pages + page
                 self.last_use[b, c] = t
                 blocks[b][h][bi][0] = b * self.C + c
-                inserts.append((b, h, page, c))
-        for (b, h, page, c) in inserts:
+                inserts.append((b, h, page, c, blocks[b][h][bi][1]))
+        for (b, h, page, c, ntok) in inserts:
             self.insert(b, h, page, c)
-            self._pending.append((b * self.C + c, b, h, page))
+            self._pending.append((b * self.C + c, b, h, page, ntok))
         return blocks
 
     def retrieve(self):
-        """Fig. 5 steps 3-4: copy each missed page (K and V bytes verbatim) from
-        its host address into its GPU slot.  Returns the bytes moved."""
-        for gslot, b, h, page in self._pending:
-            self.pool[gslot] = self.requests[b].host[h, page]
+        """Fig. 5 steps 3-4: copy each missed page from its host address into
+        its GPU slot: the keys and values of its valid tokens verbatim, and
+        zeros in every other token slot of the page, whatever the host holds
+        there (reading R25: token slots past a partition's last token carry
+        nothing the method uses).  Returns the bytes that land in the pool."""
+        D = self.D
+        for gslot, b, h, page, ntok in self._pending:
+            src = self.requests[b].host[h, page]
+            dst = np.zeros(PAGE_ELEMS, np.uint16)
+            dst[: ntok * D] = src[: ntok * D]                        # key rows, token-major
+            vs = src[PAGE_TOKENS * D:].reshape(D, PAGE_TOKENS)       # values, dim-major
+            dst[PAGE_TOKENS * D:].reshape(D, PAGE_TOKENS)[:, :ntok] = vs[:, :ntok]
+            self.pool[gslot] = dst
         return len(self._pending) * PAGE_ELEMS * 2
 
     # ------------------------------------------------------------------ Attention

@@ -5,8 +5,8 @@ the oracle's (exact, except members whose oracle scores are within 1e-5 of the
 oracle's k-th score); then the GPU's resolve is fed the *oracle's* selection,
 so a legitimate near-tie cannot cascade into a state mismatch, and the whole
 residency state is compared bit for bit; every pool slot the step filled is
-compared byte for byte with the oracle's copy of the host page (whose token
-slots past the valid ones are zero, as the transfer leaves them), and the
+compared byte for byte with the oracle's copy of the host page (its valid
+tokens, zeros in the other token slots), and the
 device's count of bytes read over the link must have grown by exactly the
 valid key rows and the value halves of those pages; attention outputs are
 compared within max-abs 2e-3.  Nothing the GPU produces is fed to the oracle.
@@ -97,26 +97,16 @@ class Pair:
         log(f"[setup] {w.name} B={w.B} ctx={w.ctx[0]} C={C} segs={self.cfg.num_segments} "
             f"splits={self.spin.splits} in {time.time() - t0:.1f}s")
 
-    def _page_ntok(self, b):
-        """Valid tokens of each page of request b (partitions start on fresh
-        pages), as indexed (the padding test appends no tokens)."""
-        cache = self.__dict__.setdefault("_ntok_cache", {})
-        if b not in cache:
-            out = []
-            for L in self.geo.lens[b]:
-                L = int(L)
-                out += [min(W.PAGE_TOKENS, L - W.PAGE_TOKENS * j) for j in range(-(-L // W.PAGE_TOKENS))]
-            cache[b] = out
-        return cache[b]
-
     def _fill_padding(self, value):
         """Write `value` into every key and value entry of every token slot
         past a page's valid tokens, in the host copy (which the library is
-        told to ignore)."""
-        self.pad_zeroed = True
+        told to ignore, and the oracle's transfer leaves as zeros)."""
         D, T = W.HEAD_DIM, W.PAGE_TOKENS
         for b in range(self.w.B):
-            ntok = self._page_ntok(b)
+            ntok = []
+            for L in self.geo.lens[b]:
+                L = int(L)
+                ntok += [min(T, L - T * j) for j in range(-(-L // T))]
             pages = self.host[b][1][: self.w.Hkv * len(ntok) * W.PAGE_ELEMS].reshape(
                 self.w.Hkv, len(ntok), W.PAGE_ELEMS)
             for p, n in enumerate(ntok):
@@ -124,25 +114,6 @@ class Pair:
                     for h in range(self.w.Hkv):
                         pages[h, p, n * D:T * D] = value
                         pages[h, p, T * D:].reshape(D, T)[:, n:] = value  # (a view: rows are contiguous)
-
-    def _expected_pool(self, part):
-        """The oracle's pool rows of global slots `part`; with padding written
-        into the host copy, as the transfer leaves them: zeros past each
-        page's valid tokens."""
-        want = self.oracle.pool[part]
-        if not getattr(self, "pad_zeroed", False):
-            return want
-        want = want.copy()
-        D, T = W.HEAD_DIM, W.PAGE_TOKENS
-        o = self.oracle
-        for i, g in enumerate(part):
-            b, c = divmod(int(g), o.C)
-            page = int(o.owner[b, c]) % o.max_pages
-            n = self._page_ntok(b)[page]
-            if n < T:
-                want[i, n * D:T * D] = 0
-                want[i, T * D:].reshape(D, T)[:, n:] = 0
-        return want
 
     # ------------------------------------------------------------------ checks
     def n_parts(self, b):
@@ -222,7 +193,7 @@ class Pair:
         for a in range(0, len(gslots), 4096):   # at most 128 MiB at a time
             part = gslots[a:a + 4096]
             got = self._pool_rows(part)
-            want = self._expected_pool(part)
+            want = self.oracle.pool[part]
             if not np.array_equal(got, want):
                 bad = [int(s) for s, g, o in zip(part, got, want) if not np.array_equal(g, o)]
                 raise AssertionError(f"{what}: pool slots {bad[:8]} ({len(bad)} of {len(part)}) "

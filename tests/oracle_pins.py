@@ -370,6 +370,59 @@ def pin_retrieve_bytes(om):
                     assert np.array_equal(o.pool[b * o.C + c], host[h, p])
 
 
+def pin_retrieve_padding(om):
+    """Reading R25: token slots past a partition's last token carry nothing
+    the method uses.  Two oracles get the same partitions, one with zeros and
+    one with NaN in every padding slot of the host pages: summaries,
+    selections, residency and outputs agree exactly (and stay finite), and
+    every resident slot holds its page's valid keys and values (token counts
+    taken from the partition lengths here) and zeros in all other token
+    slots."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, k = 2, 8, 2, 4
+    lens_all = [list(rng.integers(16, 200, size=int(rng.integers(30, 60)))) for _ in range(B)]
+    pages = [sum((L + 63) // 64 for L in lens) for lens in lens_all]
+    C = Hkv * k * 4 + 5
+    oz, on = make(om, B, Hq, Hkv, k, C, max(pages)), make(om, B, Hq, Hkv, k, C, max(pages))
+    hosts, ntoks = [], []
+    for b in range(B):
+        Kp, Vp = random_parts(rng, Hkv, lens_all[b])
+        bz, lens = pack_request(Kp, Vp, Hkv, pad_value=0.0)
+        bn, _ = pack_request(Kp, Vp, Hkv, pad_value=float("nan"))
+        oz.index(b, bz, lens)
+        on.index(b, bn, lens)
+        hosts.append(bn.reshape(Hkv, pages[b], -1))
+        ntoks.append([min(64, L - 64 * j) for L in lens for j in range((L + 63) // 64)])
+        assert np.array_equal(oz.requests[b].summaries, on.requests[b].summaries)
+    q = bf16_exact(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    partial = 0
+    for t in range(16):
+        q = bf16_exact(0.5 * q + rng.standard_normal(q.shape).astype(np.float32))
+        outs = []
+        for o in (oz, on):
+            sel, _ = o.select(bits(q))
+            blocks = o.resolve_evict(sel, t)
+            o.retrieve()
+            outs.append(o.attend(bits(q), blocks))
+        assert np.array_equal(oz.owner, on.owner) and np.all(np.isfinite(outs[1]))
+        assert np.array_equal(outs[0], outs[1])
+        assert np.array_equal(oz.pool, on.pool)
+        for b in range(B):
+            for c in range(C):
+                own = int(on.owner[b, c])
+                if own == -1:
+                    continue
+                h, p = divmod(own, on.max_pages)
+                n = ntoks[b][p]
+                partial += n < 64
+                got = on.pool[b * C + c]
+                host = hosts[b][h, p]
+                assert np.array_equal(got[: n * D], host[: n * D]) and not np.any(got[n * D: 64 * D])
+                gv, hv = got[64 * D:].reshape(D, 64), host[64 * D:].reshape(D, 64)
+                assert np.array_equal(gv[:, :n], hv[:, :n]) and not np.any(gv[:, n:])
+    assert partial > 0
+
+
 # ----------------------------------------------------------------------------- attention
 def pin_attend_dense(om):
     """k = all partitions and an ample pool: the sparse paged output equals dense
@@ -718,7 +771,7 @@ def pin_step_order(om):
 ALL_PINS = [
     pin_bf16_decode, pin_page_layout, pin_summary_closed_form, pin_score_closed_form,
     pin_topk_bruteforce, pin_lru_hand_example, pin_lru_properties, pin_two_level_table,
-    pin_retrieve_bytes, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
+    pin_retrieve_bytes, pin_retrieve_padding, pin_attend_dense, pin_attend_closed_forms, pin_step_invariants,
     pin_first_step_slots, pin_budget_shrink, pin_offload_append, pin_release_reindex,
     pin_step_order,
 ]

@@ -47,8 +47,9 @@ MUTATIONS = {
                                "slot_tok = int(req.lens[tail]) % PAGE_TOKENS"),
     "append_never_new_partition": ("if req.n_parts == 0 or req.lens[tail] % PAGE_TOKENS == 0:",
                                    "if req.n_parts == 0:"),
-    "retrieve_wrong_head": ("self.pool[gslot] = self.requests[b].host[h, page]",
-                            "self.pool[gslot] = self.requests[b].host[0, page]"),
+    "retrieve_wrong_head": ("src = self.requests[b].host[h, page]",
+                            "src = self.requests[b].host[0, page]"),
+    "retrieve_copies_padding": ("dst = np.zeros(PAGE_ELEMS, np.uint16)", "dst = src.copy()"),
     # request turnover
     "release_order_reversed": ("for e in range(self.ndir):\n                s = self.directory[b, h, e]\n                if s != FREE:\n",
                                "for e in reversed(range(self.ndir)):\n                s = self.directory[b, h, e]\n                if s != FREE:\n"),
