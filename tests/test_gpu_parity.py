@@ -307,6 +307,28 @@ def test_split_select_at_its_limit(spin_lib):
     p.close()
 
 
+# (partitions per list, k): lists one past k, and lists that end on, one past
+# and one short of a workgroup's rows (256-row workgroups below 1024
+# partitions, 512-row ones from there), in both split-select row layouts
+SPLIT_EDGES = [(9, 8), (65, 64), (255, 8), (256, 8), (257, 64), (511, 64), (512, 8), (513, 64),
+               (1023, 64), (1024, 8), (1025, 64), (1537, 64)]
+
+
+@pytest.mark.parametrize("n,k", SPLIT_EDGES, ids=[f"n{n}-k{k}" for n, k in SPLIT_EDGES])
+def test_split_select_chunk_edges(spin_lib, n, k):
+    """The several-workgroups-per-list select at the list lengths where its
+    work split changes (the second request one partition shorter, its last
+    page ragged): the selections and scores of every step against the
+    oracle's, with the rest of the step checked as usual."""
+    w = W.variant(W.C3, name=f"split_edge_{n}_{k}", B=2, Hq=8, Hkv=2, ctx=(n * 64, (n - 1) * 64 - 37),
+                  k=k, steps=4, hot_count=3)
+    p = _pair(w, slots=2 * k * 3)
+    assert p.geo.max_parts == n
+    st, _ = p.run()
+    assert st.misses > 0
+    p.close()
+
+
 def test_directory_beyond_lds(spin_lib):
     """A request directory larger than the resolve kernel keeps in LDS (16 KV
     heads x 313 ranges of 64 pages = 5008 entries > 4096): every lookup and
