@@ -329,6 +329,22 @@ def test_split_select_chunk_edges(spin_lib, n, k):
     p.close()
 
 
+@pytest.mark.parametrize("form", ["staged", "graph"])
+def test_step_lists_beyond_lds(spin_lib, form):
+    """One request's step past every list the resolve kernel keeps in LDS:
+    8192 misses at step 0 (the slot assignment goes through the insert list
+    itself, the misses past 2048 are read back from global memory) and about
+    5000 victims a step after it (the victim list no longer fits, so the
+    eviction pass walks every slot), with k = 1024 over 4 KV heads and
+    two-page partitions."""
+    w = W.variant(W.C5, name="big_lists", B=1, Hq=8, Hkv=4, ctx=(300000,), k=1024, steps=4,
+                  var_len=(65, 128), n_centroids=64, ar_coef=0.1)
+    p = _pair(w, slots=8192 + 64)
+    st, _ = p.run(out_sample=16) if form == "staged" else p.run_graph(out_sample=16)
+    assert st.misses > 8192 and st.evictions > 3 * 4097
+    p.close()
+
+
 def test_directory_beyond_lds(spin_lib):
     """A request directory larger than the resolve kernel keeps in LDS (16 KV
     heads x 313 ranges of 64 pages = 5008 entries > 4096): every lookup and
