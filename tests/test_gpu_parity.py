@@ -395,6 +395,10 @@ TIES = {
     # the boundary falls among the 40 equal hot scores
     "ties_in_hot": W.variant(W.C2, name="ties_in_hot", B=2, Hq=8, Hkv=2, ctx=(32768, 9000),
                              k=8, steps=4, kv_kind="ties", hot_count=40),
+    # ... among 120 equal hot scores: more boundary-bin members than one
+    # wave's lanes, ranked one per thread
+    "ties_in_hot_120": W.variant(W.C2, name="ties_in_hot_120", B=2, Hq=8, Hkv=2, ctx=(32768, 20000),
+                                 k=50, steps=4, kv_kind="ties", hot_count=120),
     # every score of a head equal (a zero-width score range)
     "ties_flat": W.variant(W.C2, name="ties_flat", B=1, Hq=8, Hkv=2, ctx=(20000,),
                            k=16, steps=3, kv_kind="ties", hot_count=0),
