@@ -402,6 +402,10 @@ TIES = {
     # every score of a head equal (a zero-width score range)
     "ties_flat": W.variant(W.C2, name="ties_flat", B=1, Hq=8, Hkv=2, ctx=(20000,),
                            k=16, steps=3, kv_kind="ties", hot_count=0),
+    # lists past the split select's 4096 partitions (scoring and top-k as two
+    # launches), ties inside the hot group at the boundary
+    "ties_two_launch": W.variant(W.C2, name="ties_two_launch", B=1, Hq=8, Hkv=2, ctx=(300000,),
+                                 k=16, steps=3, kv_kind="ties", hot_count=40),
     # 128 lists (the fused score + top-k kernel), ties inside the hot group
     "ties_fused": W.variant(W.C2, name="ties_fused", B=32, Hq=16, Hkv=4, ctx=(4096,) * 32,
                             k=8, steps=3, kv_kind="ties", hot_count=20),
