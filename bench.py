@@ -199,6 +199,107 @@ def cpu_baseline(w, geo, draws, host_np, start, end, budget_s=20.0):
                       f"{t_setup:.1f} s"}
 
 
+def prefill(args):
+    """The prefill-side operations, timed on their own (--prefill): Index over
+    the link (summaries read zero-copy from the pinned host KV), Offload (the
+    device KV copied to its reserved host runs, then Index from the device
+    copy) and decode-time append of one token to every request.  The first
+    min(B, --prefill-requests) requests of the workload; each call is timed
+    on the host around the call (Index and Offload synchronise), the appends
+    with events around a run of them back to back.  Prints one JSON line."""
+    import torch
+
+    from sparse_attention_tiered_amd import binding as bd
+    from sparse_attention_tiered_amd import workload as W
+
+    w0 = W.get(args.config)
+    n_req = max(1, min(w0.B, args.prefill_requests))
+    w = W.variant(w0, B=n_req)
+    n_app = args.appends
+    extra = -(-n_app // W.PAGE_TOKENS) + 1          # host pages reserved per head for the appends
+    t0 = time.time()
+    geo = W.geometry(w)
+    draws = W.draw_queries(w, geo, 1)
+    src = [bd.pinned_u16(w.Hkv * geo.pages[b] * W.PAGE_ELEMS) for b in range(w.B)]
+    W.fill_all(w, geo, draws, [h[1] for h in src])
+    d_kv = [s[0].to("cuda") for s in src]
+    dst = [torch.zeros(w.Hkv * (geo.pages[b] + extra) * W.PAGE_ELEMS, dtype=torch.int16, pin_memory=True)
+           for b in range(w.B)]
+    torch.cuda.synchronize()
+    log(f"[prefill] {w.name}: {n_req} requests, inputs in {time.time() - t0:.1f}s")
+    cfg = bd.make_config(w.B, w.Hq, w.Hkv, geo.max_parts + extra, geo.max_pages + extra, w.k,
+                         w.slots_per_request, max_pages_per_partition=geo.max_ppp)
+    spin = bd.Spin(cfg)
+    S = torch.cuda.Stream()
+    lens = [geo.lens[b] if w.var_len is not None else None for b in range(w.B)]
+    tokens = [int(sum(geo.lens[b])) for b in range(w.B)]
+    kv_bytes = [w.Hkv * geo.pages[b] * PAGE_BYTES for b in range(w.B)]
+    key_bytes = [w.Hkv * tokens[b] * W.HEAD_DIM * 2 for b in range(w.B)]   # the valid tokens' keys
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) * 1e3
+
+    # untimed first calls (a kernel's first launch in a process costs ~0.6 ms)
+    spin.index(0, src[0][0], w.ctx[0], lens[0], stream=S)
+    spin.offload(0, d_kv[0], dst[0], w.ctx[0], lens[0], stream=S)
+    idx_ms = [timed(lambda b=b: spin.index(b, src[b][0], w.ctx[b], lens[b], stream=S)) for b in range(w.B)]
+    off_ms = [timed(lambda b=b: spin.offload(b, d_kv[b], dst[b], w.ctx[b], lens[b], stream=S))
+              for b in range(w.B)]
+    # the host copy must be the device KV, head by head in its reserved run
+    for b in range(w.B):
+        cap = geo.pages[b] + extra
+        got = dst[b].view(w.Hkv, cap * W.PAGE_ELEMS)[:, : geo.pages[b] * W.PAGE_ELEMS]
+        if not torch.equal(got, src[b][0].view(w.Hkv, geo.pages[b] * W.PAGE_ELEMS)):
+            raise RuntimeError(f"offloaded host copy of request {b} differs from the device KV")
+    # a plain device -> pinned host copy of the same bytes (one DMA transfer)
+    flat = [dst[b][: w.Hkv * geo.pages[b] * W.PAGE_ELEMS] for b in range(w.B)]
+    flat[0].copy_(d_kv[0], non_blocking=True)
+    d2h_ms = [timed(lambda b=b: flat[b].copy_(d_kv[b], non_blocking=True)) for b in range(w.B)]
+    # the appends: one token per request per call, on top of the offloaded KV
+    g = torch.Generator().manual_seed(w.seed)
+    dk = torch.randint(-16000, 16000, (n_app + 1, w.B, w.Hkv, W.HEAD_DIM), dtype=torch.int16, generator=g)
+    dv = torch.randint(-16000, 16000, (n_app + 1, w.B, w.Hkv, W.HEAD_DIM), dtype=torch.int16, generator=g)
+    dk, dv = (dk & 0x3FFF).to("cuda"), (dv & 0x3FFF).to("cuda")   # finite bf16 bit patterns
+    with torch.cuda.stream(S):
+        spin.append(dk[0], dv[0], stream=S)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(S)
+        for i in range(1, n_app + 1):
+            spin.append(dk[i], dv[i], stream=S)
+        e1.record(S)
+    torch.cuda.synchronize()
+    app_ms = e0.elapsed_time(e1) / n_app
+    spin.close()
+    link = pcie_link()
+    off_gbs = sum(kv_bytes) / (sum(off_ms) * 1e-3) / 1e9
+    line = {
+        "metric": "prefill offload GB/s (device KV to its host runs + Index from HBM)",
+        "value": off_gbs, "unit": "GB/s", "n_gpus": 1, "steps": w.B, "warmup": 1,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.B, "kv_heads": w.Hkv, "context": w.ctx[0],
+                   "partitions": "variable 16-256" if w.var_len else "fixed 64",
+                   "parallelism": "single-gpu"},
+        "offload": {"ms_per_request": float(np.mean(off_ms)), "bytes_per_request": float(np.mean(kv_bytes)),
+                    "GBps": off_gbs, "frac_of_link": off_gbs / PCIE_GEN5_X16_GBS,
+                    "plain_d2h_copy_ms_per_request": float(np.mean(d2h_ms)),
+                    "plain_d2h_copy_GBps": sum(kv_bytes) / (sum(d2h_ms) * 1e-3) / 1e9,
+                    "host_copy_checked": True},
+        "index_over_link": {"ms_per_request": float(np.mean(idx_ms)),
+                            "key_bytes_per_request": float(np.mean(key_bytes)),
+                            "GBps": sum(key_bytes) / (sum(idx_ms) * 1e-3) / 1e9,
+                            "frac_of_link": sum(key_bytes) / (sum(idx_ms) * 1e-3) / 1e9 / PCIE_GEN5_X16_GBS},
+        "append": {"us_per_call": app_ms * 1e3, "calls": n_app, "tokens_per_call": w.B,
+                   "timed_as": "back-to-back calls on one stream, events at the ends"},
+        "pcie": {"link": link, "peak_GBps": PCIE_GEN5_X16_GBS},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,12 +325,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain elementwise copy of 256 MiB three times "
                          "(reference kernel for the HBM byte counters)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time Index, Offload and append on their own instead of decode steps")
+    ap.add_argument("--prefill-requests", type=int, default=4,
+                    help="with --prefill: how many of the workload's requests")
+    ap.add_argument("--appends", type=int, default=256, help="with --prefill: appends timed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path shards by "
               "request with no exchange, so N GPUs run N independent copies of this benchmark.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.prefill:
+        prefill(args)
+        return
 
     import torch
 

@@ -133,53 +133,88 @@ __global__ __launch_bounds__(64) void k_index(Dev d, int req, const char* __rest
 // host copy and, when the page is resident, to its pool slot; the tail
 // partition's summary is its exact fp64 key sum over its length.  The host
 // has checked that every request has room.
-__global__ __launch_bounds__(256) void k_append(Dev d, const uint16_t* __restrict__ k,
-                                                const uint16_t* __restrict__ v) {
+//
+// One 1024-lane workgroup per request; lane e owns element e (and e + 1024
+// when Hkv > 8) of the token's [Hkv][128] rows.  The kernel is a chain of
+// dependent round trips (the request's tail, then the token and its
+// directory entry, then the segment entry), so every load a lane needs is
+// issued before its first store and loads are never conditional: the
+// compiler cannot tell the stores from the loads apart, and would otherwise
+// wait for each store before the next load.
+constexpr int kAppendLanes = 1024;
+constexpr int kAppendPer = kMaxKvHeads * kHeadDim / kAppendLanes;
+
+__global__ __launch_bounds__(kAppendLanes) void k_append(Dev d, const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v) {
   __shared__ int sh[5];  // new partition?, tail index, page, token slot, new length
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (d.host_base[b] == 0) return;  // no registered KV
-  const int n = d.req_parts[b];
+  const unsigned long long host = d.host_base[b];
+  const int stride = d.req_stride[b];
   if (tid == 0) {
-    const int L = n > 0 ? d.part_len[(size_t)b * d.Nmax + n - 1] : 0;
+    const int n = d.req_parts[b], pages = d.req_pages[b];
+    const size_t last = (size_t)b * d.Nmax + (n > 0 ? n - 1 : 0);
+    int L0 = d.part_len[last], F0 = d.part_first[last];
+    asm volatile("" : "+s"(L0), "+s"(F0));  // both loads in flight before either is used
+    const int L = n > 0 ? L0 : 0;
     const bool fresh = n == 0 || (L % kPageTokens) == 0;
-    const int tail = fresh ? n : n - 1;
     const int len = fresh ? 1 : L + 1;
-    const int first = fresh ? d.req_pages[b] : d.part_first[(size_t)b * d.Nmax + tail];
+    const int first = fresh ? pages : F0;
     sh[0] = fresh;
-    sh[1] = tail;
+    sh[1] = fresh ? n : n - 1;
     sh[2] = first + (len - 1) / kPageTokens;
     sh[3] = (len - 1) % kPageTokens;
     sh[4] = len;
   }
   __syncthreads();
+  if (host == 0) return;  // no registered KV (uniform over the workgroup)
   const bool fresh = sh[0];
   const int tail = sh[1], page = sh[2], tok = sh[3], len = sh[4];
-  const int stride = d.req_stride[b];
-  for (int e = tid; e < d.Hkv * kHeadDim; e += 256) {
+  const int nel = d.Hkv * kHeadDim;
+  uint16_t kb[kAppendPer], vb[kAppendPer];
+  int seg[kAppendPer];
+  double prev[kAppendPer];
+#pragma unroll
+  for (int j = 0; j < kAppendPer; ++j) {
+    const int e = min(tid + j * kAppendLanes, nel - 1);
+    const int h = e / kHeadDim;
+    kb[j] = k[(size_t)b * nel + e];
+    vb[j] = v[(size_t)b * nel + e];
+    seg[j] = d.directory[((size_t)b * d.Hkv + h) * d.ndir + (page >> 6)];
+    prev[j] = d.tail_sum[(size_t)b * nel + e];
+  }
+  int slot[kAppendPer];
+#pragma unroll
+  for (int j = 0; j < kAppendPer; ++j) {
+    const bool ok = seg[j] >= 0 && seg[j] < d.n_seg;
+    slot[j] = d.segments[(size_t)(ok ? seg[j] : 0) * kSegEntries + (page & 63)];
+    if (!ok) slot[j] = -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kAppendPer; ++j) {
+    const int e = tid + j * kAppendLanes;
+    if (e >= nel) break;
     const int h = e / kHeadDim, dim = e - h * kHeadDim;
-    const uint16_t kb = k[((size_t)b * d.Hkv + h) * kHeadDim + dim];
-    const uint16_t vb = v[((size_t)b * d.Hkv + h) * kHeadDim + dim];
-    uint16_t* hp = reinterpret_cast<uint16_t*>(d.host_base[b] + ((size_t)h * stride + page) * (size_t)kPageBytes);
-    hp[tok * kHeadDim + dim] = kb;
-    hp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb;
-    const int seg = d.directory[((size_t)b * d.Hkv + h) * d.ndir + (page >> 6)];
-    const int slot = (seg >= 0 && seg < d.n_seg) ? d.segments[(size_t)seg * kSegEntries + (page & 63)] : -1;
-    if (slot >= 0 && slot < d.C) {
-      uint16_t* pp = d.pool + ((size_t)b * d.C + slot) * kPageElems;
-      pp[tok * kHeadDim + dim] = kb;
-      pp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb;
+    // a global (not generic) pointer: generic stores may complete out of
+    // order with loads, so every later wait would have to drain them
+    __attribute__((address_space(1))) uint16_t* hp =
+        reinterpret_cast<__attribute__((address_space(1))) uint16_t*>(
+            host + ((size_t)h * stride + page) * (size_t)kPageBytes);
+    hp[tok * kHeadDim + dim] = kb[j];
+    hp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb[j];
+    if (slot[j] >= 0 && slot[j] < d.C) {
+      uint16_t* pp = d.pool + ((size_t)b * d.C + slot[j]) * kPageElems;
+      pp[tok * kHeadDim + dim] = kb[j];
+      pp[kPageTokens * kHeadDim + dim * kPageTokens + tok] = vb[j];
     }
-    double* ts = d.tail_sum + ((size_t)b * d.Hkv + h) * kHeadDim + dim;
-    const double sum = (fresh ? 0.0 : *ts) + (double)__uint_as_float((uint32_t)kb << 16);
-    *ts = sum;
+    const double sum = (fresh ? 0.0 : prev[j]) + (double)__uint_as_float((uint32_t)kb[j] << 16);
+    d.tail_sum[(size_t)b * nel + e] = sum;
     d.summaries[(((size_t)b * d.Hkv + h) * d.Nmax + tail) * kHeadDim + dim] = (float)(sum / (double)len);
   }
-  __syncthreads();
-  if (tid == 0) {
+  if (tid == 0) {  // read only by later launches
     d.part_len[(size_t)b * d.Nmax + tail] = len;
     if (fresh) {
       d.part_first[(size_t)b * d.Nmax + tail] = page;
-      d.req_parts[b] = n + 1;
+      d.req_parts[b] = tail + 1;
       d.req_pages[b] = page + 1;
     }
   }
@@ -211,7 +246,7 @@ hipError_t launch_index(const Dev& d, int req, int n_parts, const void* src, int
 }
 
 hipError_t launch_append(const Dev& d, const uint16_t* k, const uint16_t* v, hipStream_t s) {
-  hipLaunchKernelGGL(k_append, dim3(d.B), dim3(256), 0, s, d, k, v);
+  hipLaunchKernelGGL(k_append, dim3(d.B), dim3(kAppendLanes), 0, s, d, k, v);
   return hipGetLastError();
 }
 

@@ -528,7 +528,7 @@ SPIN_API int spin_offload(spin_ctx* ctx, int32_t req, const void* d_kv, void* h_
     HIPCHK(ctx, hipMemcpy2DAsync(h_kv, (size_t)capacity * spin::kPageBytes, d_kv,
                                  (size_t)pages * spin::kPageBytes, (size_t)pages * spin::kPageBytes,
                                  c.num_kv_heads, hipMemcpyDeviceToHost, s));
-  // Index from the device copy (HBM), while the host copy is written
+  // Index from the device copy (HBM), after the copy in stream order
   return register_request(ctx, req, reinterpret_cast<unsigned long long>(dptr), (int)capacity, lens,
                           first, (int)pages, d_kv, (int)pages, s);
 }

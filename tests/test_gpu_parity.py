@@ -220,14 +220,19 @@ def test_metadata_footprint(spin_lib):
     p.close()
 
 
-@pytest.mark.parametrize("name", ["fixed", "variable"])
+@pytest.mark.parametrize("name", ["fixed", "variable", "kv16"])
 def test_offload_and_append(spin_lib, name):
     """Prefill-side Offload + Index from device KV, then one appended token per
     request per step: host bytes, summaries, selection, residency state and
-    outputs match the oracle every step (ragged requests, a partial tail)."""
+    outputs match the oracle every step (ragged requests, a partial tail;
+    with 16 KV heads each lane of the append kernel owns two elements)."""
     if name == "fixed":
         w = W.variant(W.C4, B=3, ctx=(5000, 3000, 64 * 20), k=8, steps=40, ar_coef=0.5)
         slots = 8 * 8 + 24
+    elif name == "kv16":
+        w = W.variant(W.C5, name="kv16", B=2, Hq=32, Hkv=16, ctx=(7000, 3333), k=6, steps=30,
+                      n_centroids=64)
+        slots = 16 * 6 * 4 + 24
     else:
         w = W.variant(W.C5, B=2, ctx=(9000, 4321), k=8, steps=30, n_centroids=64)
         slots = 8 * 8 * 4 + 24
