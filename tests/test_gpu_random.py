@@ -120,3 +120,54 @@ def test_random_shape_variants(spin_lib, i):
         p.check_summaries()
     assert st.error_word == 0
     p.close()
+
+
+N_KV16 = 8
+
+
+def kv16_case(i: int):
+    """Random offload + append case i with 16 KV heads, where each lane of the
+    append kernel owns two elements of the token (a pure function of i)."""
+    rng = np.random.default_rng([5151, i])
+    G = int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 4))
+    var_len = None
+    if rng.random() < 0.5:
+        lo = int(rng.integers(8, 96))
+        var_len = (lo, int(rng.integers(lo, 257)))
+    ctx = tuple(int(rng.integers(1, 9000)) for _ in range(B))
+    k = int(rng.integers(1, 17))
+    ppp = 1 if var_len is None else -(-var_len[1] // W.PAGE_TOKENS)
+    mand = 16 * k * ppp
+    slots = mand + int(mand * rng.uniform(0.0, 0.6))
+    w = W.variant(W.C1, name=f"kv16_{i}", cfg_id=300 + i, seed=i, B=B, Hq=16 * G, Hkv=16, ctx=ctx, k=k,
+                  slots_per_request=slots, steps=int(rng.integers(20, 80)),
+                  kv_kind=str(rng.choice(["hot", "plain", "cluster"])), hot_count=int(rng.integers(0, 5)),
+                  n_centroids=64, var_len=var_len, ar_coef=float(rng.uniform(0.2, 0.95)))
+    host_segments = bool(rng.random() < 0.5)
+    return w, slots, host_segments
+
+
+KV16 = [kv16_case(i) for i in range(N_KV16)]
+
+
+@pytest.mark.parametrize("i", range(N_KV16),
+                         ids=[f"{w.name}-B{w.B}-{w.Hq}x16-k{w.k}-{'var' if w.var_len else 'fixed'}-"
+                              f"{'hostseg' if hs else 'gpuseg'}" for w, _, hs in KV16])
+def test_random_append_kv16(spin_lib, i):
+    """Offload, then a token appended per request per step, with 16 KV heads
+    (pages crossed, new partitions started, resident tail pages written):
+    host bytes, summaries and every stage against the oracle."""
+    from tests.gpu_harness import Pair, log
+    w, slots, host_segments = KV16[i]
+    log(f"[case] {w.name} B={w.B} Hq={w.Hq} ctx={w.ctx} k={w.k} var_len={w.var_len} C={slots} "
+        f"steps={w.steps} host_segments={host_segments}")
+    extra = (w.steps + W.PAGE_TOKENS - 1) // W.PAGE_TOKENS + 2
+    p = Pair(w, slots=slots, host_segments=host_segments, offload_extra_pages=extra)
+    p.check_host()
+    p.check_summaries()
+    st, _ = p.run(append=True)
+    p.check_host()
+    p.check_summaries()
+    assert st.error_word == 0 and st.misses > 0
+    p.close()
